@@ -1,0 +1,759 @@
+// libcd host runtime: buffer plan, argument/state validation, and the
+// orchestration of the canvas denoise step, block commit and generation loop
+// on one HIP stream.  The library never allocates device memory: weights and
+// state live in two caller buffers carved up by Plan.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cd.h"
+#include "kernels.h"
+
+using namespace cd;
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t hip_status(const char* where) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CD_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+  return CD_OK;
+}
+
+constexpr int64_t ALIGN = 256;
+constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows
+constexpr int MAX_SPLIT = 16;          // attention key splits
+
+struct Carve {
+  int64_t off = 0;
+  int64_t take(int64_t bytes) {
+    int64_t o = off;
+    off = round_up(off + std::max<int64_t>(bytes, 1), ALIGN);
+    return o;
+  }
+};
+
+struct LayerOff {
+  int64_t qkv, qkv_s, wo, wo_s, wr, gu, gu_s, dn, dn_s, sgu, sdn;
+};
+
+struct Plan {
+  cd_config c;
+  int wdt_attn, wdt_exp, wdt_other, adt;
+  int ctx;                 // KV capacity rounded to 64
+  int Tmax;                // rows of the largest forward
+  int qkv_npad, wo_npad, wr_npad, gu_npad, dn_npad, sgu_npad, sdn_npad, lm_npad;
+  int64_t gu_stride, dn_stride;        // bytes per expert
+  // weights
+  int64_t embed, lm;
+  std::vector<LayerOff> layer;
+  int64_t weights_bytes;
+  // state
+  int64_t rq, canvas, argmax, lock, entropy, pmax, info, h, u, q, o, part_o, part_ml, rlog, topk_id,
+      topk_gate, blk_cnt, seg_off, row_map, slot, tiles, n_tiles, aperm, yperm, sact, logits, spart, rope,
+      kcache, vcache, zero;
+  int64_t max_rows, max_tiles, n_blk_max, n_chunks;
+  int64_t kv_req_stride, kv_layer_stride;   // elements
+  int64_t state_bytes;
+};
+
+int32_t validate_config(const cd_config* c) {
+  if (!c) return fail(CD_ERR_INVALID_ARG, "null config");
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->n_experts < 1 || c->top_k < 1 || c->expert_hidden < 1 || c->shared_hidden < 0 || c->vocab < 1 ||
+      c->canvas_len < 1 || c->max_steps < 1 || c->max_requests < 1 || c->max_ctx < 1 || c->max_prefill < 1)
+    return fail(CD_ERR_INVALID_ARG, "config fields must be positive");
+  if (c->weight_dtype < CD_F32 || c->weight_dtype > CD_FP8) return fail(CD_ERR_INVALID_ARG, "bad weight_dtype");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(CD_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->n_q_heads % c->n_kv_heads) return fail(CD_ERR_INVALID_ARG, "n_q_heads %% n_kv_heads != 0");
+  if (c->n_q_heads / c->n_kv_heads > 4) return fail(CD_ERR_UNSUPPORTED, "at most 4 query heads per KV head");
+  if (c->d_model % 64 || c->expert_hidden % 64 || c->shared_hidden % 64 || (c->n_q_heads * c->head_dim) % 64)
+    return fail(CD_ERR_UNSUPPORTED, "d_model, expert_hidden, shared_hidden, n_q_heads*head_dim must be multiples of 64");
+  if (c->n_experts > 256 || c->top_k > 16 || c->top_k > c->n_experts)
+    return fail(CD_ERR_UNSUPPORTED, "n_experts <= 256 and top_k <= min(16, n_experts) required");
+  if (c->vocab % 128) return fail(CD_ERR_UNSUPPORTED, "vocab must be a multiple of 128");
+  if (c->max_ctx < c->canvas_len + 1) return fail(CD_ERR_INVALID_ARG, "max_ctx must exceed canvas_len");
+  if (!(c->lock_threshold >= 0.f && c->lock_threshold <= 1.f) || !(c->stop_entropy >= 0.f) || !(c->rms_eps >= 0.f) ||
+      !(c->rope_theta >= 0.f))
+    return fail(CD_ERR_INVALID_ARG, "bad sampler/norm constants");
+  return CD_OK;
+}
+
+int sampler_chunks(int V) {
+  int n = 1;
+  while (V / n > 16384 && (V % (2 * n * 4)) == 0) n *= 2;
+  return n;
+}
+
+Plan make_plan(const cd_config& c) {
+  Plan p;
+  p.c = c;
+  p.wdt_attn = c.weight_dtype;
+  p.wdt_exp = c.weight_dtype;
+  p.wdt_other = c.weight_dtype == CD_FP8 ? CD_BF16 : c.weight_dtype;
+  p.adt = c.weight_dtype == CD_F32 ? CD_F32 : CD_BF16;
+  p.ctx = (int)round_up(c.max_ctx, 64);
+  const int C = c.canvas_len, d = c.d_model, dh = c.head_dim, L = c.n_layers, E = c.n_experts;
+  p.Tmax = std::max(c.max_requests * C, c.max_prefill);
+  p.qkv_npad = (int)round_up((c.n_q_heads + 2 * c.n_kv_heads) * dh, 32);
+  p.wo_npad = (int)round_up(d, 32);
+  p.wr_npad = (int)round_up(E, 32);
+  p.gu_npad = 2 * c.expert_hidden;
+  p.dn_npad = (int)round_up(d, 32);
+  p.sgu_npad = 2 * c.shared_hidden;
+  p.sdn_npad = (int)round_up(d, 32);
+  p.lm_npad = (int)round_up(c.vocab, 32);
+  const bool f8 = c.weight_dtype == CD_FP8;
+  p.gu_stride = round_up(packed_bytes(p.gu_npad, d, p.wdt_exp), ALIGN);
+  p.dn_stride = round_up(packed_bytes(p.dn_npad, c.expert_hidden, p.wdt_exp), ALIGN);
+
+  Carve w;
+  p.embed = w.take((int64_t)c.vocab * d * esize(p.wdt_other));
+  p.lm = w.take(packed_bytes(p.lm_npad, d, p.wdt_other));
+  p.layer.resize(L);
+  for (int l = 0; l < L; ++l) {
+    LayerOff& o = p.layer[l];
+    o.qkv = w.take(packed_bytes(p.qkv_npad, d, p.wdt_attn));
+    o.qkv_s = f8 ? w.take(p.qkv_npad * 4) : -1;
+    o.wo = w.take(packed_bytes(p.wo_npad, (int64_t)c.n_q_heads * dh, p.wdt_attn));
+    o.wo_s = f8 ? w.take(p.wo_npad * 4) : -1;
+    o.wr = w.take(packed_bytes(p.wr_npad, d, p.wdt_other));
+    o.gu = w.take(p.gu_stride * E);
+    o.gu_s = f8 ? w.take((int64_t)p.gu_npad * 4 * E) : -1;
+    o.dn = w.take(p.dn_stride * E);
+    o.dn_s = f8 ? w.take((int64_t)p.dn_npad * 4 * E) : -1;
+    o.sgu = c.shared_hidden ? w.take(packed_bytes(p.sgu_npad, d, p.wdt_other)) : -1;
+    o.sdn = c.shared_hidden ? w.take(packed_bytes(p.sdn_npad, c.shared_hidden, p.wdt_other)) : -1;
+  }
+  p.weights_bytes = w.off;
+
+  const int R = c.max_requests, T = p.Tmax, k = c.top_k, ae = esize(p.adt);
+  const int mrows = 16 * GROUPED_MT;
+  p.max_rows = round_up((int64_t)T * k + (int64_t)E * mrows, 64);
+  p.max_tiles = ((int64_t)T * k + mrows - 1) / mrows + E;
+  p.n_blk_max = ((int64_t)T * k + 511) / 512;
+  p.n_chunks = sampler_chunks(c.vocab);
+  p.kv_layer_stride = (int64_t)c.n_kv_heads * p.ctx * dh;
+  p.kv_req_stride = p.kv_layer_stride * L;
+
+  Carve s;
+  p.zero = s.take(256);
+  p.rq = s.take(sizeof(ReqDev) * R);
+  p.canvas = s.take(4LL * R * C);
+  p.argmax = s.take(4LL * R * C);
+  p.lock = s.take(1LL * R * C);
+  p.entropy = s.take(8LL * R * C);
+  p.pmax = s.take(8LL * R * C);
+  p.info = s.take(sizeof(cd_step_info) * R);
+  p.h = s.take(4LL * T * d);
+  p.u = s.take((int64_t)ae * T * d);
+  p.q = s.take((int64_t)ae * T * c.n_q_heads * dh);
+  p.o = s.take((int64_t)ae * T * c.n_q_heads * dh);
+  p.part_o = s.take(4LL * MAX_SPLIT * T * c.n_q_heads * dh);
+  p.part_ml = s.take(8LL * MAX_SPLIT * T * c.n_q_heads);
+  p.rlog = s.take(4LL * T * E);
+  p.topk_id = s.take(4LL * T * k);
+  p.topk_gate = s.take(4LL * T * k);
+  p.blk_cnt = s.take(4LL * p.n_blk_max * E);
+  p.seg_off = s.take(4LL * (E + 1));
+  p.row_map = s.take(4LL * p.max_rows);
+  p.slot = s.take(4LL * T * k);
+  p.tiles = s.take(16LL * p.max_tiles);
+  p.n_tiles = s.take(4);
+  p.aperm = s.take((int64_t)ae * p.max_rows * c.expert_hidden);
+  p.yperm = s.take((int64_t)ae * p.max_rows * d);
+  p.sact = s.take((int64_t)ae * T * std::max(c.shared_hidden, 1));
+  p.logits = s.take(4LL * R * C * c.vocab);
+  p.spart = s.take(16LL * R * C * p.n_chunks);
+  p.rope = s.take(8LL * p.ctx * (dh / 2));
+  p.kcache = s.take((int64_t)ae * p.kv_req_stride * R);
+  p.vcache = s.take((int64_t)ae * p.kv_req_stride * R);
+  p.state_bytes = s.off;
+  return p;
+}
+
+struct HostReq {
+  int P = 0, t = 0, block = 0;
+  bool active = false;
+  uint64_t seed = 0;
+};
+
+}  // namespace
+
+struct cd_ctx {
+  Plan p;
+  uint8_t* W;
+  uint8_t* S;
+  std::vector<HostReq> req;
+  float* trace_h = nullptr;
+  int32_t* trace_ids = nullptr;
+  float* trace_gates = nullptr;
+  template <class T> T* st(int64_t off) const { return reinterpret_cast<T*>(S + off); }
+  template <class T> T* wt(int64_t off) const { return off < 0 ? nullptr : reinterpret_cast<T*>(W + off); }
+};
+
+namespace {
+
+hipStream_t strm(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---- GEMM dispatch ---------------------------------------------------------------
+struct GemmCall {
+  int wdt, epi, mt;
+  GemmArgs a;
+};
+
+GemmArgs gemm_base(const void* X, int64_t ldx, const uint8_t* W, const float* wscale, int K, int Npad, int N,
+                   void* Y, int64_t ldy) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.X = X; a.ldx = ldx; a.W = W; a.wscale = wscale; a.K = K;
+  a.Nt = Npad / 16; a.N = N; a.n_chunks = (a.Nt + 7) / 8;
+  a.Y = Y; a.ldy = ldy;
+  return a;
+}
+
+void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
+  const int mt = M >= 64 ? 4 : (M > 16 ? 2 : 1);
+  a.M = M;
+  a.max_tiles = (M + 16 * mt - 1) / (16 * mt);
+  a.chunk_major = 1;
+  a.tiles = nullptr;
+  launch_gemm(wdt, c->p.adt, mt, epi, a, s);
+}
+
+void gemm_grouped(const cd_ctx* c, int wdt, int epi, GemmArgs a, hipStream_t s) {
+  a.tiles = c->st<int32_t>(c->p.tiles);
+  a.n_tiles = c->st<int32_t>(c->p.n_tiles);
+  a.max_tiles = (int)c->p.max_tiles;
+  a.chunk_major = 0;
+  launch_gemm(wdt, c->p.adt, GROUPED_MT, epi, a, s);
+}
+
+// ---- forward over rows of requests r0..r0+n_req-1 --------------------------------------
+// ids: rows_per_req ids per request; positions P_r + i; causal: prefill mask.
+void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids, bool causal, bool head,
+             bool trace, hipStream_t s) {
+  const Plan& p = c->p;
+  const cd_config& g = p.c;
+  const int T = n_req * rows_per_req;
+  const int d = g.d_model, dh = g.head_dim, E = g.n_experts, k = g.top_k;
+  const int qd = g.n_q_heads * dh;
+  const int adt = p.adt, ae = esize(adt);
+  float* h = c->st<float>(p.h);
+  void* u = c->st<void>(p.u);
+  void* Q = c->st<void>(p.q);
+  void* O = c->st<void>(p.o);
+  ReqDev* rq = c->st<ReqDev>(p.rq) + r0;
+  const int32_t* pos0 = &rq->P;
+  const int pos_stride = (int)(sizeof(ReqDev) / 4);
+  const float* rope = g.rope_theta > 0 ? c->st<float>(p.rope) : nullptr;
+
+  int nkeys_max = 0;
+  for (int r = r0; r < r0 + n_req; ++r) nkeys_max = std::max(nkeys_max, c->req[r].P + rows_per_req);
+  const int G = g.n_q_heads / g.n_kv_heads;
+  const int TB = 128 / G;
+  AttnArgs at;
+  memset(&at, 0, sizeof at);
+  at.Q = Q; at.O = O;
+  at.kv_req_stride = p.kv_req_stride;
+  at.max_ctx = p.ctx; at.Hq = g.n_q_heads; at.Hkv = g.n_kv_heads; at.dh = dh;
+  at.rows_per_req = rows_per_req; at.n_req = n_req;
+  at.pos0 = pos0; at.pos0_stride = pos_stride;
+  at.causal = causal ? 1 : 0;
+  at.q_blocks = (rows_per_req + TB - 1) / TB;
+  const int base_wg = n_req * g.n_kv_heads * at.q_blocks;
+  int ns = std::max(1, (512 + base_wg - 1) / base_wg);
+  ns = std::min(ns, MAX_SPLIT);
+  ns = std::min(ns, std::max(1, (nkeys_max + 63) / 64));
+  at.split_len = (int)round_up((nkeys_max + ns - 1) / ns, 32);
+  at.n_split = (nkeys_max + at.split_len - 1) / at.split_len;
+  at.part_o = c->st<float>(p.part_o);
+  at.part_ml = c->st<float>(p.part_ml);
+
+  launch_embed(p.wdt_other, c->W + p.embed, ids, T, g.vocab, d, h, s);
+  for (int l = 0; l < g.n_layers; ++l) {
+    const LayerOff& lw = p.layer[l];
+    if (trace && c->trace_h) launch_copy_f32(h, c->trace_h + (int64_t)l * T * d, (int64_t)T * d, s);
+    launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s);
+    // QKV + rotary, K/V scattered into the cache at positions P_r + i
+    {
+      GemmArgs a = gemm_base(u, d, c->W + lw.qkv, c->wt<float>(lw.qkv_s), d, p.qkv_npad,
+                             (g.n_q_heads + 2 * g.n_kv_heads) * dh, Q, qd);
+      uint8_t* kc = c->S + p.kcache + ((int64_t)r0 * p.kv_req_stride + l * p.kv_layer_stride) * ae;
+      uint8_t* vc = c->S + p.vcache + ((int64_t)r0 * p.kv_req_stride + l * p.kv_layer_stride) * ae;
+      a.kc = kc; a.vc = vc; a.kv_req_stride = p.kv_req_stride;
+      a.max_ctx = p.ctx; a.Hq = g.n_q_heads; a.Hkv = g.n_kv_heads; a.dh = dh;
+      a.rows_per_req = rows_per_req; a.pos0 = pos0; a.pos0_stride = pos_stride; a.rope_cs = rope;
+      gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s);
+      at.kc = kc; at.vc = vc;
+    }
+    launch_attention(adt, at, s);
+    launch_attn_merge(adt, at, s);
+    {
+      GemmArgs a = gemm_base(O, qd, c->W + lw.wo, c->wt<float>(lw.wo_s), qd, p.wo_npad, d, h, d);
+      gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
+    }
+    launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s);
+    {
+      GemmArgs a = gemm_base(u, d, c->W + lw.wr, nullptr, d, p.wr_npad, E, c->st<float>(p.rlog), E);
+      gemm_dense(c, p.wdt_other, EPI_F32, a, T, s);
+    }
+    RouteArgs ra;
+    memset(&ra, 0, sizeof ra);
+    ra.logits = c->st<float>(p.rlog); ra.T = T; ra.E = E; ra.k = k;
+    ra.topk_id = c->st<int32_t>(p.topk_id); ra.topk_gate = c->st<float>(p.topk_gate);
+    ra.blk_cnt = c->st<int32_t>(p.blk_cnt); ra.seg_off = c->st<int32_t>(p.seg_off);
+    ra.row_map = c->st<int32_t>(p.row_map); ra.slot = c->st<int32_t>(p.slot);
+    ra.tiles = c->st<int32_t>(p.tiles); ra.n_tiles = c->st<int32_t>(p.n_tiles);
+    ra.mrows = 16 * GROUPED_MT; ra.max_rows = (int)p.max_rows; ra.max_tiles = (int)p.max_tiles;
+    if (trace && c->trace_ids) {
+      ra.trace_ids = c->trace_ids + (int64_t)l * T * k;
+      ra.trace_gates = c->trace_gates + (int64_t)l * T * k;
+    }
+    launch_route(ra, s);
+    {
+      GemmArgs a = gemm_base(u, d, c->W + lw.gu, c->wt<float>(lw.gu_s), d, p.gu_npad, 2 * g.expert_hidden,
+                             c->st<void>(p.aperm), g.expert_hidden);
+      a.row_map = c->st<int32_t>(p.row_map);
+      a.w_gstride = p.gu_stride; a.s_gstride = p.gu_npad;
+      gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, s);
+    }
+    {
+      GemmArgs a = gemm_base(c->st<void>(p.aperm), g.expert_hidden, c->W + lw.dn, c->wt<float>(lw.dn_s),
+                             g.expert_hidden, p.dn_npad, d, c->st<void>(p.yperm), d);
+      a.w_gstride = p.dn_stride; a.s_gstride = p.dn_npad;
+      gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, s);
+    }
+    launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate), T, k, d, h, s);
+    if (g.shared_hidden) {
+      GemmArgs a = gemm_base(u, d, c->W + lw.sgu, nullptr, d, p.sgu_npad, 2 * g.shared_hidden,
+                             c->st<void>(p.sact), g.shared_hidden);
+      gemm_dense(c, p.wdt_other, EPI_SWIGLU, a, T, s);
+      GemmArgs b = gemm_base(c->st<void>(p.sact), g.shared_hidden, c->W + lw.sdn, nullptr, g.shared_hidden,
+                             p.sdn_npad, d, h, d);
+      gemm_dense(c, p.wdt_other, EPI_RESID, b, T, s);
+    }
+  }
+  if (head) {
+    launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s);
+    float* logits = c->st<float>(p.logits) + (int64_t)r0 * g.canvas_len * g.vocab;
+    GemmArgs a = gemm_base(u, d, c->W + p.lm, nullptr, d, p.lm_npad, g.vocab, logits, g.vocab);
+    gemm_dense(c, p.wdt_other, EPI_F32, a, T, s);
+  }
+}
+
+void sample(cd_ctx* c, int r0, int n_req, hipStream_t s) {
+  const Plan& p = c->p;
+  const cd_config& g = p.c;
+  const int C = g.canvas_len;
+  SampleArgs a;
+  memset(&a, 0, sizeof a);
+  a.logits = c->st<float>(p.logits) + (int64_t)r0 * C * g.vocab;
+  a.rows = n_req * C; a.V = g.vocab; a.C = C;
+  a.n_chunks = (int)p.n_chunks; a.chunk = g.vocab / a.n_chunks;
+  a.part = c->st<float4>(p.spart);
+  a.prev_a = c->st<int32_t>(p.argmax) + (int64_t)r0 * C;
+  a.tokens = c->st<int32_t>(p.canvas) + (int64_t)r0 * C;
+  a.argmax = c->st<int32_t>(p.argmax) + (int64_t)r0 * C;
+  a.lock = c->st<uint8_t>(p.lock) + (int64_t)r0 * C;
+  a.entropy = c->st<double>(p.entropy) + (int64_t)r0 * C;
+  a.pmax = c->st<double>(p.pmax) + (int64_t)r0 * C;
+  a.info = c->st<cd_step_info>(p.info) + r0;
+  a.canvas_in = c->st<int32_t>(p.canvas) + (int64_t)r0 * C;
+  a.rq = c->st<ReqDev>(p.rq) + r0;
+  a.req0 = r0;
+  a.max_steps = g.max_steps; a.lock_th = g.lock_threshold; a.stop_H = g.stop_entropy;
+  launch_sampler(a, s);
+}
+
+int32_t check_ctx(cd_ctx* c) { return c ? CD_OK : fail(CD_ERR_INVALID_ARG, "null context"); }
+
+int32_t step_internal(cd_ctx* c, int r0, int n_req, hipStream_t s) {
+  const cd_config& g = c->p.c;
+  for (int r = r0; r < r0 + n_req; ++r) {
+    const HostReq& q = c->req[r];
+    if (!q.active) return fail(CD_ERR_BAD_STATE, "request %d has no active canvas", r);
+    if (q.t >= g.max_steps) return fail(CD_ERR_BAD_STATE, "request %d reached the step cap", r);
+  }
+  forward(c, r0, n_req, g.canvas_len, c->st<int32_t>(c->p.canvas) + (int64_t)r0 * g.canvas_len, false, true,
+          true, s);
+  sample(c, r0, n_req, s);
+  for (int r = r0; r < r0 + n_req; ++r) c->req[r].t++;
+  return hip_status("denoise step");
+}
+
+int32_t read_info(cd_ctx* c, int r, cd_step_info* out, hipStream_t s) {
+  if (hipMemcpyAsync(out, c->st<cd_step_info>(c->p.info) + r, sizeof(cd_step_info), hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return hip_status("step info copy");
+  if (hipStreamSynchronize(s) != hipSuccess) return hip_status("stream sync");
+  return CD_OK;
+}
+
+PackDesc desc_for(const cd_ctx* c, int kind, int layer, int expert, int& status) {
+  const Plan& p = c->p;
+  const cd_config& g = p.c;
+  PackDesc d;
+  memset(&d, 0, sizeof d);
+  d.only_sel = -1;
+  status = CD_OK;
+  const int dh = g.head_dim, dm = g.d_model, E = g.n_experts;
+  const bool layered = kind >= CD_W_Q;
+  if (layered && (layer < 0 || layer >= g.n_layers)) { status = fail(CD_ERR_INVALID_ARG, "layer out of range"); return d; }
+  const bool per_expert = kind == CD_W_GATE || kind == CD_W_UP || kind == CD_W_DOWN;
+  if (per_expert && (expert < 0 || expert >= E)) { status = fail(CD_ERR_INVALID_ARG, "expert out of range"); return d; }
+  if ((kind >= CD_W_SHARED_GATE) && !g.shared_hidden) { status = fail(CD_ERR_INVALID_ARG, "no shared FFN"); return d; }
+  const LayerOff* lw = layered ? &p.layer[layer] : nullptr;
+  uint8_t* W = c->W;
+  switch (kind) {
+    case CD_W_EMBED:
+      d.dst = W + p.embed; d.dt = p.wdt_other; d.perm = PERM_NONE; d.Npad = g.vocab; d.K = dm; d.rowmajor = 1;
+      d.n_rows_src[0] = g.vocab; break;
+    case CD_W_LM:
+      d.dst = W + p.lm; d.dt = p.wdt_other; d.perm = PERM_NONE; d.Npad = p.lm_npad; d.K = dm; d.n_rows_src[0] = g.vocab;
+      break;
+    case CD_W_Q: case CD_W_K: case CD_W_V:
+      d.dst = W + lw->qkv; d.scale = c->wt<float>(lw->qkv_s); d.dt = p.wdt_attn; d.perm = PERM_QKV;
+      d.Npad = p.qkv_npad; d.K = dm; d.Hq = g.n_q_heads; d.Hkv = g.n_kv_heads; d.dh = dh;
+      d.only_sel = kind - CD_W_Q; break;
+    case CD_W_O:
+      d.dst = W + lw->wo; d.scale = c->wt<float>(lw->wo_s); d.dt = p.wdt_attn; d.perm = PERM_NONE;
+      d.Npad = p.wo_npad; d.K = g.n_q_heads * dh; d.n_rows_src[0] = dm; break;
+    case CD_W_ROUTER:
+      d.dst = W + lw->wr; d.dt = p.wdt_other; d.perm = PERM_NONE; d.Npad = p.wr_npad; d.K = dm; d.n_rows_src[0] = E;
+      break;
+    case CD_W_GATE: case CD_W_UP:
+      d.dst = W + lw->gu + p.gu_stride * expert;
+      d.scale = lw->gu_s >= 0 ? c->wt<float>(lw->gu_s) + (int64_t)p.gu_npad * expert : nullptr;
+      d.dt = p.wdt_exp; d.perm = PERM_GU; d.Npad = p.gu_npad; d.K = dm;
+      d.n_rows_src[0] = d.n_rows_src[1] = g.expert_hidden; d.only_sel = kind - CD_W_GATE; break;
+    case CD_W_DOWN:
+      d.dst = W + lw->dn + p.dn_stride * expert;
+      d.scale = lw->dn_s >= 0 ? c->wt<float>(lw->dn_s) + (int64_t)p.dn_npad * expert : nullptr;
+      d.dt = p.wdt_exp; d.perm = PERM_NONE; d.Npad = p.dn_npad; d.K = g.expert_hidden; d.n_rows_src[0] = dm; break;
+    case CD_W_SHARED_GATE: case CD_W_SHARED_UP:
+      d.dst = W + lw->sgu; d.dt = p.wdt_other; d.perm = PERM_GU; d.Npad = p.sgu_npad; d.K = dm;
+      d.n_rows_src[0] = d.n_rows_src[1] = g.shared_hidden; d.only_sel = kind - CD_W_SHARED_GATE; break;
+    case CD_W_SHARED_DOWN:
+      d.dst = W + lw->sdn; d.dt = p.wdt_other; d.perm = PERM_NONE; d.Npad = p.sdn_npad; d.K = g.shared_hidden;
+      d.n_rows_src[0] = dm; break;
+    default:
+      status = fail(CD_ERR_INVALID_ARG, "unknown weight kind %d", kind);
+  }
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t cd_weights_bytes(const cd_config* cfg, size_t* bytes) {
+  int32_t st = validate_config(cfg);
+  if (st) return st;
+  if (!bytes) return fail(CD_ERR_INVALID_ARG, "null bytes");
+  *bytes = (size_t)make_plan(*cfg).weights_bytes;
+  return CD_OK;
+}
+
+int32_t cd_state_bytes(const cd_config* cfg, size_t* bytes) {
+  int32_t st = validate_config(cfg);
+  if (st) return st;
+  if (!bytes) return fail(CD_ERR_INVALID_ARG, "null bytes");
+  *bytes = (size_t)make_plan(*cfg).state_bytes;
+  return CD_OK;
+}
+
+int32_t cd_ctx_create(const cd_config* cfg, void* d_weights, void* d_state, cd_ctx** out) {
+  int32_t st = validate_config(cfg);
+  if (st) return st;
+  if (!d_weights || !d_state || !out) return fail(CD_ERR_INVALID_ARG, "null buffer or output pointer");
+  if ((reinterpret_cast<uintptr_t>(d_weights) | reinterpret_cast<uintptr_t>(d_state)) % ALIGN)
+    return fail(CD_ERR_INVALID_ARG, "buffers must be 256-byte aligned");
+  cd_ctx* c = new cd_ctx;
+  c->p = make_plan(*cfg);
+  c->W = reinterpret_cast<uint8_t*>(d_weights);
+  c->S = reinterpret_cast<uint8_t*>(d_state);
+  c->req.assign(cfg->max_requests, HostReq());
+  *out = c;
+  g_err.clear();
+  return CD_OK;
+}
+
+int32_t cd_ctx_destroy(cd_ctx* ctx) {
+  delete ctx;
+  return CD_OK;
+}
+
+int32_t cd_reset(cd_ctx* c, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  hipStream_t s = strm(stream);
+  if (hipMemsetAsync(c->S, 0, c->p.state_bytes, s) != hipSuccess) return hip_status("state clear");
+  launch_rope_table(c->st<float>(c->p.rope), c->p.ctx, c->p.c.head_dim, c->p.c.rope_theta, s);
+  for (auto& r : c->req) r = HostReq();
+  return hip_status("reset");
+}
+
+int32_t cd_synth_weights(cd_ctx* c, uint64_t seed, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  hipStream_t s = strm(stream);
+  const Plan& p = c->p;
+  const cd_config& g = p.c;
+  const uint32_t S = 8 + 3 * g.n_experts;
+  int status;
+  PackDesc d = desc_for(c, CD_W_EMBED, 0, 0, status);
+  d.tau[0] = 0;
+  launch_synth(d, 1, 0, 0, 0, seed, s);
+  d = desc_for(c, CD_W_LM, 0, 0, status);
+  d.tau[0] = 1;
+  launch_synth(d, 1, 0, 0, 0, seed, s);
+  for (int l = 0; l < g.n_layers; ++l) {
+    const uint32_t b = 2 + l * S;
+    d = desc_for(c, CD_W_Q, l, 0, status);
+    d.only_sel = -1; d.tau[0] = b; d.tau[1] = b + 1; d.tau[2] = b + 2;
+    launch_synth(d, 1, 0, 0, 0, seed, s);
+    d = desc_for(c, CD_W_O, l, 0, status);
+    d.tau[0] = b + 3;
+    launch_synth(d, 1, 0, 0, 0, seed, s);
+    d = desc_for(c, CD_W_ROUTER, l, 0, status);
+    d.tau[0] = b + 4;
+    launch_synth(d, 1, 0, 0, 0, seed, s);
+    d = desc_for(c, CD_W_GATE, l, 0, status);
+    d.only_sel = -1; d.tau[0] = b + 5; d.tau[1] = b + 6;
+    launch_synth(d, g.n_experts, p.gu_stride, p.gu_npad, 3, seed, s);
+    d = desc_for(c, CD_W_DOWN, l, 0, status);
+    d.tau[0] = b + 7;
+    launch_synth(d, g.n_experts, p.dn_stride, p.dn_npad, 3, seed, s);
+    if (g.shared_hidden) {
+      const uint32_t sb = b + 5 + 3 * g.n_experts;
+      d = desc_for(c, CD_W_SHARED_GATE, l, 0, status);
+      d.only_sel = -1; d.tau[0] = sb; d.tau[1] = sb + 1;
+      launch_synth(d, 1, 0, 0, 0, seed, s);
+      d = desc_for(c, CD_W_SHARED_DOWN, l, 0, status);
+      d.tau[0] = sb + 2;
+      launch_synth(d, 1, 0, 0, 0, seed, s);
+    }
+  }
+  return hip_status("synth weights");
+}
+
+int32_t cd_set_weight(cd_ctx* c, int32_t kind, int32_t layer, int32_t expert, const float* d_logical, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (!d_logical) return fail(CD_ERR_INVALID_ARG, "null source");
+  int status;
+  PackDesc d = desc_for(c, kind, layer, expert, status);
+  if (status) return status;
+  const float* src[3] = {nullptr, nullptr, nullptr};
+  src[d.only_sel < 0 ? 0 : d.only_sel] = d_logical;
+  if (d.perm == PERM_QKV) {   // rows of each part: Hq*dh, Hkv*dh, Hkv*dh
+    d.n_rows_src[0] = c->p.c.n_q_heads * c->p.c.head_dim;
+    d.n_rows_src[1] = d.n_rows_src[2] = c->p.c.n_kv_heads * c->p.c.head_dim;
+  }
+  launch_pack(d, src[0], src[1], src[2], strm(stream));
+  return hip_status("set weight");
+}
+
+int32_t cd_get_weight(cd_ctx* c, int32_t kind, int32_t layer, int32_t expert, float* d_logical, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (!d_logical) return fail(CD_ERR_INVALID_ARG, "null destination");
+  int status;
+  PackDesc d = desc_for(c, kind, layer, expert, status);
+  if (status) return status;
+  float* dst[3] = {nullptr, nullptr, nullptr};
+  dst[d.only_sel < 0 ? 0 : d.only_sel] = d_logical;
+  launch_unpack(d, dst[0], dst[1], dst[2], strm(stream));
+  return hip_status("get weight");
+}
+
+int32_t cd_prefill(cd_ctx* c, int32_t req, const int32_t* d_ids, int32_t n, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  const cd_config& g = c->p.c;
+  if (req < 0 || req >= g.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
+  if (!d_ids || n < 1 || n > g.max_prefill) return fail(CD_ERR_INVALID_ARG, "prefill needs 1..max_prefill ids");
+  HostReq& q = c->req[req];
+  if (q.active) return fail(CD_ERR_BAD_STATE, "request %d has an active canvas", req);
+  if ((int64_t)q.P + n + g.canvas_len > g.max_ctx) return fail(CD_ERR_CAPACITY, "KV cache too small for prefill");
+  hipStream_t s = strm(stream);
+  forward(c, req, 1, n, d_ids, true, false, false, s);
+  launch_advance(c->st<ReqDev>(c->p.rq), req, n, 0, s);
+  q.P += n;
+  return hip_status("prefill");
+}
+
+int32_t cd_init_canvas(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  const cd_config& g = c->p.c;
+  if (req < 0 || req >= g.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
+  if (block < 0) return fail(CD_ERR_INVALID_ARG, "negative block index");
+  HostReq& q = c->req[req];
+  if (q.active) return fail(CD_ERR_BAD_STATE, "request %d already has an active canvas", req);
+  if ((int64_t)q.P + g.canvas_len > g.max_ctx) return fail(CD_ERR_CAPACITY, "KV cache full");
+  launch_init_canvas(c->st<int32_t>(c->p.canvas), c->st<ReqDev>(c->p.rq), req, g.canvas_len, g.vocab, seed, block,
+                     strm(stream));
+  q.active = true; q.t = 0; q.block = block; q.seed = seed;
+  return hip_status("init canvas");
+}
+
+int32_t cd_denoise_step(cd_ctx* c, int32_t n_req, cd_step_info* d_info, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (n_req < 1 || n_req > c->p.c.max_requests) return fail(CD_ERR_INVALID_ARG, "n_req out of range");
+  if (!d_info) return fail(CD_ERR_INVALID_ARG, "null step info");
+  hipStream_t s = strm(stream);
+  if (int32_t st = step_internal(c, 0, n_req, s)) return st;
+  if (hipMemcpyAsync(d_info, c->st<cd_step_info>(c->p.info), sizeof(cd_step_info) * n_req, hipMemcpyDeviceToDevice,
+                     s) != hipSuccess)
+    return hip_status("step info copy");
+  return CD_OK;
+}
+
+int32_t cd_read_step_info(cd_ctx* c, const cd_step_info* d_info, int32_t n_req, cd_step_info* h_info, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (!d_info || !h_info || n_req < 1) return fail(CD_ERR_INVALID_ARG, "bad step info arguments");
+  hipStream_t s = strm(stream);
+  if (hipMemcpyAsync(h_info, d_info, sizeof(cd_step_info) * n_req, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return hip_status("step info copy");
+  if (hipStreamSynchronize(s) != hipSuccess) return hip_status("stream sync");
+  return CD_OK;
+}
+
+int32_t cd_commit_block(cd_ctx* c, int32_t req, int32_t* d_out_ids, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  const cd_config& g = c->p.c;
+  if (req < 0 || req >= g.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
+  if (!d_out_ids) return fail(CD_ERR_INVALID_ARG, "null output ids");
+  HostReq& q = c->req[req];
+  if (!q.active || q.t < 1) return fail(CD_ERR_BAD_STATE, "request %d has no denoised canvas to commit", req);
+  hipStream_t s = strm(stream);
+  cd_step_info info;
+  if (int32_t st = read_info(c, req, &info, s)) return st;
+  int32_t* a = c->st<int32_t>(c->p.argmax) + (int64_t)req * g.canvas_len;
+  if (!info.canvas_is_argmax) forward(c, req, 1, g.canvas_len, a, false, false, false, s);
+  launch_copy_i32(a, d_out_ids, g.canvas_len, s);
+  launch_advance(c->st<ReqDev>(c->p.rq), req, g.canvas_len, 1, s);
+  q.P += g.canvas_len;
+  q.active = false;
+  return hip_status("commit");
+}
+
+int32_t cd_generate(cd_ctx* c, int32_t req, const int32_t* d_prefix, int32_t n_prefix, int32_t n_blocks,
+                    uint64_t seed, int32_t* d_out_ids, int32_t* h_steps_per_block, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  const cd_config& g = c->p.c;
+  if (req < 0 || req >= g.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
+  if (n_blocks < 1 || !d_out_ids || !h_steps_per_block || n_prefix < 0 || (n_prefix > 0 && !d_prefix))
+    return fail(CD_ERR_INVALID_ARG, "bad generate arguments");
+  HostReq& q = c->req[req];
+  if (q.active) return fail(CD_ERR_BAD_STATE, "request %d has an active canvas", req);
+  if ((int64_t)q.P + n_prefix + (int64_t)n_blocks * g.canvas_len > g.max_ctx)
+    return fail(CD_ERR_CAPACITY, "KV cache too small for %d blocks", n_blocks);
+  if (n_prefix > g.max_prefill) return fail(CD_ERR_INVALID_ARG, "prefix longer than max_prefill");
+  hipStream_t s = strm(stream);
+  if (n_prefix > 0)
+    if (int32_t st = cd_prefill(c, req, d_prefix, n_prefix, stream)) return st;
+  for (int b = 0; b < n_blocks; ++b) {
+    if (int32_t st = cd_init_canvas(c, req, seed, b, stream)) return st;
+    int steps = 0;
+    for (;;) {
+      if (int32_t st = step_internal(c, req, 1, s)) return st;
+      cd_step_info info;
+      if (int32_t st = read_info(c, req, &info, s)) return st;
+      steps = info.step;
+      if (info.nonfinite) return fail(CD_ERR_NUMERIC, "non-finite logits at block %d pass %d", b, steps);
+      if (info.stop) break;
+    }
+    h_steps_per_block[b] = steps;
+    if (int32_t st = cd_commit_block(c, req, d_out_ids + (int64_t)b * g.canvas_len, stream)) return st;
+  }
+  return hip_status("generate");
+}
+
+int32_t cd_sample_workspace_bytes(int32_t rows, int32_t vocab, size_t* bytes) {
+  if (rows < 1 || vocab < 128 || vocab % 128 || !bytes) return fail(CD_ERR_INVALID_ARG, "bad sampler shape");
+  *bytes = (size_t)16 * rows * sampler_chunks(vocab);
+  return CD_OK;
+}
+
+int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows, const int32_t* d_prev_argmax,
+                       uint64_t seed, int32_t step, int32_t block, int32_t req0, int32_t* d_tokens,
+                       int32_t* d_argmax, uint8_t* d_lock, double* d_entropy, double* d_pmax,
+                       cd_step_info* d_info, void* d_workspace, void* stream) {
+  if (!cfg) return fail(CD_ERR_INVALID_ARG, "null config");
+  if (cfg->vocab < 128 || cfg->vocab % 128 || cfg->canvas_len < 1)
+    return fail(CD_ERR_UNSUPPORTED, "vocab must be a positive multiple of 128");
+  if (rows < 1 || rows % cfg->canvas_len) return fail(CD_ERR_INVALID_ARG, "rows must be a multiple of canvas_len");
+  if (!d_logits || !d_tokens || !d_argmax || !d_lock || !d_entropy || !d_pmax || !d_info || !d_workspace)
+    return fail(CD_ERR_INVALID_ARG, "null buffer");
+  if (step < 1 || block < 0 || req0 < 0) return fail(CD_ERR_INVALID_ARG, "bad step/block/request");
+  SampleArgs a;
+  memset(&a, 0, sizeof a);
+  a.logits = d_logits; a.rows = rows; a.V = cfg->vocab; a.C = cfg->canvas_len;
+  a.n_chunks = sampler_chunks(cfg->vocab); a.chunk = cfg->vocab / a.n_chunks;
+  a.part = reinterpret_cast<float4*>(d_workspace);
+  a.prev_a = d_prev_argmax; a.tokens = d_tokens; a.argmax = d_argmax; a.lock = d_lock;
+  a.entropy = d_entropy; a.pmax = d_pmax; a.info = d_info; a.canvas_in = nullptr; a.rq = nullptr;
+  a.seed = seed; a.step = step; a.block = block; a.req0 = req0;
+  a.max_steps = cfg->max_steps; a.lock_th = cfg->lock_threshold; a.stop_H = cfg->stop_entropy;
+  launch_sampler(a, strm(stream));
+  return hip_status("sample step");
+}
+
+int32_t cd_get_buffer(cd_ctx* c, int32_t which, void** d_ptr, size_t* bytes) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (!d_ptr) return fail(CD_ERR_INVALID_ARG, "null output");
+  const Plan& p = c->p;
+  const cd_config& g = p.c;
+  const int64_t RC = (int64_t)g.max_requests * g.canvas_len;
+  const int ae = esize(p.adt);
+  int64_t off, n;
+  switch (which) {
+    case CD_BUF_LOGITS: off = p.logits; n = 4 * RC * g.vocab; break;
+    case CD_BUF_CANVAS: off = p.canvas; n = 4 * RC; break;
+    case CD_BUF_ARGMAX: off = p.argmax; n = 4 * RC; break;
+    case CD_BUF_ENTROPY: off = p.entropy; n = 8 * RC; break;
+    case CD_BUF_PMAX: off = p.pmax; n = 8 * RC; break;
+    case CD_BUF_LOCK: off = p.lock; n = RC; break;
+    case CD_BUF_KCACHE: off = p.kcache; n = (int64_t)ae * p.kv_req_stride * g.max_requests; break;
+    case CD_BUF_VCACHE: off = p.vcache; n = (int64_t)ae * p.kv_req_stride * g.max_requests; break;
+    case CD_BUF_HIDDEN: off = p.h; n = 4LL * p.Tmax * g.d_model; break;
+    default: return fail(CD_ERR_INVALID_ARG, "unknown buffer %d", which);
+  }
+  *d_ptr = c->S + off;
+  if (bytes) *bytes = (size_t)n;
+  return CD_OK;
+}
+
+int32_t cd_get_length(cd_ctx* c, int32_t req, int32_t* P) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (req < 0 || req >= c->p.c.max_requests || !P) return fail(CD_ERR_INVALID_ARG, "bad request or output");
+  *P = c->req[req].P;
+  return CD_OK;
+}
+
+int32_t cd_set_trace(cd_ctx* c, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates) {
+  if (int32_t st = check_ctx(c)) return st;
+  c->trace_h = d_h_layers;
+  c->trace_ids = d_topk_ids;
+  c->trace_gates = d_topk_gates;
+  return CD_OK;
+}
+
+const char* cd_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Device-side helpers shared by the canvas-denoise kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cd {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// ---- bf16 -------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+// fp32 -> bf16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- E4M3FN (OCP) -> fp32, exact ----------------------------------------
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t s = (b & 0x80u) << 24;
+  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// ---- Philox4x32-10 (Salmon et al., SC'11) -------------------------------
+struct u4 { uint32_t x, y, z, w; };
+__device__ __forceinline__ u4 philox(u4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    u4 n;
+    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.y = (uint32_t)p1;
+    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.w = (uint32_t)p0;
+    c = n;
+  }
+  return c;
+}
+
+// uniform token id in [0, V) for (seed; pos, step, block, req), tag 0
+__device__ __forceinline__ int32_t canvas_token(uint64_t seed, uint32_t pos, uint32_t step,
+                                                uint32_t block, uint32_t req, uint32_t V) {
+  u4 c = {pos, step, block, req};
+  u4 r = philox(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return (int32_t)(((uint64_t)r.x * V) >> 32);
+}
+
+// ---- wave reductions -----------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace cd

@@ -1,0 +1,111 @@
+// Small kernels of the step: embedding gather, RMSNorm (unit gain), rotary
+// table, canvas start (uniform Philox token ids), request bookkeeping.
+#include "common.h"
+#include "kernels.h"
+
+namespace cd {
+
+// h[t] = E[ids[t]] (storage fp32 or bf16), residual stream kept in fp32
+// ids outside [0, V) are clamped (the embedding table is never read out of range)
+__global__ __launch_bounds__(256) void k_embed(int edt, const void* E, const int32_t* ids, int V, int d, float* h) {
+  const int t = blockIdx.x;
+  const int64_t row = min(max(ids[t], 0), V - 1);
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = edt == DT_F32 ? reinterpret_cast<const float*>(E)[row * d + c]
+                            : bf2f(reinterpret_cast<const uint16_t*>(E)[row * d + c]);
+    h[(int64_t)t * d + c] = v;
+  }
+}
+void launch_embed(int edt, const void* E, const int32_t* ids, int T, int V, int d, float* h, hipStream_t s) {
+  hipLaunchKernelGGL(k_embed, dim3(T), dim3(256), 0, s, edt, E, ids, V, d, h);
+}
+
+// u = h / sqrt(mean(h^2) + eps), one workgroup per row
+template <int AT>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int d, float eps, void* u) {
+  __shared__ float sh[4];
+  const int t = blockIdx.x;
+  const float* x = h + (int64_t)t * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    float4 v = *reinterpret_cast<const float4*>(x + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = sh[0] + sh[1] + sh[2] + sh[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    float4 v = *reinterpret_cast<const float4*>(x + c);
+    if constexpr (AT == DT_F32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(u) + (int64_t)t * d + c) =
+          make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    } else {
+      uint2 p;
+      p.x = (uint32_t)f2bf(v.x * inv) | ((uint32_t)f2bf(v.y * inv) << 16);
+      p.y = (uint32_t)f2bf(v.z * inv) | ((uint32_t)f2bf(v.w * inv) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(u) + (int64_t)t * d + c) = p;
+    }
+  }
+}
+void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s) {
+  if (adt == DT_F32) hipLaunchKernelGGL(k_rmsnorm<DT_F32>, dim3(T), dim3(256), 0, s, h, d, eps, u);
+  else hipLaunchKernelGGL(k_rmsnorm<DT_BF16>, dim3(T), dim3(256), 0, s, h, d, eps, u);
+}
+
+// cs[pos][i] = (cos, sin)(pos * theta^(-2i/dh)), computed in fp64
+__global__ void k_rope_table(float* cs, int max_ctx, int dh, double theta) {
+  const int half = dh / 2;
+  const int64_t n = (int64_t)max_ctx * half;
+  for (int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(j / half), i = (int)(j % half);
+    const double ang = (double)pos * pow(theta, -2.0 * i / dh);
+    cs[2 * j] = (float)cos(ang);
+    cs[2 * j + 1] = (float)sin(ang);
+  }
+}
+void launch_rope_table(float* cs, int max_ctx, int dh, float theta, hipStream_t s) {
+  hipLaunchKernelGGL(k_rope_table, dim3(1024), dim3(256), 0, s, cs, max_ctx, dh, (double)theta);
+}
+
+__global__ void k_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed, int block) {
+  for (int i = threadIdx.x; i < C; i += blockDim.x)
+    canvas[(int64_t)req * C + i] = canvas_token(seed, i, 0, block, req, V);
+  if (threadIdx.x == 0) {
+    rq[req].t = 0;
+    rq[req].block = block;
+    rq[req].active = 1;
+    rq[req].seed = seed;
+  }
+}
+void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed, int block,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_init_canvas, dim3(1), dim3(256), 0, s, canvas, rq, req, C, V, seed, block);
+}
+
+__global__ void k_advance(ReqDev* rq, int req, int dP, int clear_active) {
+  rq[req].P += dP;
+  if (clear_active) rq[req].active = 0;
+}
+void launch_advance(ReqDev* rq, int req, int dP, int clear_active, hipStream_t s) {
+  hipLaunchKernelGGL(k_advance, dim3(1), dim3(1), 0, s, rq, req, dP, clear_active);
+}
+
+__global__ void k_copy_i32(const int32_t* src, int32_t* dst, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = src[i];
+}
+void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_i32, dim3((n + 255) / 256), dim3(256), 0, s, src, dst, n);
+}
+__global__ void k_copy_f32(const float* src, float* dst, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s) {
+  int64_t b = (n + 255) / 256;
+  if (b > 65536) b = 65536;
+  hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)b), dim3(256), 0, s, src, dst, n);
+}
+
+}  // namespace cd

@@ -1,0 +1,180 @@
+// MoE routing: top-k over router logits, deterministic counting sort of the
+// (token, slot) assignments by expert, the tile table of the grouped GEMM,
+// and the gate-weighted combine back into the residual stream.
+//
+// Top-k: one wave per token; k rounds of a wave-wide argmax (ties to the
+// lower expert id); gates = softmax over the k selected logits.
+// Sort: assignments (t, j) in order t*k + j are cut into blocks of 512; one
+// thread per expert counts its assignments per block, a single workgroup
+// turns the counts into per-block bases and expert segments padded to the
+// GEMM row tile, and the same per-expert scan places every assignment.  The
+// permuted order is therefore (expert, token, slot) regardless of timing.
+#include "common.h"
+#include "kernels.h"
+
+namespace cd {
+
+constexpr int ROUTE_BLK = 512;
+
+__global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const float* r = a.logits + (int64_t)t * a.E;
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = lane + 64 * i;
+    v[i] = e < a.E ? r[e] : -INFINITY;
+  }
+  float sel[16];
+  int ids[16];
+  for (int j = 0; j < a.k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = lane + 64 * i;
+      if (e < a.E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      float ov = __shfl_xor(bv, o, 64);
+      int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    sel[j] = bv;
+    ids[j] = bi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == bi) v[i] = -INFINITY;
+  }
+  if (lane == 0) {
+    float mx = sel[0], sum = 0.f;
+    float g[16];
+    for (int j = 0; j < a.k; ++j) { g[j] = expf(sel[j] - mx); sum += g[j]; }
+    for (int j = 0; j < a.k; ++j) {
+      a.topk_id[(int64_t)t * a.k + j] = ids[j];
+      a.topk_gate[(int64_t)t * a.k + j] = g[j] / sum;
+      if (a.trace_ids) {
+        a.trace_ids[(int64_t)t * a.k + j] = ids[j];
+        a.trace_gates[(int64_t)t * a.k + j] = g[j] / sum;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_route_count(RouteArgs a) {
+  __shared__ int32_t ex[ROUTE_BLK];
+  const int b = blockIdx.x;
+  const int n = a.T * a.k;
+  const int beg = b * ROUTE_BLK, cnt = min(ROUTE_BLK, n - beg);
+  for (int i = threadIdx.x; i < cnt; i += 256) ex[i] = a.topk_id[beg + i];
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e >= a.E) return;
+  int c = 0;
+  for (int i = 0; i < cnt; ++i) c += (ex[i] == e);
+  a.blk_cnt[(int64_t)b * a.E + e] = c;
+}
+
+// single workgroup: per-block bases, padded segments, tile table, pad rows
+__global__ __launch_bounds__(256) void k_route_scan(RouteArgs a, int n_blk) {
+  __shared__ int32_t padded[256], tcount[256];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < a.E) {
+    for (int b = 0; b < n_blk; ++b) {
+      int c = a.blk_cnt[(int64_t)b * a.E + e];
+      a.blk_cnt[(int64_t)b * a.E + e] = total;   // exclusive base within the expert
+      total += c;
+    }
+  }
+  const int pad = (total + a.mrows - 1) / a.mrows * a.mrows;
+  padded[e] = e < a.E ? pad : 0;
+  tcount[e] = e < a.E ? pad / a.mrows : 0;
+  __syncthreads();
+  if (e == 0) {
+    int acc = 0, tacc = 0;
+    for (int i = 0; i < a.E; ++i) {
+      int p = padded[i], tc = tcount[i];
+      padded[i] = acc; tcount[i] = tacc;
+      acc += p; tacc += tc;
+    }
+    a.seg_off[a.E] = acc;
+    *a.n_tiles = tacc;
+  }
+  __syncthreads();
+  if (e >= a.E) return;
+  const int off = padded[e];
+  a.seg_off[e] = off;
+  int t0 = tcount[e];
+  for (int i = 0; i * a.mrows < total; ++i) {
+    int32_t* tl = a.tiles + 4 * (int64_t)(t0 + i);
+    tl[0] = e;
+    tl[1] = off + i * a.mrows;
+    tl[2] = min(a.mrows, total - i * a.mrows);
+    tl[3] = 0;
+  }
+  for (int r = off + total; r < off + pad; ++r) a.row_map[r] = -1;
+}
+
+__global__ __launch_bounds__(256) void k_route_place(RouteArgs a) {
+  __shared__ int32_t ex[ROUTE_BLK];
+  const int b = blockIdx.x;
+  const int n = a.T * a.k;
+  const int beg = b * ROUTE_BLK, cnt = min(ROUTE_BLK, n - beg);
+  for (int i = threadIdx.x; i < cnt; i += 256) ex[i] = a.topk_id[beg + i];
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e >= a.E) return;
+  int slot = a.seg_off[e] + a.blk_cnt[(int64_t)b * a.E + e];
+  for (int i = 0; i < cnt; ++i) {
+    if (ex[i] == e) {
+      const int asg = beg + i;
+      a.slot[asg] = slot;
+      a.row_map[slot] = asg / a.k;
+      ++slot;
+    }
+  }
+}
+
+void launch_route(const RouteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  const int n_blk = (a.T * a.k + ROUTE_BLK - 1) / ROUTE_BLK;
+  hipLaunchKernelGGL(k_route_count, dim3(n_blk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, s, a, n_blk);
+  hipLaunchKernelGGL(k_route_place, dim3(n_blk), dim3(256), 0, s, a);
+}
+
+// h[t] += sum_j gate[t][j] * Y[slot[t][j]]   (j in order: deterministic)
+template <int AT>
+__global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* slot, const float* gate, int k,
+                                                 int d, float* h) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    float4 acc = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
+    for (int j = 0; j < k; ++j) {
+      const float g = gate[(int64_t)t * k + j];
+      const int64_t row = slot[(int64_t)t * k + j];
+      float y0, y1, y2, y3;
+      if constexpr (AT == DT_F32) {
+        float4 y = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Yp) + row * d + c);
+        y0 = y.x; y1 = y.y; y2 = y.z; y3 = y.w;
+      } else {
+        uint2 y = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Yp) + row * d + c);
+        y0 = bf2f(y.x & 0xFFFF); y1 = bf2f(y.x >> 16); y2 = bf2f(y.y & 0xFFFF); y3 = bf2f(y.y >> 16);
+      }
+      acc.x += g * y0; acc.y += g * y1; acc.z += g * y2; acc.w += g * y3;
+    }
+    *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = acc;
+  }
+}
+
+void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, int T, int k, int d, float* h,
+                    hipStream_t s) {
+  if (adt == DT_F32) hipLaunchKernelGGL(k_combine<DT_F32>, dim3(T), dim3(256), 0, s, Yp, slot, gate, k, d, h);
+  else hipLaunchKernelGGL(k_combine<DT_BF16>, dim3(T), dim3(256), 0, s, Yp, slot, gate, k, d, h);
+}
+
+}  // namespace cd

@@ -1,0 +1,163 @@
+// Kernel argument structs and host launchers (internal to libcd).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cd {
+
+// ---------------------------------------------------------------------------
+// Packed weight layout.  A weight W[N][K] (output rows x contraction) is
+// stored as 16-row x KF-column fragment tiles of 1024 bytes: tile (nt, kt)
+// at byte ((nt * (K/KF)) + kt) * 1024; lane l of a wave holds the 16 bytes of
+// row nt*16 + l%16, columns kt*KF + (l/16)*(KF/4) + [0, KF/4).  KF = 64 / size
+// of the element (fp32 16, bf16 32, fp8 64).  One 16-byte load per lane then
+// fetches a whole tile as one contiguous 1 KB wave access, already in MFMA
+// operand order.  N is padded to a multiple of 32 (zero rows).
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int esize(int dt) { return dt == 0 ? 4 : dt == 1 ? 2 : 1; }
+__host__ __device__ inline int kfrag(int dt) { return 64 / esize(dt); }
+__host__ __device__ inline int64_t packed_bytes(int64_t Npad, int64_t K, int dt) {
+  return Npad * K * esize(dt);
+}
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Row permutations applied when packing.
+enum { PERM_NONE = 0, PERM_QKV = 1, PERM_GU = 2 };
+
+enum { EPI_F32 = 0, EPI_ROWS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
+
+struct GemmArgs {
+  // activations: row-major [rows][ldx], element type = act dtype
+  const void* X;
+  int64_t ldx;
+  const int32_t* row_map;  // tile row -> source row of X, or null (identity)
+  // weights: packed tiles, one block of tiles per group
+  const uint8_t* W;
+  int64_t w_gstride;       // bytes between groups
+  const float* wscale;     // fp8 per-row scales [group][Npad], or null
+  int64_t s_gstride;
+  int K, Nt, N, n_chunks;  // Nt = packed 16-row tiles; N = logical outputs
+  // work tiles: grouped (device table) or dense (M rows)
+  const int32_t* tiles;    // [max_tiles][4]: group, row0, rows, 0
+  const int32_t* n_tiles;  // device count for grouped launches
+  int max_tiles;
+  int M;
+  int chunk_major;
+  // epilogue
+  void* Y;
+  int64_t ldy;
+  // EPI_QKV
+  void* kc;
+  void* vc;
+  int64_t kv_req_stride;   // elements between requests (same layer)
+  int max_ctx, Hq, Hkv, dh;
+  int rows_per_req;
+  const int32_t* pos0;     // per request: position of its row 0
+  int pos0_stride;         // int32 stride between requests in pos0
+  const float* rope_cs;    // [max_ctx][dh/2] (cos, sin) pairs, or null
+};
+
+void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
+
+// ---- weight synthesis / packing --------------------------------------------
+struct PackDesc {
+  uint8_t* dst;        // packed tiles (or row-major for embedding)
+  float* scale;        // fp8 per-row scales or null
+  int dt;              // storage dtype
+  int perm;            // PERM_*
+  int Npad, K;
+  int rowmajor;        // 1: plain row-major [N][K] (embedding)
+  int n_rows_src[3];   // logical rows of each source tensor
+  int Hq, Hkv, dh;     // PERM_QKV
+  uint32_t tau[3];     // tensor ids of the sources (synthesis)
+  int only_sel;        // >= 0: touch only rows of that source (pack / unpack)
+};
+void launch_synth(const PackDesc& d, int n_groups, int64_t dst_gstride, int64_t scale_gstride,
+                  int tau_gstride, uint64_t seed, hipStream_t s);
+void launch_pack(const PackDesc& d, const float* src0, const float* src1, const float* src2,
+                 hipStream_t s);
+void launch_unpack(const PackDesc& d, float* out0, float* out1, float* out2, hipStream_t s);
+
+// ---- attention ---------------------------------------------------------------
+struct AttnArgs {
+  const void* Q;          // [rows][Hq*dh] act
+  void* O;                // [rows][Hq*dh] act
+  const void* kc;         // layer base of request 0: [Hkv][max_ctx][dh]
+  const void* vc;         // layer base of request 0: [Hkv][dh][max_ctx]
+  int64_t kv_req_stride;
+  int max_ctx, Hq, Hkv, dh;
+  int rows_per_req, n_req;
+  const int32_t* pos0;    // per-request position of row 0 (= committed length)
+  int pos0_stride;
+  int causal;             // 0: keys [0, pos0+rows) all visible; 1: key <= query pos
+  int n_split, split_len; // key range split
+  float* part_o;          // [n_split][rows_total][Hq][dh] f32
+  float* part_ml;         // [n_split][rows_total][Hq][2] f32
+  int q_blocks;           // query blocks of 64 tokens per request
+};
+void launch_attention(int adt, const AttnArgs& a, hipStream_t s);
+
+// ---- MoE routing ----------------------------------------------------------------
+struct RouteArgs {
+  const float* logits;   // [T][E] router logits
+  int T, E, k;
+  int32_t* topk_id;      // [T][k]
+  float* topk_gate;      // [T][k]
+  int32_t* blk_cnt;      // [n_blk][E]
+  int32_t* seg_off;      // [E+1] padded segment offsets
+  int32_t* row_map;      // [max_rows] token of each permuted row, -1 pad
+  int32_t* slot;         // [T][k] permuted row of assignment (t, j)
+  int32_t* tiles;        // [max_tiles][4]
+  int32_t* n_tiles;      // [1]
+  int mrows;             // rows per GEMM tile
+  int max_rows, max_tiles;
+  int32_t* trace_ids;    // optional
+  float* trace_gates;
+};
+void launch_route(const RouteArgs& a, hipStream_t s);
+
+// ---- misc ---------------------------------------------------------------------------
+void launch_embed(int edt, const void* E, const int32_t* ids, int T, int V, int d, float* h, hipStream_t s);
+void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s);
+void launch_rope_table(float* cs, int max_ctx, int dh, float theta, hipStream_t s);
+void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, int T, int k,
+                    int d, float* h, hipStream_t s);
+void launch_attn_merge(int adt, const AttnArgs& a, hipStream_t s);
+void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+// per-request device state
+struct ReqDev {
+  int32_t P;        // committed length
+  int32_t t;        // passes done in the current block
+  int32_t block;
+  int32_t active;   // canvas active
+  uint64_t seed;
+};
+void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed,
+                        int block, hipStream_t s);
+void launch_advance(ReqDev* rq, int req, int dP, int clear_active, hipStream_t s);
+void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s);
+
+// ---- sampler ------------------------------------------------------------------------
+struct SampleArgs {
+  const float* logits;   // [rows][V]
+  int rows, V, C;
+  int n_chunks, chunk;   // chunk = V / n_chunks floats
+  float4* part;          // [rows][n_chunks] (m, S, U, idx as float bits)
+  const int32_t* prev_a; // [rows] or null
+  int32_t* tokens;       // [rows] next canvas
+  int32_t* argmax;       // [rows]
+  uint8_t* lock;         // [rows]
+  double* entropy;       // [rows]
+  double* pmax;          // [rows]
+  void* info;            // cd_step_info per request
+  const int32_t* canvas_in;  // canvas fed to this pass (for canvas_is_argmax), or null
+  ReqDev* rq;            // per-request state of request req0 + i, or null
+  uint64_t seed;         // used when rq is null
+  int step, block, req0; // used when rq is null
+  int max_steps;
+  float lock_th, stop_H;
+};
+void launch_sampler(const SampleArgs& a, hipStream_t s);
+
+}  // namespace cd

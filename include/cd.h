@@ -1,0 +1,212 @@
+/*
+ * cd.h — C ABI of libcd: the canvas denoise step of block text diffusion
+ * (DiffusionGemma-style) on one AMD MI355X (gfx950).
+ *
+ * The method (see the DiffusionGemma pages: the 256-token canvas explainer,
+ * section "256-token Canvas 怎麼從雜訊變成文字？" steps ① to ④; the
+ * MarkTechPost article, sections "how text diffusion works" and
+ * "architecture"; the Google launch blog, "how text diffusion works"):
+ *   ① the prompt is encoded causally into a reusable KV cache;
+ *   ② a canvas of 256 token ids is drawn uniformly from the vocabulary;
+ *   ③ passes run a bidirectional forward over the canvas (reading the
+ *      committed KV cache), lock confident positions, re-noise the rest, and
+ *      stop once the canvas mean entropy is below 0.005 nats and the argmax is
+ *      unchanged over two consecutive passes (at most 48 passes);
+ *   ④ the converged block is committed to the KV cache and the next canvas
+ *      is conditioned on it.
+ *
+ * Conventions
+ *  - Memory: every device buffer passed in is owned by the caller.  The
+ *    library allocates no device memory: weights and state live in two
+ *    caller-allocated device buffers whose sizes cd_weights_bytes and
+ *    cd_state_bytes report.  Pointers marked d_ are device pointers, h_ host.
+ *  - Streams: every call enqueues on the caller's hipStream_t (passed as
+ *    void*) and returns without waiting, except where stated (cd_commit_block,
+ *    cd_generate and cd_read_step_info synchronise the stream).
+ *  - Errors: every function returns CD_OK (0) or a negative code.  All
+ *    arguments and the request state are checked before anything is
+ *    enqueued, so a failing call changes nothing.  A kernel fault surfaces as
+ *    CD_ERR_HIP from the next call that synchronises.  cd_last_error() gives a
+ *    message for the calling thread's last failure.
+ *  - Threads: a context is used from one host thread at a time.
+ */
+#ifndef CD_H_
+#define CD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CD_OK = 0,
+  CD_ERR_INVALID_ARG = -1,  /* bad pointer, size or shape */
+  CD_ERR_BAD_STATE = -2,    /* call out of order for this request */
+  CD_ERR_CAPACITY = -3,     /* KV cache or workspace too small */
+  CD_ERR_HIP = -4,          /* HIP runtime error */
+  CD_ERR_UNSUPPORTED = -5,  /* shape the kernels do not handle */
+  CD_ERR_NUMERIC = -6       /* non-finite logits met by the sampler */
+};
+
+/* Weight storage formats.  CD_FP8 stores attention projections and routed
+ * experts as OCP E4M3FN with one bf16 scale per output row and every other
+ * tensor as bf16; activations are then bf16. */
+enum { CD_F32 = 0, CD_BF16 = 1, CD_FP8 = 2 };
+
+typedef struct cd_config {
+  int32_t n_layers;       /* decoder layers */
+  int32_t d_model;        /* hidden width, multiple of 64 */
+  int32_t n_q_heads;      /* query heads */
+  int32_t n_kv_heads;     /* key/value heads (grouped-query attention) */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t n_experts;      /* routed experts, <= 256 */
+  int32_t top_k;          /* experts per token, <= 16 */
+  int32_t expert_hidden;  /* SwiGLU hidden width of each expert, mult. of 64 */
+  int32_t shared_hidden;  /* hidden width of the shared SwiGLU FFN, 0 = none */
+  int32_t vocab;          /* vocabulary size, multiple of 128 */
+  int32_t canvas_len;     /* tokens per canvas / block (the pages: 256) */
+  int32_t max_steps;      /* pass cap per block (the pages: 48) */
+  float lock_threshold;   /* lock a position when max prob > this (0.9) */
+  float stop_entropy;     /* stop when mean canvas entropy < this (0.005) */
+  float rms_eps;          /* RMSNorm epsilon */
+  float rope_theta;       /* rotary base; 0 disables rotary embedding */
+  int32_t weight_dtype;   /* CD_F32, CD_BF16 or CD_FP8 */
+  int32_t max_requests;   /* requests denoised together */
+  int32_t max_ctx;        /* KV capacity per request, tokens */
+  int32_t max_prefill;    /* largest single prefill call, tokens */
+} cd_config;
+
+/* Per-request result of one denoise pass, written to device memory. */
+typedef struct cd_step_info {
+  int32_t step;             /* pass index t (1-based) within the block */
+  int32_t stop;             /* 1 when the adaptive stop or the cap fired */
+  int32_t n_locked;         /* positions whose max prob exceeded the threshold */
+  int32_t stable;           /* argmax equal to the previous pass's everywhere */
+  int32_t canvas_is_argmax; /* the canvas fed to this pass equals its argmax */
+  int32_t nonfinite;        /* a logit was NaN or infinite */
+  double mean_entropy;      /* canvas mean entropy, nats */
+} cd_step_info;
+
+typedef struct cd_ctx cd_ctx;
+
+/* Sizes of the caller-allocated device buffers for a configuration.
+ * Returns CD_ERR_INVALID_ARG / CD_ERR_UNSUPPORTED for shapes outside the
+ * documented limits. */
+int32_t cd_weights_bytes(const cd_config* cfg, size_t* bytes);
+int32_t cd_state_bytes(const cd_config* cfg, size_t* bytes);
+
+/* Bind a context to caller buffers (d_weights: cd_weights_bytes bytes,
+ * d_state: cd_state_bytes bytes, both 256-byte aligned).  The context keeps
+ * the pointers; the caller keeps the buffers alive until cd_ctx_destroy.
+ * Enqueues nothing; the state is cleared by cd_reset on a stream. */
+int32_t cd_ctx_create(const cd_config* cfg, void* d_weights, void* d_state, cd_ctx** out);
+int32_t cd_ctx_destroy(cd_ctx* ctx);
+
+/* Clear all request state (KV lengths, canvases) on the stream. */
+int32_t cd_reset(cd_ctx* ctx, void* stream);
+
+/* Fill the weight buffer with synthetic N(0, 0.02^2) weights drawn from
+ * Philox4x32-10 + Box-Muller in fp64 and rounded once to the storage format
+ * (tensor and counter layout in DESIGN.md, "Synthetic weights"). */
+int32_t cd_synth_weights(cd_ctx* ctx, uint64_t seed, void* stream);
+
+/* Tensor kinds for cd_set_weight / cd_get_weight (logical [out][in] layout). */
+enum { CD_W_EMBED = 0, CD_W_LM = 1, CD_W_Q = 2, CD_W_K = 3, CD_W_V = 4, CD_W_O = 5,
+       CD_W_ROUTER = 6, CD_W_GATE = 7, CD_W_UP = 8, CD_W_DOWN = 9,
+       CD_W_SHARED_GATE = 10, CD_W_SHARED_UP = 11, CD_W_SHARED_DOWN = 12 };
+
+/* Copy one tensor between a caller fp32 device buffer d_logical
+ * ([out][in] row-major) and the library's internal layout.  set rounds to the
+ * storage format (fp8 tensors get fresh per-row scales); get returns the
+ * stored values.  layer / expert are ignored where they do not apply. */
+int32_t cd_set_weight(cd_ctx* ctx, int32_t kind, int32_t layer, int32_t expert,
+                      const float* d_logical, void* stream);
+int32_t cd_get_weight(cd_ctx* ctx, int32_t kind, int32_t layer, int32_t expert,
+                      float* d_logical, void* stream);
+
+/* ① Causal prefill: forward of n prompt ids (d_ids, int32, device) of
+ * request req at positions P..P+n-1 with causal attention, appending their
+ * keys/values to the KV cache; P grows by n.  Allowed when no canvas is
+ * active; n <= max_prefill; CD_ERR_CAPACITY if P + n + canvas_len > max_ctx. */
+int32_t cd_prefill(cd_ctx* ctx, int32_t req, const int32_t* d_ids, int32_t n, void* stream);
+
+/* ② Canvas start for request req, block index `block`: token i is
+ * floor(r0 * V / 2^32) with (r0..r3) = Philox4x32-10(key = seed;
+ * counter = (i, 0, block, req)).  Allowed when no canvas is active. */
+int32_t cd_init_canvas(cd_ctx* ctx, int32_t req, uint64_t seed, int32_t block, void* stream);
+
+/* ③ One denoise pass over requests 0..n_req-1 (all with an active canvas):
+ * bidirectional forward over every canvas (keys = committed cache + canvas),
+ * LM head to fp32 logits, then the sampler: per position entropy (nats),
+ * argmax (ties to the lowest id) and max prob; lock when max prob >
+ * lock_threshold (the position takes the argmax), else re-noise with
+ * Philox(seed; i, t, block, req); stop when t >= 2, mean entropy <
+ * stop_entropy and the argmax equals the previous pass's at every position,
+ * or when t == max_steps.  d_info receives n_req cd_step_info records.
+ * CD_ERR_BAD_STATE if a request has no canvas or has reached max_steps. */
+int32_t cd_denoise_step(cd_ctx* ctx, int32_t n_req, cd_step_info* d_info, void* stream);
+
+/* Copy n_req step records from device to host and wait for the stream. */
+int32_t cd_read_step_info(cd_ctx* ctx, const cd_step_info* d_info, int32_t n_req,
+                          cd_step_info* h_info, void* stream);
+
+/* ④ Commit the block of request req: the committed ids are the argmax of
+ * the last pass (written to d_out_ids, canvas_len int32).  Their keys/values
+ * come from a canvas-mode pass over the committed ids at positions
+ * P..P+C-1, unless the last pass's canvas already equalled its argmax (then
+ * that pass's keys/values are the same and are kept).  The cache below P is
+ * never written.  P grows by canvas_len.  Synchronises the stream once. */
+int32_t cd_commit_block(cd_ctx* ctx, int32_t req, int32_t* d_out_ids, void* stream);
+
+/* Whole loop for one request: optional prefill of n_prefix ids, then
+ * n_blocks blocks of init -> passes to the adaptive stop -> commit.
+ * d_out_ids receives n_blocks*canvas_len ids; h_steps_per_block (host,
+ * n_blocks entries) the passes each block took.  Synchronises every pass.
+ * CD_ERR_NUMERIC if the sampler met non-finite logits. */
+int32_t cd_generate(cd_ctx* ctx, int32_t req, const int32_t* d_prefix, int32_t n_prefix,
+                    int32_t n_blocks, uint64_t seed, int32_t* d_out_ids,
+                    int32_t* h_steps_per_block, void* stream);
+
+/* Sampler alone on caller logits (rows x vocab fp32, device), rows a
+ * multiple of canvas_len, treated as rows/canvas_len requests at pass `step`
+ * of block `block`, request indices req0, req0+1, ...  d_prev_argmax (rows
+ * int32, may be NULL: then no stability) is the previous pass's argmax.
+ * Outputs (device, rows entries each): d_tokens next canvas ids, d_argmax,
+ * d_lock (uint8), d_entropy (f64), d_pmax (f64); d_info one record per
+ * request.  d_workspace: cd_sample_workspace_bytes bytes. */
+int32_t cd_sample_workspace_bytes(int32_t rows, int32_t vocab, size_t* bytes);
+int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows,
+                       const int32_t* d_prev_argmax, uint64_t seed, int32_t step,
+                       int32_t block, int32_t req0, int32_t* d_tokens, int32_t* d_argmax,
+                       uint8_t* d_lock, double* d_entropy, double* d_pmax,
+                       cd_step_info* d_info, void* d_workspace, void* stream);
+
+/* Internal buffers exposed for inspection (device pointers into d_state). */
+enum { CD_BUF_LOGITS = 0,   /* f32 [max_requests*C][vocab] last pass logits */
+       CD_BUF_CANVAS = 1,   /* i32 [max_requests][C] current canvas */
+       CD_BUF_ARGMAX = 2,   /* i32 [max_requests][C] last pass argmax */
+       CD_BUF_ENTROPY = 3,  /* f64 [max_requests][C] last pass entropies */
+       CD_BUF_PMAX = 4,     /* f64 [max_requests][C] last pass max probs */
+       CD_BUF_LOCK = 5,     /* u8 [max_requests][C] last pass lock mask */
+       CD_BUF_KCACHE = 6,   /* [max_requests][L][Hkv][max_ctx][dh] keys (act type) */
+       CD_BUF_VCACHE = 7,   /* [max_requests][L][Hkv][dh][max_ctx] values (act type) */
+       CD_BUF_HIDDEN = 8 }; /* f32 [tokens][d] residual stream after the last layer */
+int32_t cd_get_buffer(cd_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes);
+
+/* Committed length P of a request (host mirror; no synchronisation). */
+int32_t cd_get_length(cd_ctx* ctx, int32_t req, int32_t* P);
+
+/* Optional parity trace: when set, each layer of a denoise pass writes its
+ * input residual rows (f32 [L][T][d]) and routing (i32 ids / f32 gates
+ * [L][T][top_k]) to these caller buffers.  NULL pointers switch it off. */
+int32_t cd_set_trace(cd_ctx* ctx, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates);
+
+/* Message for the calling thread's last error ("" if none). */
+const char* cd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CD_H_ */

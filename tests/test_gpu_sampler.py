@@ -1,0 +1,125 @@
+"""GPU sampler (cd_sample_step) against the oracle sampler on identical fp32
+logits.  Full size: 256 positions x 262144 vocabulary, rows N(0, sigma) with
+sigma ~ U[0.5, 8] (seed 1).  Decisions must match bit-exactly except where
+the oracle's top-2 probability margin is <= 1e-3 (token ids) or its max
+probability is within 1e-3 of the lock threshold (lock bits)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs
+from block_text_diffusion_amd import binding as B
+from oracle import philox, sampler as osamp
+from tests.gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(V, C=256, max_steps=48):
+    w = synth_inputs.workload("tiny", V=V, C=C, max_steps=max_steps)
+    return B.make_config(w), w
+
+
+def run(z, seed=1, step=1, block=0, req0=0, prev=None, C=256, max_steps=48):
+    rows, V = z.shape
+    cfg, w = _cfg(V, C, max_steps)
+    dev = torch.device("cuda")
+    zt = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to(dev)
+    tok = torch.empty(rows, dtype=torch.int32, device=dev)
+    am = torch.empty(rows, dtype=torch.int32, device=dev)
+    lk = torch.empty(rows, dtype=torch.uint8, device=dev)
+    H = torch.empty(rows, dtype=torch.float64, device=dev)
+    pm = torch.empty(rows, dtype=torch.float64, device=dev)
+    info = torch.zeros(rows // C * B.STEP_INFO_BYTES, dtype=torch.uint8, device=dev)
+    ws = torch.empty(B.cd_sample_workspace_bytes(rows, V), dtype=torch.uint8, device=dev)
+    pv = None if prev is None else torch.from_numpy(np.asarray(prev, dtype=np.int32)).to(dev)
+    B.cd_sample_step(cfg, zt, rows, pv, seed, step, block, req0, tok, am, lk, H, pm, info, ws)
+    torch.cuda.synchronize()
+    raw = info.cpu().numpy().tobytes()
+    infos = [B.cd_step_info.from_buffer_copy(raw[i * B.STEP_INFO_BYTES:(i + 1) * B.STEP_INFO_BYTES])
+             for i in range(rows // C)]
+    return dict(tokens=tok.cpu().numpy(), a=am.cpu().numpy(), lock=lk.cpu().numpy().astype(bool),
+                H=H.cpu().numpy(), pmax=pm.cpu().numpy(), info=infos), w
+
+
+def test_sampler_full_size_matches_oracle():
+    announce("sampler_full", rows=256, V=262144)
+    z = synth_inputs.sampler_logits(256, 262144, 1)
+    g, w = run(z, seed=1, step=1)
+    ref = osamp.sample(w, z, seed=1, step=1, block=0, req=0)
+    decided = ref["margin"] > 1e-3
+    assert decided.mean() > 0.5
+    assert np.array_equal(g["a"][decided], ref["a"][decided])
+    assert np.mean(g["a"] == ref["a"]) > 0.999
+    lock_ok = np.abs(ref["pmax"] - w["lock"]) > 1e-3
+    assert np.array_equal(g["lock"][lock_ok], ref["lock"][lock_ok])
+    same = g["lock"] == ref["lock"]
+    assert np.array_equal(g["tokens"][same & (decided | ~g["lock"])], ref["x_next"][same & (decided | ~g["lock"])])
+    assert np.all(np.abs(g["H"] - ref["H"]) <= 1e-5 + 1e-5 * ref["H"])
+    assert np.all(np.abs(g["pmax"] - ref["pmax"]) <= 1e-6)
+    assert abs(g["info"][0].mean_entropy - ref["Hbar"]) <= 1e-6 * ref["Hbar"]
+    assert g["info"][0].n_locked == int(ref["lock"].sum())
+    assert g["info"][0].stop == 0 and g["info"][0].step == 1
+    assert 0 < ref["lock"].sum() < 256
+
+
+def test_uniform_and_two_level_rows():
+    announce("sampler_closed_forms", V=4096)
+    V = 4096
+    z = np.zeros((256, V), np.float32)
+    z[128:, 1234] = np.linspace(0.5, 30, 128, dtype=np.float32)
+    g, _ = run(z)
+    assert np.allclose(g["H"][:128], math.log(V), rtol=0, atol=2e-6)
+    assert np.all(g["a"][:128] == 0) and not g["lock"][:128].any()
+    a = z[128:, 1234].astype(np.float64)
+    p1 = np.exp(a) / (np.exp(a) + V - 1)
+    q = (1 - p1) / (V - 1)
+    H = -p1 * np.log(p1) - (1 - p1) * np.log(q)
+    assert np.all(np.abs(g["H"][128:] - H) <= 2e-6 + 1e-5 * H)
+    assert np.all(g["a"][128:] == 1234)
+    assert np.array_equal(g["lock"][128:], p1 > 0.9)
+
+
+def test_argmax_ties_and_philox_renoise():
+    announce("sampler_ties", V=4096)
+    V = 4096
+    z = np.zeros((512, V), np.float32)
+    z[:, [7, 3000, 4095]] = 2.0                 # three-way tie
+    g, w = run(z, seed=77, step=5, block=2, req0=3)
+    assert np.all(g["a"] == 7)
+    for r in range(2):
+        want = philox.token_draw(77, np.arange(256), 5, 2, 3 + r, V)
+        assert np.array_equal(g["tokens"][256 * r:256 * (r + 1)], want)
+
+
+def test_stop_rule_truth_table():
+    announce("sampler_stop_rule", V=4096)
+    V = 4096
+    z = np.zeros((256, V), np.float32)
+    ids = (np.arange(256) * 13) % V
+    z[np.arange(256), ids] = 40.0                # H ~ 0, all locked
+    g, _ = run(z, step=2, prev=ids)
+    assert g["info"][0].stop == 1 and g["info"][0].stable == 1
+    assert g["info"][0].mean_entropy < 0.005 and g["info"][0].n_locked == 256
+    assert np.array_equal(g["tokens"], ids)
+    g, _ = run(z, step=1, prev=ids)
+    assert g["info"][0].stop == 0                 # pass 1 never stops
+    prev = ids.copy(); prev[77] += 1
+    g, _ = run(z, step=3, prev=prev)
+    assert g["info"][0].stop == 0 and g["info"][0].stable == 0
+    flat = np.zeros((256, V), np.float32)
+    g, _ = run(flat, step=7, prev=np.zeros(256))
+    assert g["info"][0].stable == 1 and g["info"][0].stop == 0
+    g, _ = run(flat, step=48, prev=np.ones(256))
+    assert g["info"][0].stop == 1                 # cap
+
+
+def test_nonfinite_logits_flagged():
+    announce("sampler_nonfinite", V=4096)
+    z = np.zeros((256, 4096), np.float32)
+    z[10, 5] = np.nan
+    z[20, 6] = np.inf
+    g, _ = run(z)
+    assert g["info"][0].nonfinite == 1
