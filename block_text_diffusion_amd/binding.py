@@ -81,6 +81,9 @@ def lib():
             "cd_get_buffer": [c_void_p, c_int32, P(c_void_p), P(c_size_t)],
             "cd_get_length": [c_void_p, c_int32, P(c_int32)],
             "cd_set_trace": [c_void_p, c_void_p, c_void_p, c_void_p],
+            "cd_abort_canvas": [c_void_p, c_int32],
+            "cd_profile": [c_void_p, c_int32],
+            "cd_profile_read": [c_void_p, c_void_p, c_void_p, c_int32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -97,7 +100,7 @@ def exported_names():
             "cd_synth_weights", "cd_set_weight", "cd_get_weight", "cd_prefill", "cd_init_canvas",
             "cd_denoise_step", "cd_read_step_info", "cd_commit_block", "cd_generate",
             "cd_sample_workspace_bytes", "cd_sample_step", "cd_get_buffer", "cd_get_length",
-            "cd_set_trace", "cd_last_error"]
+            "cd_set_trace", "cd_abort_canvas", "cd_profile", "cd_profile_read", "cd_last_error"]
 
 
 def _check(code):
@@ -229,6 +232,27 @@ def cd_get_length(ctx, req):
 
 def cd_set_trace(ctx, h_layers=None, topk_ids=None, topk_gates=None):
     _check(lib().cd_set_trace(ctx, _ptr(h_layers), _ptr(topk_ids), _ptr(topk_gates)))
+
+
+PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "attn_merge", "o_proj", "router", "route",
+                "expert_gate_up", "expert_down", "combine", "shared_gate_up", "shared_down", "lm_head",
+                "sampler_part", "sampler_final", "other"]
+
+
+def cd_abort_canvas(ctx, req):
+    _check(lib().cd_abort_canvas(ctx, req))
+
+
+def cd_profile(ctx, enable):
+    _check(lib().cd_profile(ctx, 1 if enable else 0))
+
+
+def cd_profile_read(ctx):
+    n = len(PROF_CLASSES)
+    ms = (c_double * n)()
+    cnt = (c_int32 * n)()
+    _check(lib().cd_profile_read(ctx, ms, cnt, n))
+    return {PROF_CLASSES[i]: (ms[i], cnt[i]) for i in range(n)}
 
 
 def cd_last_error():

@@ -198,11 +198,20 @@ struct HostReq {
 
 }  // namespace
 
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+};
+
 struct cd_ctx {
   Plan p;
   uint8_t* W;
   uint8_t* S;
   std::vector<HostReq> req;
+  bool prof = false;
+  std::vector<ProfRec> recs;          // recorded this window
+  std::vector<hipEvent_t> pool;       // reusable events
+  size_t pool_used = 0;
   float* trace_h = nullptr;
   int32_t* trace_ids = nullptr;
   float* trace_gates = nullptr;
@@ -213,6 +222,39 @@ struct cd_ctx {
 namespace {
 
 hipStream_t strm(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+hipEvent_t pool_event(cd_ctx* c) {
+  if (c->pool_used == c->pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->pool.push_back(e);
+  }
+  return c->pool[c->pool_used++];
+}
+
+// Records events around one launch when profiling is on.
+struct Prof {
+  cd_ctx* c;
+  int cls;
+  hipStream_t s;
+  hipEvent_t b = nullptr;
+  Prof(cd_ctx* c_, int cls_, hipStream_t s_) : c(c_), cls(cls_), s(s_) {
+    if (c->prof) {
+      hipEvent_t a = pool_event(c);
+      b = pool_event(c);
+      if (a && b) {
+        hipEventRecord(a, s);
+        c->recs.push_back({cls, a, b});
+      } else {
+        b = nullptr;
+      }
+    }
+  }
+  ~Prof() {
+    if (b) hipEventRecord(b, s);
+  }
+};
+#define PROF(cls) Prof prof_guard_##__LINE__(c, cls, s)
 
 // ---- GEMM dispatch ---------------------------------------------------------------
 struct GemmCall {
@@ -239,10 +281,13 @@ void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_
   launch_gemm(wdt, c->p.adt, mt, epi, a, s);
 }
 
-void gemm_grouped(const cd_ctx* c, int wdt, int epi, GemmArgs a, hipStream_t s) {
+// rows: assignments of this forward (T * top_k); the grid is sized for the
+// most tiles they can form, so idle workgroups stay few
+void gemm_grouped(const cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, hipStream_t s) {
+  const int mrows = 16 * GROUPED_MT;
   a.tiles = c->st<int32_t>(c->p.tiles);
   a.n_tiles = c->st<int32_t>(c->p.n_tiles);
-  a.max_tiles = (int)c->p.max_tiles;
+  a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + mrows - 1) / mrows + std::min<int64_t>(rows, c->p.c.n_experts));
   a.chunk_major = 0;
   launch_gemm(wdt, c->p.adt, GROUPED_MT, epi, a, s);
 }
@@ -288,11 +333,11 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
   at.part_o = c->st<float>(p.part_o);
   at.part_ml = c->st<float>(p.part_ml);
 
-  launch_embed(p.wdt_other, c->W + p.embed, ids, T, g.vocab, d, h, s);
+  { PROF(CD_PROF_EMBED); launch_embed(p.wdt_other, c->W + p.embed, ids, T, g.vocab, d, h, s); }
   for (int l = 0; l < g.n_layers; ++l) {
     const LayerOff& lw = p.layer[l];
     if (trace && c->trace_h) launch_copy_f32(h, c->trace_h + (int64_t)l * T * d, (int64_t)T * d, s);
-    launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s);
+    { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
     // QKV + rotary, K/V scattered into the cache at positions P_r + i
     {
       GemmArgs a = gemm_base(u, d, c->W + lw.qkv, c->wt<float>(lw.qkv_s), d, p.qkv_npad,
@@ -302,18 +347,20 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       a.kc = kc; a.vc = vc; a.kv_req_stride = p.kv_req_stride;
       a.max_ctx = p.ctx; a.Hq = g.n_q_heads; a.Hkv = g.n_kv_heads; a.dh = dh;
       a.rows_per_req = rows_per_req; a.pos0 = pos0; a.pos0_stride = pos_stride; a.rope_cs = rope;
-      gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s);
+      { PROF(CD_PROF_QKV); gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s); }
       at.kc = kc; at.vc = vc;
     }
-    launch_attention(adt, at, s);
-    launch_attn_merge(adt, at, s);
+    { PROF(CD_PROF_ATTN); launch_attention(adt, at, s); }
+    { PROF(CD_PROF_ATTN_MERGE); launch_attn_merge(adt, at, s); }
     {
       GemmArgs a = gemm_base(O, qd, c->W + lw.wo, c->wt<float>(lw.wo_s), qd, p.wo_npad, d, h, d);
+      PROF(CD_PROF_O_PROJ);
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
-    launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s);
+    { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
     {
       GemmArgs a = gemm_base(u, d, c->W + lw.wr, nullptr, d, p.wr_npad, E, c->st<float>(p.rlog), E);
+      PROF(CD_PROF_ROUTER);
       gemm_dense(c, p.wdt_other, EPI_F32, a, T, s);
     }
     RouteArgs ra;
@@ -328,34 +375,38 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       ra.trace_ids = c->trace_ids + (int64_t)l * T * k;
       ra.trace_gates = c->trace_gates + (int64_t)l * T * k;
     }
-    launch_route(ra, s);
+    { PROF(CD_PROF_ROUTE); launch_route(ra, s); }
     {
       GemmArgs a = gemm_base(u, d, c->W + lw.gu, c->wt<float>(lw.gu_s), d, p.gu_npad, 2 * g.expert_hidden,
                              c->st<void>(p.aperm), g.expert_hidden);
       a.row_map = c->st<int32_t>(p.row_map);
       a.w_gstride = p.gu_stride; a.s_gstride = p.gu_npad;
-      gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, s);
+      PROF(CD_PROF_EXPERT_GU);
+      gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, (int64_t)T * k, s);
     }
     {
       GemmArgs a = gemm_base(c->st<void>(p.aperm), g.expert_hidden, c->W + lw.dn, c->wt<float>(lw.dn_s),
                              g.expert_hidden, p.dn_npad, d, c->st<void>(p.yperm), d);
       a.w_gstride = p.dn_stride; a.s_gstride = p.dn_npad;
-      gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, s);
+      PROF(CD_PROF_EXPERT_DOWN);
+      gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, s);
     }
-    launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate), T, k, d, h, s);
+    { PROF(CD_PROF_COMBINE); launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate), T, k, d, h, s); }
     if (g.shared_hidden) {
       GemmArgs a = gemm_base(u, d, c->W + lw.sgu, nullptr, d, p.sgu_npad, 2 * g.shared_hidden,
                              c->st<void>(p.sact), g.shared_hidden);
-      gemm_dense(c, p.wdt_other, EPI_SWIGLU, a, T, s);
+      { PROF(CD_PROF_SHARED_GU); gemm_dense(c, p.wdt_other, EPI_SWIGLU, a, T, s); }
       GemmArgs b = gemm_base(c->st<void>(p.sact), g.shared_hidden, c->W + lw.sdn, nullptr, g.shared_hidden,
                              p.sdn_npad, d, h, d);
+      PROF(CD_PROF_SHARED_DOWN);
       gemm_dense(c, p.wdt_other, EPI_RESID, b, T, s);
     }
   }
   if (head) {
-    launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s);
+    { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
     float* logits = c->st<float>(p.logits) + (int64_t)r0 * g.canvas_len * g.vocab;
     GemmArgs a = gemm_base(u, d, c->W + p.lm, nullptr, d, p.lm_npad, g.vocab, logits, g.vocab);
+    PROF(CD_PROF_LM_HEAD);
     gemm_dense(c, p.wdt_other, EPI_F32, a, T, s);
   }
 }
@@ -381,7 +432,8 @@ void sample(cd_ctx* c, int r0, int n_req, hipStream_t s) {
   a.rq = c->st<ReqDev>(p.rq) + r0;
   a.req0 = r0;
   a.max_steps = g.max_steps; a.lock_th = g.lock_threshold; a.stop_H = g.stop_entropy;
-  launch_sampler(a, s);
+  { PROF(CD_PROF_SAMPLER_PART); launch_sampler_part(a, s); }
+  { PROF(CD_PROF_SAMPLER_FINAL); launch_sampler_final(a, s); }
 }
 
 int32_t check_ctx(cd_ctx* c) { return c ? CD_OK : fail(CD_ERR_INVALID_ARG, "null context"); }
@@ -498,6 +550,8 @@ int32_t cd_ctx_create(const cd_config* cfg, void* d_weights, void* d_state, cd_c
 }
 
 int32_t cd_ctx_destroy(cd_ctx* ctx) {
+  if (ctx)
+    for (hipEvent_t e : ctx->pool) hipEventDestroy(e);
   delete ctx;
   return CD_OK;
 }
@@ -591,7 +645,7 @@ int32_t cd_prefill(cd_ctx* c, int32_t req, const int32_t* d_ids, int32_t n, void
   if (q.active) return fail(CD_ERR_BAD_STATE, "request %d has an active canvas", req);
   if ((int64_t)q.P + n + g.canvas_len > g.max_ctx) return fail(CD_ERR_CAPACITY, "KV cache too small for prefill");
   hipStream_t s = strm(stream);
-  forward(c, req, 1, n, d_ids, true, false, false, s);
+  forward(c, req, 1, n, d_ids, true, false, true, s);
   launch_advance(c->st<ReqDev>(c->p.rq), req, n, 0, s);
   q.P += n;
   return hip_status("prefill");
@@ -623,6 +677,40 @@ int32_t cd_denoise_step(cd_ctx* c, int32_t n_req, cd_step_info* d_info, void* st
   return CD_OK;
 }
 
+int32_t cd_abort_canvas(cd_ctx* c, int32_t req) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (req < 0 || req >= c->p.c.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
+  HostReq& q = c->req[req];
+  if (!q.active) return fail(CD_ERR_BAD_STATE, "request %d has no active canvas", req);
+  q.active = false;
+  q.t = 0;
+  return CD_OK;
+}
+
+int32_t cd_profile(cd_ctx* c, int32_t enable) {
+  if (int32_t st = check_ctx(c)) return st;
+  c->prof = enable != 0;
+  if (c->prof) {
+    c->recs.clear();
+    c->pool_used = 0;
+  }
+  return CD_OK;
+}
+
+int32_t cd_profile_read(cd_ctx* c, double* ms, int32_t* launches, int32_t n_classes) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (!ms || !launches || n_classes < 1 || n_classes > CD_PROF_CLASSES)
+    return fail(CD_ERR_INVALID_ARG, "bad profile output arrays");
+  for (int i = 0; i < n_classes; ++i) { ms[i] = 0.0; launches[i] = 0; }
+  for (const ProfRec& r : c->recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return hip_status("profile event sync");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return hip_status("profile elapsed");
+    if (r.cls < n_classes) { ms[r.cls] += t; launches[r.cls] += 1; }
+  }
+  return CD_OK;
+}
+
 int32_t cd_read_step_info(cd_ctx* c, const cd_step_info* d_info, int32_t n_req, cd_step_info* h_info, void* stream) {
   if (int32_t st = check_ctx(c)) return st;
   if (!d_info || !h_info || n_req < 1) return fail(CD_ERR_INVALID_ARG, "bad step info arguments");
@@ -644,7 +732,7 @@ int32_t cd_commit_block(cd_ctx* c, int32_t req, int32_t* d_out_ids, void* stream
   cd_step_info info;
   if (int32_t st = read_info(c, req, &info, s)) return st;
   int32_t* a = c->st<int32_t>(c->p.argmax) + (int64_t)req * g.canvas_len;
-  if (!info.canvas_is_argmax) forward(c, req, 1, g.canvas_len, a, false, false, false, s);
+  if (!info.canvas_is_argmax) forward(c, req, 1, g.canvas_len, a, false, false, true, s);
   launch_copy_i32(a, d_out_ids, g.canvas_len, s);
   launch_advance(c->st<ReqDev>(c->p.rq), req, g.canvas_len, 1, s);
   q.P += g.canvas_len;
@@ -710,7 +798,8 @@ int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows
   a.entropy = d_entropy; a.pmax = d_pmax; a.info = d_info; a.canvas_in = nullptr; a.rq = nullptr;
   a.seed = seed; a.step = step; a.block = block; a.req0 = req0;
   a.max_steps = cfg->max_steps; a.lock_th = cfg->lock_threshold; a.stop_H = cfg->stop_entropy;
-  launch_sampler(a, strm(stream));
+  launch_sampler_part(a, strm(stream));
+  launch_sampler_final(a, strm(stream));
   return hip_status("sample step");
 }
 

@@ -15,9 +15,9 @@
 //  * the product is computed transposed (A = weight tile, B = activation
 //    tile), so each lane ends with 4 consecutive output columns of one row
 //    and the epilogues store 8-16 contiguous bytes per lane;
-//  * block ids are remapped so that consecutive logical tiles run on the
-//    same XCD (the dispatcher deals workgroups to the 8 XCDs round-robin),
-//    keeping a weight tile's re-reads by neighbouring row blocks in one L2.
+//  * dense launches remap block ids so that the row blocks of one weight
+//    slice run on the same XCD and share its L2; grouped launches keep the
+//    dispatcher's round-robin so the real tiles spread over all 8 XCDs.
 // Epilogues: fp32 store (router / LM head logits), row store (expert
 // outputs), fp32 residual add, SwiGLU of interleaved gate/up tiles, and
 // QKV with rotary embedding scattering K/V into the cache.
@@ -93,9 +93,13 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  // Dense launches (chunk-major) remap block ids so the row blocks that share
+  // a weight slice run on one XCD (the dispatcher deals workgroups to the 8
+  // XCDs round-robin) and share its L2.  Grouped launches keep the natural
+  // order: their real tiles come first and must spread over all XCDs.
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
-  const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int logical = a.chunk_major ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
   int tile, chunk;
   if (a.chunk_major) { chunk = logical / a.max_tiles; tile = logical - chunk * a.max_tiles; }
   else { tile = logical / a.n_chunks; chunk = logical - tile * a.n_chunks; }
@@ -161,13 +165,34 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
       }
   };
 
+  // Two register stages; inside the loop every load is unconditional so the
+  // compiler's wait counts keep the next stage's loads in flight while the
+  // current stage's MFMAs run.
+  // sched_barrier keeps the scheduler from sinking the prefetch loads next to
+  // their uses, which would serialise the stages again.
   const int nfull = KT / U;
-  if (nfull > 0) load(wA, xA, 0);
-  for (int b = 0; b < nfull; b += 2) {
-    if (b + 1 < nfull) load(wB, xB, (b + 1) * U);
-    compute(wA, xA);
-    if (b + 2 < nfull) load(wA, xA, (b + 2) * U);
-    if (b + 1 < nfull) compute(wB, xB);
+  if (nfull > 0) {
+    load(wA, xA, 0);
+    int b = 0;
+    for (; b + 2 < nfull; b += 2) {
+      load(wB, xB, (b + 1) * U);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wA, xA);
+      __builtin_amdgcn_sched_barrier(0);
+      load(wA, xA, (b + 2) * U);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wB, xB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (b + 1 < nfull) {
+      load(wB, xB, (b + 1) * U);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wA, xA);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wB, xB);
+    } else {
+      compute(wA, xA);
+    }
   }
   for (int kt = nfull * U; kt < KT; ++kt) {
     u32x4 w0 = *reinterpret_cast<const u32x4*>(wp0 + (int64_t)kt * 1024);

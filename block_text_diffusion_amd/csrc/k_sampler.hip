@@ -157,8 +157,10 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
   }
 }
 
-void launch_sampler(const SampleArgs& a, hipStream_t s) {
+void launch_sampler_part(const SampleArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_sample_part, dim3(a.n_chunks, a.rows), dim3(256), 0, s, a);
+}
+void launch_sampler_final(const SampleArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_sample_final, dim3(a.rows / a.C), dim3(256), 0, s, a);
 }
 

@@ -158,6 +158,7 @@ struct SampleArgs {
   int max_steps;
   float lock_th, stop_H;
 };
-void launch_sampler(const SampleArgs& a, hipStream_t s);
+void launch_sampler_part(const SampleArgs& a, hipStream_t s);
+void launch_sampler_final(const SampleArgs& a, hipStream_t s);
 
 }  // namespace cd

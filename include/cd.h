@@ -107,9 +107,15 @@ int32_t cd_ctx_destroy(cd_ctx* ctx);
 /* Clear all request state (KV lengths, canvases) on the stream. */
 int32_t cd_reset(cd_ctx* ctx, void* stream);
 
-/* Fill the weight buffer with synthetic N(0, 0.02^2) weights drawn from
- * Philox4x32-10 + Box-Muller in fp64 and rounded once to the storage format
- * (tensor and counter layout in DESIGN.md, "Synthetic weights"). */
+/* Fill the weight buffer with synthetic N(0, 0.02^2) weights.  Element n of
+ * the [out][in] row-major tensor with id tau is 0.02*z, z from Box-Muller in
+ * fp64 over Philox4x32-10(key = seed; counter = (n/4 low, n/4 high, tau,
+ * 1 << 24)): words (r0, r1) give elements 4q, 4q+1 as
+ * sqrt(-2 ln((r0+1)/2^32)) * (cos, sin)(2 pi r1/2^32), words (r2, r3) give
+ * 4q+2, 4q+3; the value is rounded once to the storage format.  Tensor ids:
+ * embedding 0, LM head 1, and for layer l, base 2 + l*(8 + 3E): +0 Wq, +1 Wk,
+ * +2 Wv, +3 Wo, +4 router, +5+3e / +6+3e / +7+3e expert e gate / up / down,
+ * +5+3E / +6+3E / +7+3E shared gate / up / down. */
 int32_t cd_synth_weights(cd_ctx* ctx, uint64_t seed, void* stream);
 
 /* Tensor kinds for cd_set_weight / cd_get_weight (logical [out][in] layout). */
@@ -147,6 +153,10 @@ int32_t cd_init_canvas(cd_ctx* ctx, int32_t req, uint64_t seed, int32_t block, v
  * or when t == max_steps.  d_info receives n_req cd_step_info records.
  * CD_ERR_BAD_STATE if a request has no canvas or has reached max_steps. */
 int32_t cd_denoise_step(cd_ctx* ctx, int32_t n_req, cd_step_info* d_info, void* stream);
+
+/* Drop the active canvas of request req without committing it (the
+ * request returns to the state after its last commit).  Host-side only. */
+int32_t cd_abort_canvas(cd_ctx* ctx, int32_t req);
 
 /* Copy n_req step records from device to host and wait for the stream. */
 int32_t cd_read_step_info(cd_ctx* ctx, const cd_step_info* d_info, int32_t n_req,
@@ -198,10 +208,24 @@ int32_t cd_get_buffer(cd_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes);
 /* Committed length P of a request (host mirror; no synchronisation). */
 int32_t cd_get_length(cd_ctx* ctx, int32_t req, int32_t* P);
 
-/* Optional parity trace: when set, each layer of a denoise pass writes its
- * input residual rows (f32 [L][T][d]) and routing (i32 ids / f32 gates
- * [L][T][top_k]) to these caller buffers.  NULL pointers switch it off. */
+/* Optional parity trace: when set, every forward (prefill, denoise pass,
+ * commit recompute) over T rows writes each layer's input residual rows
+ * (f32 [L][T][d]) and routing (i32 ids / f32 gates [L][T][top_k]) to these
+ * caller buffers, sized for the largest T used.  NULL pointers switch a part
+ * off; cd_set_trace(ctx, NULL, NULL, NULL) switches tracing off. */
 int32_t cd_set_trace(cd_ctx* ctx, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates);
+
+/* Per-kernel timing with HIP events recorded on the call's stream around
+ * every launch (enable = 1 starts a fresh window, 0 stops recording).
+ * cd_profile_read waits for the recorded events and returns, per kernel
+ * class, the summed milliseconds and the number of launches (arrays of
+ * n_classes entries, at most CD_PROF_CLASSES). */
+enum { CD_PROF_EMBED = 0, CD_PROF_RMSNORM, CD_PROF_QKV, CD_PROF_ATTN, CD_PROF_ATTN_MERGE, CD_PROF_O_PROJ,
+       CD_PROF_ROUTER, CD_PROF_ROUTE, CD_PROF_EXPERT_GU, CD_PROF_EXPERT_DOWN, CD_PROF_COMBINE,
+       CD_PROF_SHARED_GU, CD_PROF_SHARED_DOWN, CD_PROF_LM_HEAD, CD_PROF_SAMPLER_PART, CD_PROF_SAMPLER_FINAL,
+       CD_PROF_OTHER, CD_PROF_CLASSES };
+int32_t cd_profile(cd_ctx* ctx, int32_t enable);
+int32_t cd_profile_read(cd_ctx* ctx, double* ms, int32_t* launches, int32_t n_classes);
 
 /* Message for the calling thread's last error ("" if none). */
 const char* cd_last_error(void);

@@ -18,7 +18,7 @@ Sources.  The pages are five web pages about Google's DiffusionGemma:
   [P5] Google launch blog in Vietnamese translation (aitoday.skyai.vn),
        sections "why diffusion for text" and "how text diffusion works".
 Every function cites the passage it follows.  Points the pages leave open
-take the plainest reading; each reading is listed in the design doc.
+take the plainest reading, stated in the docstring of the module that uses it.
 
 Precision: everything is fp64.  Weights are held at their storage precision
 (fp32, bf16, or e4m3 with a bf16 per-row scale) and used exactly as stored.

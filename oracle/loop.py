@@ -50,10 +50,11 @@ class Request:
         return r
 
 
-def prefill(cfg, W, req, ids):
+def prefill(cfg, W, req, ids, forced_routing=None):
     """Causal forward over prompt ids at positions P.. ; appends their K/V."""
     pos = req.P + np.arange(len(ids))
-    _, new_kv, _ = model.forward(cfg, W, ids, pos, req.cache, causal=True, head=False)
+    _, new_kv, _ = model.forward(cfg, W, ids, pos, req.cache, causal=True, head=False,
+                                 forced_routing=forced_routing)
     req.append(new_kv, ids)
 
 
@@ -61,20 +62,22 @@ def init_canvas(cfg, seed, block, req_idx):
     return philox.token_draw(seed, np.arange(cfg["C"]), 0, block, req_idx, cfg["V"])
 
 
-def denoise_pass(cfg, W, req, x, t, block, seed, trace=None):
+def denoise_pass(cfg, W, req, x, t, block, seed, trace=None, forced_routing=None):
     """Pass t over canvas x: logits, sampler outputs and this pass's K/V."""
     pos = req.P + np.arange(cfg["C"])
-    z, new_kv, _ = model.forward(cfg, W, x, pos, req.cache, causal=False, trace=trace)
+    z, new_kv, _ = model.forward(cfg, W, x, pos, req.cache, causal=False, trace=trace,
+                                 forced_routing=forced_routing)
     out = sampler.sample(cfg, z, seed, t, block, req.req)
     out["z"] = z
     out["kv"] = new_kv
     return out
 
 
-def commit(cfg, W, req, ids):
+def commit(cfg, W, req, ids, forced_routing=None):
     """Append the K/V of a canvas-mode pass over the committed ids."""
     pos = req.P + np.arange(len(ids))
-    _, new_kv, _ = model.forward(cfg, W, ids, pos, req.cache, causal=False, head=False)
+    _, new_kv, _ = model.forward(cfg, W, ids, pos, req.cache, causal=False, head=False,
+                                 forced_routing=forced_routing)
     req.append(new_kv, ids)
 
 

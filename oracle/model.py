@@ -98,10 +98,22 @@ def topk_route(r, k):
     return ids, g
 
 
-def moe(cfg, W, layer, u):
-    """MoE FFN output for normed rows u[n][d]: routed experts + shared FFN."""
+def moe(cfg, W, layer, u, forced_ids=None):
+    """MoE FFN output for normed rows u[n][d]: routed experts + shared FFN.
+
+    forced_ids (optional [n][k]) replaces the top-k choice; the gates are still
+    the softmax of this oracle's router logits over those experts.  Used only
+    to follow another implementation's routing where a top-k decision was a
+    near-tie (lockstep comparison).
+    """
     r = u @ W.get("wr", layer).T
-    ids, gates = topk_route(r, cfg["k"])
+    if forced_ids is None:
+        ids, gates = topk_route(r, cfg["k"])
+    else:
+        ids = np.asarray(forced_ids, dtype=np.int64)
+        sel = np.take_along_axis(r, ids, axis=1)
+        gates = np.exp(sel - sel.max(axis=1, keepdims=True))
+        gates /= gates.sum(axis=1, keepdims=True)
     out = np.zeros_like(u)
     for e in range(cfg["E"]):
         rows, slot = np.nonzero(ids == e)
@@ -114,7 +126,7 @@ def moe(cfg, W, layer, u):
     return out, r, ids, gates
 
 
-def layer(cfg, W, l, h, positions, K_prev, V_prev, allowed=None):
+def layer(cfg, W, l, h, positions, K_prev, V_prev, allowed=None, forced_ids=None):
     """One decoder layer over rows h[n][d].
 
     K_prev, V_prev: [Hkv][m][dh] cached keys/values this layer attends in
@@ -136,7 +148,7 @@ def layer(cfg, W, l, h, positions, K_prev, V_prev, allowed=None):
     o = attention(q, K, V, allowed).reshape(n, Hq * dh)
     h = h + o @ W.get("wo", l).T
     u2 = rmsnorm(h, cfg["eps"])
-    f, r, ids, gates = moe(cfg, W, l, u2)
+    f, r, ids, gates = moe(cfg, W, l, u2, forced_ids)
     h = h + f
     return h, k_new, v_new, dict(router=r, ids=ids, gates=gates)
 
@@ -146,13 +158,15 @@ def empty_cache(cfg):
     return [(np.zeros((Hkv, 0, dh)), np.zeros((Hkv, 0, dh))) for _ in range(cfg["L"])]
 
 
-def forward(cfg, W, ids, positions, cache, causal=False, head=True, trace=None):
+def forward(cfg, W, ids, positions, cache, causal=False, head=True, trace=None, forced_routing=None):
     """Forward of token ids at the given positions over a KV cache.
 
     cache: per-layer (K, V) [Hkv][m][dh] of the committed history.
     causal=False: the canvas mode (no mask).  causal=True: token i also sees
     new tokens j <= i (prefill).  Returns (logits or None, new per-layer
     (k, v), final hidden rows).  ``trace`` (a list) receives each layer's input.
+    ``forced_routing`` (optional, per layer [n][k] or None) follows given
+    top-k choices (see moe).
     """
     h = W.rows("embed", np.asarray(ids))
     n = h.shape[0]
@@ -165,7 +179,8 @@ def forward(cfg, W, ids, positions, cache, causal=False, head=True, trace=None):
             allowed = np.concatenate([np.ones((n, m), bool), np.tril(np.ones((n, n), bool))], axis=1)
         if trace is not None:
             trace.append(dict(h_in=h.copy()))
-        h, k_new, v_new, tr = layer(cfg, W, l, h, positions, K_prev, V_prev, allowed)
+        fr = None if forced_routing is None else forced_routing[l]
+        h, k_new, v_new, tr = layer(cfg, W, l, h, positions, K_prev, V_prev, allowed, fr)
         if trace is not None:
             trace[-1].update(tr)
         new_kv.append((k_new, v_new))

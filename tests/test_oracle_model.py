@@ -146,3 +146,14 @@ def test_canvas_forward_is_permutation_equivariant_without_rope():
     ca, _, _ = model.forward(cfg, W, ids, np.arange(5), cache, causal=True)
     cb, _, _ = model.forward(cfg, W, ids[perm], np.arange(5), cache, causal=True)
     assert not np.allclose(ca[perm], cb)
+
+
+def test_forced_routing_with_own_choice_is_identity():
+    cfg = _small_cfg(fs=8)
+    W = Weights(cfg)
+    u = np.random.default_rng(8).standard_normal((9, 32))
+    a, r, ids, g = model.moe(cfg, W, 0, u)
+    b, r2, ids2, g2 = model.moe(cfg, W, 0, u, forced_ids=ids[:, ::-1])
+    assert np.array_equal(ids2, ids[:, ::-1]) and np.allclose(a, b, atol=1e-15)
+    c, _, _, _ = model.moe(cfg, W, 0, u, forced_ids=(ids + 1) % cfg["E"])
+    assert not np.allclose(a, c)
