@@ -41,6 +41,7 @@ int32_t hip_status(const char* where) {
 constexpr int64_t ALIGN = 256;
 constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows
 constexpr int MAX_SPLIT = 16;          // attention key splits
+constexpr int MAX_RSPLIT = 16;         // router contraction splits
 
 struct Carve {
   int64_t off = 0;
@@ -169,7 +170,7 @@ Plan make_plan(const cd_config& c) {
   p.o = s.take((int64_t)ae * T * c.n_q_heads * dh);
   p.part_o = s.take(4LL * MAX_SPLIT * T * c.n_q_heads * dh);
   p.part_ml = s.take(8LL * MAX_SPLIT * T * c.n_q_heads);
-  p.rlog = s.take(4LL * T * E);
+  p.rlog = s.take(4LL * MAX_RSPLIT * T * E);
   p.topk_id = s.take(4LL * T * k);
   p.topk_gate = s.take(4LL * T * k);
   p.blk_cnt = s.take(4LL * p.n_blk_max * E);
@@ -272,6 +273,16 @@ GemmArgs gemm_base(const void* X, int64_t ldx, const uint8_t* W, const float* ws
   return a;
 }
 
+// contraction split of the router GEMM: enough k-splits that the launch has
+// about 128 workgroups, at least 8 k-tiles each
+int router_split(const cd_config& g, int T) {
+  const int kt = g.d_model / (g.weight_dtype == CD_F32 ? 16 : 32);
+  const int tiles = (T + 63) / 64;
+  int sp = 1;
+  while (sp < MAX_RSPLIT && tiles * sp * 2 <= 128 && kt / (sp * 2) >= 8) sp *= 2;
+  return sp;
+}
+
 void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
   const int mt = M >= 64 ? 4 : (M > 16 ? 2 : 1);
   a.M = M;
@@ -358,14 +369,20 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
     { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
+    // router logits as fp32 partial sums over a split contraction (the
+    // top-k kernel adds them in split order): the router weight is small, so
+    // splitting K is what gives the launch enough waves
+    const int rsplit = router_split(g, T);
     {
       GemmArgs a = gemm_base(u, d, c->W + lw.wr, nullptr, d, p.wr_npad, E, c->st<float>(p.rlog), E);
+      a.ksplit = rsplit;
+      a.y_kstride = (int64_t)T * E;
       PROF(CD_PROF_ROUTER);
       gemm_dense(c, p.wdt_other, EPI_F32, a, T, s);
     }
     RouteArgs ra;
     memset(&ra, 0, sizeof ra);
-    ra.logits = c->st<float>(p.rlog); ra.T = T; ra.E = E; ra.k = k;
+    ra.logits = c->st<float>(p.rlog); ra.nsplit = rsplit; ra.T = T; ra.E = E; ra.k = k;
     ra.topk_id = c->st<int32_t>(p.topk_id); ra.topk_gate = c->st<float>(p.topk_gate);
     ra.blk_cnt = c->st<int32_t>(p.blk_cnt); ra.seg_off = c->st<int32_t>(p.seg_off);
     ra.row_map = c->st<int32_t>(p.row_map); ra.slot = c->st<int32_t>(p.slot);

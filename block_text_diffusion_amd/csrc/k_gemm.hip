@@ -99,7 +99,10 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
   // order: their real tiles come first and must spread over all XCDs.
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
-  const int logical = a.chunk_major ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
+  int logical = a.chunk_major ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
+  const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
+  const int ks = logical % ksplit;
+  logical /= ksplit;
   int tile, chunk;
   if (a.chunk_major) { chunk = logical / a.max_tiles; tile = logical - chunk * a.max_tiles; }
   else { tile = logical / a.n_chunks; chunk = logical - tile * a.n_chunks; }
@@ -120,9 +123,11 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
   const int nt0 = chunk * 8 + wave * 2;
   if (nt0 >= a.Nt) return;
 
-  const int KT = a.K / KF;
-  const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)nt0 * KT) * 1024 + lane * 16;
-  const uint8_t* wp1 = wp0 + (int64_t)KT * 1024;
+  const int KTall = a.K / KF;
+  const int kt_beg = (int)((int64_t)KTall * ks / ksplit);
+  const int KT = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt_beg;   // k-tiles of this split
+  const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)nt0 * KTall + kt_beg) * 1024 + lane * 16;
+  const uint8_t* wp1 = wp0 + (int64_t)KTall * 1024;
   const int esa = (AT == DT_F32) ? 4 : 2;
   const uint8_t* xp[MT];
 #pragma unroll
@@ -131,7 +136,8 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     int src = 0;
     if (r < rows) src = a.row_map ? a.row_map[row0 + r] : row0 + r;
     if (src < 0) src = 0;
-    xp[mt] = reinterpret_cast<const uint8_t*>(a.X) + ((int64_t)src * a.ldx) * esa + (lane >> 4) * 16 * XW;
+    xp[mt] = reinterpret_cast<const uint8_t*>(a.X) + ((int64_t)src * a.ldx) * esa + (lane >> 4) * 16 * XW +
+             (int64_t)kt_beg * XSTEP;
   }
 
   f32x4 acc[MT][2];
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
           for (int q = 0; q < 4; ++q) v[q] *= sc[n + q];
         }
         if constexpr (EPI == EPI_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + (int64_t)row * a.ldy + n) =
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + ks * a.y_kstride + (int64_t)row * a.ldy + n) =
               make_float4(v[0], v[1], v[2], v[3]);
         } else if constexpr (EPI == EPI_ROWS) {
           store4<AT>(a.Y, (int64_t)row * a.ldy + n, v[0], v[1], v[2], v[3]);
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
 
 template <int WT, int AT, int MT, int EPI>
 static void run(const GemmArgs& a, hipStream_t s) {
-  int64_t blocks = (int64_t)a.max_tiles * a.n_chunks;
+  int64_t blocks = (int64_t)a.max_tiles * a.n_chunks * (a.ksplit > 1 ? a.ksplit : 1);
   blocks = round_up(blocks, 8);
   hipLaunchKernelGGL((k_gemm<WT, AT, MT, EPI>), dim3((unsigned)blocks), dim3(256), 0, s, a);
 }

@@ -16,50 +16,150 @@ namespace cd {
 
 constexpr int ROUTE_BLK = 512;
 
+// one wave per token; lane j ends up holding the j-th choice
 __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  const float* r = a.logits + (int64_t)t * a.E;
   float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int e = lane + 64 * i;
-    v[i] = e < a.E ? r[e] : -INFINITY;
+    const int e = lane + 64 * i;
+    float x = -INFINITY;
+    if (e < a.E) {
+      x = 0.f;
+      for (int s = 0; s < a.nsplit; ++s) x += a.logits[((int64_t)s * a.T + t) * a.E + e];
+    }
+    v[i] = x;
   }
-  float sel[16];
-  int ids[16];
+  float my_v = -INFINITY;
+  int my_id = 0;
   for (int j = 0; j < a.k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = lane + 64 * i;
-      if (e < a.E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+      const int e = lane + 64 * i;
+      if (e < a.E && v[i] != -INFINITY && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
-    sel[j] = bv;
-    ids[j] = bi;
+    if (lane == j) { my_v = bv; my_id = bi; }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lane + 64 * i == bi) v[i] = -INFINITY;
   }
-  if (lane == 0) {
-    float mx = sel[0], sum = 0.f;
-    float g[16];
-    for (int j = 0; j < a.k; ++j) { g[j] = expf(sel[j] - mx); sum += g[j]; }
-    for (int j = 0; j < a.k; ++j) {
-      a.topk_id[(int64_t)t * a.k + j] = ids[j];
-      a.topk_gate[(int64_t)t * a.k + j] = g[j] / sum;
-      if (a.trace_ids) {
-        a.trace_ids[(int64_t)t * a.k + j] = ids[j];
-        a.trace_gates[(int64_t)t * a.k + j] = g[j] / sum;
-      }
+  // gates: softmax over the k selected logits (lane 0 holds the largest)
+  const float mx = __shfl(my_v, 0, 64);
+  float g = lane < a.k ? expf(my_v - mx) : 0.f;
+  const float sum = wave_sum(g);
+  if (lane < a.k) {
+    g = g / sum;
+    a.topk_id[(int64_t)t * a.k + lane] = my_id;
+    a.topk_gate[(int64_t)t * a.k + lane] = g;
+    if (a.trace_ids) a.trace_ids[(int64_t)t * a.k + lane] = my_id;
+    if (a.trace_gates) a.trace_gates[(int64_t)t * a.k + lane] = g;
+  }
+}
+
+// Small batches: count, scan, tile table and placement in one workgroup.
+// Thread g owns the 16 consecutive assignments of group g; cnt[e][g] counts
+// expert e in group g and becomes, after a per-expert prefix over groups, the
+// rank base of that group inside expert e's segment.  Ranks therefore follow
+// assignment order (token, slot).
+constexpr int RG = 16;
+constexpr int ROUTE_ONE_CNT = 24576;   // E * groups (uint16 LDS cells)
+
+__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+
+__global__ __launch_bounds__(256) void k_route_one(RouteArgs a) {
+  __shared__ uint16_t cnt[ROUTE_ONE_CNT];
+  __shared__ int32_t seg[256], tile0[256], tot[256];
+  __shared__ int32_t totals[2];
+  const int n = a.T * a.k, ng = (n + RG - 1) / RG, E = a.E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < E * ng; i += 256) cnt[i] = 0;
+  __syncthreads();
+  int ex[RG];
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    const int i = tid * RG + j;
+    ex[j] = (tid < ng && i < n) ? a.topk_id[i] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < RG; ++j)
+    if (ex[j] >= 0) cnt[ex[j] * ng + tid] += 1;          // column tid is this thread's alone
+  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int c = 0; c < ng; ++c) {
+      const int v = cnt[tid * ng + c];
+      cnt[tid * ng + c] = (uint16_t)run;
+      run += v;
+    }
+    tot[tid] = run;
+  }
+  __syncthreads();
+  if (tid < 64) {   // segment and tile offsets: wave-wide exclusive scans, 4 experts per lane
+    int pad[4], nt[4], sp = 0, st = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      const int t = e < E ? tot[e] : 0;
+      pad[q] = (t + a.mrows - 1) / a.mrows * a.mrows;
+      nt[q] = pad[q] / a.mrows;
+      sp += pad[q];
+      st += nt[q];
+    }
+    int ep = wave_excl_scan(sp, lane), et = wave_excl_scan(st, lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      if (e < E) { seg[e] = ep; tile0[e] = et; }
+      ep += pad[q];
+      et += nt[q];
+    }
+    if (lane == 63) { totals[0] = ep; totals[1] = et; }
+  }
+  __syncthreads();
+  if (tid == 0) { a.seg_off[E] = totals[0]; *a.n_tiles = totals[1]; }
+  if (tid < E) {
+    const int off = seg[tid], total = tot[tid];
+    const int pad = (total + a.mrows - 1) / a.mrows * a.mrows;
+    a.seg_off[tid] = off;
+    for (int i = 0; i * a.mrows < total; ++i) {
+      int32_t* tl = a.tiles + 4 * (int64_t)(tile0[tid] + i);
+      tl[0] = tid;
+      tl[1] = off + i * a.mrows;
+      tl[2] = min(a.mrows, total - i * a.mrows);
+      tl[3] = 0;
+    }
+    for (int r = off + total; r < off + pad; ++r) a.row_map[r] = -1;
+  }
+  if (tid < ng) {
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      const int e = ex[j];
+      if (e < 0) continue;
+      int r = 0;
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) r += (ex[jj] == e);
+      const int slot = seg[e] + cnt[e * ng + tid] + r;
+      const int i = tid * RG + j;
+      a.slot[i] = slot;
+      a.row_map[slot] = i / a.k;
     }
   }
 }
@@ -141,6 +241,11 @@ __global__ __launch_bounds__(256) void k_route_place(RouteArgs a) {
 
 void launch_route(const RouteArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  const int ng = (a.T * a.k + RG - 1) / RG;
+  if (ng <= 256 && ng * a.E <= ROUTE_ONE_CNT) {
+    hipLaunchKernelGGL(k_route_one, dim3(1), dim3(256), 0, s, a);
+    return;
+  }
   const int n_blk = (a.T * a.k + ROUTE_BLK - 1) / ROUTE_BLK;
   hipLaunchKernelGGL(k_route_count, dim3(n_blk), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, s, a, n_blk);

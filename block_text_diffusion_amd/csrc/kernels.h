@@ -43,6 +43,8 @@ struct GemmArgs {
   int max_tiles;
   int M;
   int chunk_major;
+  int ksplit;              // split of the contraction (EPI_F32 only); 0 or 1 = none
+  int64_t y_kstride;       // elements between the fp32 partial outputs of the splits
   // epilogue
   void* Y;
   int64_t ldy;
@@ -99,7 +101,8 @@ void launch_attention(int adt, const AttnArgs& a, hipStream_t s);
 
 // ---- MoE routing ----------------------------------------------------------------
 struct RouteArgs {
-  const float* logits;   // [T][E] router logits
+  const float* logits;   // [nsplit][T][E] router logit partials (summed in split order)
+  int nsplit;
   int T, E, k;
   int32_t* topk_id;      // [T][k]
   float* topk_gate;      // [T][k]
