@@ -34,7 +34,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gpu_part(w, steps, warmup, prof_steps):
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) read by the profiler."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def gpu_part(w, steps, warmup, prof_steps, do_block=True):
     import torch
     from block_text_diffusion_amd import binding as B
     from block_text_diffusion_amd.engine import Engine
@@ -101,6 +115,10 @@ def gpu_part(w, steps, warmup, prof_steps):
              "mean_max_tokens_per_expert": float(counts.max(axis=1).mean()),
              "mean_row_tiles": float(np.mean([(np.ceil(c / 32)).sum() for c in counts]))}
 
+    if not do_block:
+        eng.close()
+        return dict(elapsed=el, prof=prof, active=active, route=route, prefill_ms=prefill_ms, block_s=float("nan"),
+                    block_passes=0, device=torch.cuda.get_device_name(dev))
     # one full block: canvas start, passes to the stop, commit
     B.cd_abort_canvas(ctx, 0)
     out = torch.empty(C, dtype=torch.int32, device=dev)
@@ -121,6 +139,25 @@ def gpu_part(w, steps, warmup, prof_steps):
     eng.close()
     return dict(elapsed=el, prof=prof, active=active, route=route, prefill_ms=prefill_ms, block_s=block_s,
                 block_passes=passes, device=torch.cuda.get_device_name(dev))
+
+
+def measured_traffic(kernel_part):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if that summary was taken on
+    the current kernel source (else None)."""
+    import hashlib
+    import re
+    root = os.path.dirname(os.path.abspath(__file__))
+    prof = os.path.join(root, "profiles", f"expert_gemm_{kernel_part}_step_bf16.md")
+    src = os.path.join(root, "block_text_diffusion_amd", "csrc", "k_gemm.hip")
+    if not os.path.exists(prof):
+        return None
+    m = re.search(r"```json\n(\{.*?\})\n```", open(prof).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return rec["traffic_bytes_per_launch"] if rec.get("k_gemm_hip_sha256_16") == sha else None
 
 
 def expert_bytes(w, active, part):
@@ -207,13 +244,18 @@ def main():
     ap.add_argument("--prof-steps", type=int, default=10)
     ap.add_argument("--workload", default="step_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block", action="store_true", help="skip the full-block measurement")
+    ap.add_argument("--copy-calib", action="store_true", help="only run the byte-counter calibration copy")
     args = ap.parse_args()
+    if args.copy_calib:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the canvas denoise step here runs on a single MI355X "
               "(multi-GPU sharding is a design note, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     w = synth_inputs.workload(args.workload)
-    g = gpu_part(w, args.steps, args.warmup, args.prof_steps)
+    g = gpu_part(w, args.steps, args.warmup, args.prof_steps, do_block=not args.no_block)
     ms = g["elapsed"] / args.steps * 1e3
     per = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in g["prof"].items()}       # avg ms per launch
     per_step = {k: v[0] / args.prof_steps for k, v in g["prof"].items()}          # ms per step
@@ -230,12 +272,13 @@ def main():
                                 f"{w['dh']}, {w['E']} experts top-{w['k']} (hidden {w['fe']}) + shared {w['fs']}, "
                                 f"vocab {w['V']}, prefix {w['P0']}, canvas {w['C']}"),
                    "requests": w["R"], "canvas": w["C"], "prefix": w["P0"]},
-        "committed_tok_s": round(w["C"] / g["block_s"], 2),
+        "committed_tok_s": round(w["C"] / g["block_s"], 2) if g["block_passes"] else None,
         "block_passes": g["block_passes"], "block_ms": round(g["block_s"] * 1e3, 2),
         "prefill_ms": round(g["prefill_ms"], 2),
         "roofline": {"kernel": f"grouped expert GEMM ({part.replace('_', '/')})", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(part) if args.workload == "step_bf16" else None,
                      "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5),
                      "active_experts": g["active"]},
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items() if v > 0},
