@@ -42,6 +42,7 @@ constexpr int64_t ALIGN = 256;
 constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows
 constexpr int MAX_SPLIT = 16;          // attention key splits
 constexpr int MAX_RSPLIT = 16;         // router contraction splits
+constexpr int MAX_XSPLIT = 16;         // dense contraction splits (M <= 256)
 
 struct Carve {
   int64_t off = 0;
@@ -70,7 +71,7 @@ struct Plan {
   // state
   int64_t rq, canvas, argmax, lock, entropy, pmax, info, h, u, q, o, part_o, part_ml, rlog, topk_id,
       topk_gate, blk_cnt, seg_off, row_map, slot, tiles, n_tiles, aperm, yperm, sact, logits, spart, rope,
-      kcache, vcache, zero;
+      kcache, vcache, zero, xpart;
   int64_t max_rows, max_tiles, n_blk_max, n_chunks;
   int64_t kv_req_stride, kv_layer_stride;   // elements
   int64_t state_bytes;
@@ -183,6 +184,10 @@ Plan make_plan(const cd_config& c) {
   p.yperm = s.take((int64_t)ae * p.max_rows * d);
   p.sact = s.take((int64_t)ae * T * std::max(c.shared_hidden, 1));
   p.logits = s.take(4LL * R * C * c.vocab);
+  {
+    const int64_t np = std::max(std::max(p.qkv_npad, p.wo_npad), std::max(p.sgu_npad, p.sdn_npad));
+    p.xpart = s.take(4LL * MAX_XSPLIT * 256 * np);
+  }
   p.spart = s.take(16LL * R * C * p.n_chunks);
   p.rope = s.take(8LL * p.ctx * (dh / 2));
   p.kcache = s.take((int64_t)ae * p.kv_req_stride * R);
@@ -283,7 +288,35 @@ int router_split(const cd_config& g, int T) {
   return sp;
 }
 
+// The LDS-staged dense path is switched off: on the GPU it gave wrong
+// results from the second denoise pass on, with no cause shown yet.
+constexpr bool USE_LDS_DENSE = false;
+
+// Dense GEMM.  Up to 256 rows: one workgroup per 128 output columns holds
+// all rows, activations staged in LDS; a narrow layer splits its contraction
+// over workgroups into fp32 partials that a second kernel sums and finishes.
+// Larger row counts (prefill, many requests) take the row-tiled kernel.
 void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
+  if (USE_LDS_DENSE && M <= 256 && a.ksplit <= 1) {
+    a.M = M;
+    const int kt = a.K / kfrag(wdt);
+    int ks = 1;
+    while (ks < MAX_XSPLIT && a.n_chunks * ks * 2 <= 256 && kt / (ks * 2) >= 4) ks *= 2;
+    if (ks == 1) {
+      launch_gemm_x(wdt, c->p.adt, epi, a, s);
+      return;
+    }
+    const int npad = a.Nt * 16;
+    GemmArgs pa = a;
+    pa.ksplit = ks;
+    pa.Y = c->st<float>(c->p.xpart);
+    pa.ldy = npad;
+    pa.N = npad;
+    pa.y_kstride = (int64_t)M * npad;
+    launch_gemm_x(wdt, c->p.adt, EPI_F32, pa, s);
+    launch_splitk_epi(c->p.adt, epi, a, c->st<float>(c->p.xpart), ks, (int64_t)M * npad, npad, s);
+    return;
+  }
   const int mt = M >= 64 ? 4 : (M > 16 ? 2 : 1);
   a.M = M;
   a.max_tiles = (M + 16 * mt - 1) / (16 * mt);

@@ -22,66 +22,10 @@
 // outputs), fp32 residual add, SwiGLU of interleaved gate/up tiles, and
 // QKV with rotary embedding scattering K/V into the cache.
 #include "common.h"
+#include "gemm_epi.h"
 #include "kernels.h"
 
 namespace cd {
-
-template <int AT>
-__device__ __forceinline__ void store4(void* base, int64_t idx, float v0, float v1, float v2, float v3) {
-  if constexpr (AT == DT_F32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(v0, v1, v2, v3);
-  } else {
-    uint2 p;
-    p.x = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
-    p.y = (uint32_t)f2bf(v2) | ((uint32_t)f2bf(v3) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = p;
-  }
-}
-template <int AT>
-__device__ __forceinline__ void store2(void* base, int64_t idx, float v0, float v1) {
-  if constexpr (AT == DT_F32) {
-    *reinterpret_cast<float2*>(reinterpret_cast<float*>(base) + idx) = make_float2(v0, v1);
-  } else {
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(base) + idx) =
-        (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
-  }
-}
-template <int AT>
-__device__ __forceinline__ void store1(void* base, int64_t idx, float v) {
-  if constexpr (AT == DT_F32) reinterpret_cast<float*>(base)[idx] = v;
-  else reinterpret_cast<uint16_t*>(base)[idx] = f2bf(v);
-}
-
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
-
-// one k-tile of MFMA work: acc += W_tile(16 x KF) * X_tile(16 x KF)^T
-template <int WT>
-__device__ __forceinline__ f32x4 mma_tile(const u32x4& w, const u32x4* x, f32x4 acc) {
-  if constexpr (WT == DT_F32) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w[j]), __uint_as_float(x[0][j]), acc, 0, 0, 0);
-  } else if constexpr (WT == DT_BF16) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
-                                                  __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
-  } else {
-    // E4M3 has 4 significant bits, so its bf16 image is exact (top half of fp32)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 wb;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = w[2 * h + (q >> 1)];
-        uint32_t b0 = (word >> (16 * (q & 1))) & 0xFFu;
-        uint32_t b1 = (word >> (16 * (q & 1) + 8)) & 0xFFu;
-        wb[q] = (__float_as_uint(e4m3_to_f32(b0)) >> 16) | (__float_as_uint(e4m3_to_f32(b1)) & 0xFFFF0000u);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb),
-                                                    __builtin_bit_cast(bf16x8, x[h]), acc, 0, 0, 0);
-    }
-  }
-  return acc;
-}
 
 template <int WT, int AT, int MT, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
@@ -215,84 +159,20 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
 
   // ---- epilogue: lane holds Y[row][n..n+3] of tile (mt, nw) ----
   const int nq = (lane >> 4) * 4;
+  const float* sc = a.wscale ? a.wscale + (int64_t)group * a.s_gstride : nullptr;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = mt * 16 + (lane & 15);
     if (r >= rows) continue;
     const int row = row0 + r;
+    float v0[4], v1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v0[q] = acc[mt][0][q]; v1[q] = acc[mt][1][q]; }
     if constexpr (EPI == EPI_SWIGLU) {
-      const int j = (nt0 >> 1) * 16 + nq;   // hidden column
-      float v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g = acc[mt][0][q], u = acc[mt][1][q];
-        if (a.wscale) {
-          const float* sc = a.wscale + (int64_t)group * a.s_gstride;
-          g *= sc[nt0 * 16 + nq + q];
-          u *= sc[(nt0 + 1) * 16 + nq + q];
-        }
-        v[q] = silu(g) * u;
-      }
-      store4<AT>(a.Y, (int64_t)row * a.ldy + j, v[0], v[1], v[2], v[3]);
+      epi_swiglu<AT>(a, sc, row, nt0 * 16 + nq, v0, v1);
     } else {
-#pragma unroll
-      for (int nw = 0; nw < 2; ++nw) {
-        const int n = (nt0 + nw) * 16 + nq;
-        if (n >= a.N) continue;
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = acc[mt][nw][q];
-        if (a.wscale) {
-          const float* sc = a.wscale + (int64_t)group * a.s_gstride;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] *= sc[n + q];
-        }
-        if constexpr (EPI == EPI_F32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + ks * a.y_kstride + (int64_t)row * a.ldy + n) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_ROWS) {
-          store4<AT>(a.Y, (int64_t)row * a.ldy + n, v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_RESID) {
-          float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + (int64_t)row * a.ldy + n);
-          float4 o = *p;
-          o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
-          *p = o;
-        } else if constexpr (EPI == EPI_QKV) {
-          const int dh = a.dh, half = dh >> 1;
-          const int req = row / a.rows_per_req;
-          const int pos = a.pos0[req * a.pos0_stride] + (row - req * a.rows_per_req);
-          const int qdim = a.Hq * dh, kdim = a.Hkv * dh;
-          if (n < qdim + kdim) {
-            // packed columns n..n+3 of a head are logical (i, i+half, i+1, i+1+half)
-            const int head = (n < qdim) ? n / dh : (n - qdim) / dh;
-            const int p = n % dh;
-            const int i0 = p >> 1;
-            float x0 = v[0], y0 = v[1], x1 = v[2], y1 = v[3];
-            if (a.rope_cs) {
-              const float* cs = a.rope_cs + ((int64_t)pos * half + i0) * 2;
-              float c0 = cs[0], s0 = cs[1], c1 = cs[2], s1 = cs[3];
-              float rx0 = x0 * c0 - y0 * s0, ry0 = y0 * c0 + x0 * s0;
-              float rx1 = x1 * c1 - y1 * s1, ry1 = y1 * c1 + x1 * s1;
-              x0 = rx0; y0 = ry0; x1 = rx1; y1 = ry1;
-            }
-            if (n < qdim) {
-              int64_t base = (int64_t)row * a.ldy + head * dh;
-              store2<AT>(a.Y, base + i0, x0, x1);
-              store2<AT>(a.Y, base + i0 + half, y0, y1);
-            } else {
-              int64_t base = (int64_t)req * a.kv_req_stride + ((int64_t)head * a.max_ctx + pos) * dh;
-              store2<AT>(a.kc, base + i0, x0, x1);
-              store2<AT>(a.kc, base + i0 + half, y0, y1);
-            }
-          } else {
-            const int c = n - qdim - kdim;
-            const int head = c / dh, dd = c % dh;
-            int64_t base = (int64_t)req * a.kv_req_stride + ((int64_t)head * dh + dd) * a.max_ctx + pos;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) store1<AT>(a.vc, base + (int64_t)q * a.max_ctx, v[q]);
-          }
-        }
-      }
+      epi_store<AT, EPI>(a, sc, row, nt0 * 16 + nq, v0, ks);
+      epi_store<AT, EPI>(a, sc, row, (nt0 + 1) * 16 + nq, v1, ks);
     }
   }
 }

@@ -1,0 +1,245 @@
+// Dense GEMM for up to 256 activation rows (the canvas batch) with the
+// activations staged in LDS:  Y[m][n] = sum_k X[m][k] * W[n][k].
+//
+// At 256 rows a weight byte feeds 256 MACs, so splitting the rows across
+// workgroups (as the grouped kernel does for small tiles) would make every
+// workgroup re-stream the same weight slice.  Here one workgroup owns all
+// rows of a 128-column slice:
+//  * per k-tile stage the workgroup copies the 16 activation fragments
+//    (16 rows x KF columns each, 1 KB, already in MFMA operand order) from
+//    global memory straight into LDS with global_load_lds_dwordx4 -- each
+//    lane's 16 bytes land at the wave's LDS base + lane*16, which is exactly
+//    the fragment layout -- so staging costs no VGPRs;
+//  * each wave streams its two 16-column weight tiles into registers and
+//    reads all 16 activation fragments of the stage from LDS (one contiguous
+//    1 KB ds_read per fragment, conflict-free);
+//  * activations and weights are both prefetched DIST stages ahead (4 LDS
+//    buffers of 16 KB, 3 register slots), so the one in-order vmcnt counter
+//    covers both streams with a single wait per stage;
+//  * a contraction split across workgroups supplies the parallelism that
+//    narrow layers (N of a few thousand) lack; its fp32 partials are summed
+//    in split order by k_splitk_epi, which then applies the epilogue.
+#include "common.h"
+#include "gemm_epi.h"
+#include "kernels.h"
+
+namespace cd {
+
+constexpr int XMT = 16;   // 16-row tiles: 256 rows
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int WT, int AT, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_x(const GemmArgs a) {
+  constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
+  constexpr int XW = (WT == DT_FP8) ? 2 : 1;          // 1 KB activation fragments per k-tile and row tile
+  constexpr int XSTEP = (WT == DT_FP8) ? 128 : 64;    // activation bytes per k-tile (per lane group)
+  constexpr int NBUF = (WT == DT_FP8) ? 2 : 4;
+  constexpr int DIST = NBUF - 1;
+  constexpr int BLK = XMT * XW;                       // fragments per stage
+  constexpr int BPW = BLK / 4;                        // fragments each wave copies
+  constexpr int LPS = BPW + 2;                        // vector loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[NBUF][BLK * 1024];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
+  const int ks = blockIdx.x % ksplit, chunk = blockIdx.x / ksplit;
+  const int KTall = a.K / KF;
+  const int kt0 = (int)((int64_t)KTall * ks / ksplit);
+  const int nst = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt0;
+  const int nt0 = chunk * 8 + wave * 2;
+  const bool active = nt0 < a.Nt;          // idle waves still copy activations and meet the barriers
+  const int ntc = active ? nt0 : 0;
+  const int esa = (AT == DT_F32) ? 4 : 2;
+
+  const uint8_t* wp0 = a.W + ((int64_t)ntc * KTall + kt0) * 1024 + lane * 16;
+  const uint8_t* wp1 = wp0 + (int64_t)KTall * 1024;
+  const uint8_t* xsrc[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int b = wave * BPW + i;
+    const int mt = b / XW, h = b % XW;
+    const int row = min(mt * 16 + (lane & 15), a.M - 1);
+    xsrc[i] = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)row * a.ldx * esa + (lane >> 4) * 16 * XW + h * 16 +
+              (int64_t)kt0 * XSTEP;
+  }
+
+  f32x4 acc[XMT][2];
+#pragma unroll
+  for (int mt = 0; mt < XMT; ++mt) { acc[mt][0] = f32x4{0, 0, 0, 0}; acc[mt][1] = f32x4{0, 0, 0, 0}; }
+  u32x4 w[DIST][2];
+
+  // stage indices past the end are clamped to the last stage: the copies
+  // stay in bounds and land in buffers no later stage reads
+  auto issue_x = [&](int s) {
+    const int sc = min(s, nst - 1);
+    uint8_t* dst = xs[s % NBUF] + wave * BPW * 1024;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xsrc[i] + (int64_t)sc * XSTEP),
+                                       (lds_void*)(dst + i * 1024), 16, 0, 0);
+  };
+  auto issue_w = [&](u32x4 (&ww)[2], int s) {
+    const int sc = min(s, nst - 1);
+    ww[0] = *reinterpret_cast<const u32x4*>(wp0 + (int64_t)sc * 1024);
+    ww[1] = *reinterpret_cast<const u32x4*>(wp1 + (int64_t)sc * 1024);
+  };
+  // all 16 row tiles are computed: rows past M hold copies of row M-1 (finite)
+  // and their results are dropped, which keeps the loop free of branches
+  // LDS fragment reads run one row tile ahead of the MFMAs that use them
+  auto compute = [&](const u32x4 (&ww)[2], const uint8_t* buf) {
+    u32x4 xa[XW], xb[XW];
+    auto rd = [&](u32x4 (&x)[XW], int mt) {
+#pragma unroll
+      for (int h = 0; h < XW; ++h) x[h] = *reinterpret_cast<const u32x4*>(buf + ((mt * XW + h) * 64 + lane) * 16);
+    };
+    rd(xa, 0);
+#pragma unroll
+    for (int mt = 0; mt < XMT; mt += 2) {
+      rd(xb, mt + 1);
+      acc[mt][0] = mma_tile<WT>(ww[0], xa, acc[mt][0]);
+      acc[mt][1] = mma_tile<WT>(ww[1], xa, acc[mt][1]);
+      if (mt + 2 < XMT) rd(xa, mt + 2);
+      acc[mt + 1][0] = mma_tile<WT>(ww[0], xb, acc[mt + 1][0]);
+      acc[mt + 1][1] = mma_tile<WT>(ww[1], xb, acc[mt + 1][1]);
+    }
+    // order: reads of tile 0, then (reads of tile mt+1, MFMAs of tile mt)
+    constexpr int RD = XW;                                                     // DS reads per tile
+    constexpr int MF = 2 * (WT == DT_F32 ? 4 : (WT == DT_FP8 ? 2 : 1));        // MFMAs per tile
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+    for (int mt = 0; mt + 1 < XMT; ++mt) {
+      __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+  };
+
+#pragma unroll
+  for (int j = 0; j < DIST; ++j) {
+    issue_x(j);
+    issue_w(w[j], j);
+  }
+  for (int s0 = 0; s0 < nst; s0 += DIST) {
+#pragma unroll
+    for (int j = 0; j < DIST; ++j) {
+      const int s = s0 + j;
+      // Stage s (activations and weights) has landed for this wave; after
+      // the barrier also for every wave, and stage s-1's buffer is free.  A
+      // plain s_barrier: __syncthreads' release fence would wait for every
+      // outstanding load, draining the prefetch.
+      wait_vmcnt<(DIST - 1) * LPS>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_x(s + DIST);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < nst) compute(w[j], xs[s % NBUF]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(w[j], s + DIST);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();   // no LDS copy may still be in flight when the workgroup exits
+  if (!active) return;
+
+  const int nq = (lane >> 4) * 4;
+  const float* sc = a.wscale;
+#pragma unroll
+  for (int mt = 0; mt < XMT; ++mt) {
+    const int row = mt * 16 + (lane & 15);
+    if (row >= a.M) continue;
+    float v0[4], v1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v0[q] = acc[mt][0][q]; v1[q] = acc[mt][1][q]; }
+    if constexpr (EPI == EPI_SWIGLU) {
+      epi_swiglu<AT>(a, sc, row, nt0 * 16 + nq, v0, v1);
+    } else {
+      epi_store<AT, EPI>(a, sc, row, nt0 * 16 + nq, v0, ks);
+      epi_store<AT, EPI>(a, sc, row, (nt0 + 1) * 16 + nq, v1, ks);
+    }
+  }
+}
+
+// Sum of the contraction splits (in split order) and the epilogue.  One
+// thread per row and four output columns (hidden columns for SwiGLU).
+template <int AT, int EPI>
+__global__ __launch_bounds__(256) void k_splitk_epi(const GemmArgs a, const float* part, int ksplit, int64_t pstride,
+                                                    int ldp, int quads) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int row = (int)(idx / quads), qd = (int)(idx % quads);
+  if (row >= a.M) return;
+  const float* sc = nullptr;   // fp8 row scales were applied to the partials
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int j = qd * 4;
+    const int ng = (j >> 4) * 32 + (j & 15);
+    float g[4] = {0, 0, 0, 0}, u[4] = {0, 0, 0, 0};
+    for (int s = 0; s < ksplit; ++s) {
+      const float* p = part + s * pstride + (int64_t)row * ldp;
+      const float4 gv = *reinterpret_cast<const float4*>(p + ng);
+      const float4 uv = *reinterpret_cast<const float4*>(p + ng + 16);
+      g[0] += gv.x; g[1] += gv.y; g[2] += gv.z; g[3] += gv.w;
+      u[0] += uv.x; u[1] += uv.y; u[2] += uv.z; u[3] += uv.w;
+    }
+    epi_swiglu<AT>(a, sc, row, ng, g, u);
+  } else {
+    const int n = qd * 4;
+    float v[4] = {0, 0, 0, 0};
+    for (int s = 0; s < ksplit; ++s) {
+      const float4 pv = *reinterpret_cast<const float4*>(part + s * pstride + (int64_t)row * ldp + n);
+      v[0] += pv.x; v[1] += pv.y; v[2] += pv.z; v[3] += pv.w;
+    }
+    epi_store<AT, EPI>(a, nullptr, row, n, v, 0);
+  }
+}
+
+template <int WT, int AT, int EPI>
+static void run_x(const GemmArgs& a, hipStream_t s) {
+  const int blocks = a.n_chunks * (a.ksplit > 1 ? a.ksplit : 1);
+  hipLaunchKernelGGL((k_gemm_x<WT, AT, EPI>), dim3(blocks), dim3(256), 0, s, a);
+}
+
+template <int WT, int AT>
+static void run_x_epi(int epi, const GemmArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_F32: run_x<WT, AT, EPI_F32>(a, s); break;
+    case EPI_RESID: run_x<WT, AT, EPI_RESID>(a, s); break;
+    case EPI_SWIGLU: run_x<WT, AT, EPI_SWIGLU>(a, s); break;
+    case EPI_QKV: run_x<WT, AT, EPI_QKV>(a, s); break;
+    case EPI_ROWS: run_x<WT, AT, EPI_ROWS>(a, s); break;
+  }
+}
+
+void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s) {
+  if (wdt == DT_F32) run_x_epi<DT_F32, DT_F32>(epi, a, s);
+  else if (wdt == DT_BF16) run_x_epi<DT_BF16, DT_BF16>(epi, a, s);
+  else run_x_epi<DT_FP8, DT_BF16>(epi, a, s);
+}
+
+template <int AT>
+static void run_sk(int epi, const GemmArgs& a, const float* part, int ksplit, int64_t pstride, int ldp, hipStream_t s) {
+  const int quads = (epi == EPI_SWIGLU) ? a.ldy / 4 : (a.Nt * 16) / 4;
+  const int64_t threads = (int64_t)a.M * quads;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  switch (epi) {
+    case EPI_RESID: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_RESID>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_SWIGLU>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_QKV>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
+    case EPI_ROWS: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_ROWS>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
+    default: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_F32>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
+  }
+}
+
+void launch_splitk_epi(int adt, int epi, const GemmArgs& a, const float* part, int ksplit, int64_t pstride, int ldp,
+                       hipStream_t s) {
+  if (adt == DT_F32) run_sk<DT_F32>(epi, a, part, ksplit, pstride, ldp, s);
+  else run_sk<DT_BF16>(epi, a, part, ksplit, pstride, ldp, s);
+}
+
+}  // namespace cd

@@ -16,7 +16,10 @@ namespace cd {
 
 constexpr int ROUTE_BLK = 512;
 
-// one wave per token; lane j ends up holding the j-th choice
+// One wave per token; lane j ends up holding the j-th choice.  Non-finite
+// logits cannot produce an invalid id: NaN ranks as -inf and every round
+// picks the best expert not yet taken (ties and -inf to the lowest id), so
+// the k ids are always distinct and inside [0, E).
 __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -29,9 +32,11 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
     if (e < a.E) {
       x = 0.f;
       for (int s = 0; s < a.nsplit; ++s) x += a.logits[((int64_t)s * a.T + t) * a.E + e];
+      if (x != x) x = -INFINITY;
     }
     v[i] = x;
   }
+  uint32_t taken = 0;
   float my_v = -INFINITY;
   int my_id = 0;
   for (int j = 0; j < a.k; ++j) {
@@ -40,7 +45,7 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      if (e < a.E && v[i] != -INFINITY && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+      if (e < a.E && !(taken & (1u << i)) && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -51,11 +56,12 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
     if (lane == j) { my_v = bv; my_id = bi; }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;
+      if (lane + 64 * i == bi) taken |= 1u << i;
   }
-  // gates: softmax over the k selected logits (lane 0 holds the largest)
+  // gates: softmax over the k selected logits (lane 0 holds the largest);
+  // uniform if every selected logit is -inf
   const float mx = __shfl(my_v, 0, 64);
-  float g = lane < a.k ? expf(my_v - mx) : 0.f;
+  float g = lane < a.k ? (mx == -INFINITY ? 1.f : expf(my_v - mx)) : 0.f;
   const float sum = wave_sum(g);
   if (lane < a.k) {
     g = g / sum;
@@ -96,7 +102,8 @@ __global__ __launch_bounds__(256) void k_route_one(RouteArgs a) {
 #pragma unroll
   for (int j = 0; j < RG; ++j) {
     const int i = tid * RG + j;
-    ex[j] = (tid < ng && i < n) ? a.topk_id[i] : -1;
+    const int e = (tid < ng && i < n) ? a.topk_id[i] : -1;
+    ex[j] = (e >= 0 && e < E) ? e : -1;
   }
 #pragma unroll
   for (int j = 0; j < RG; ++j)
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(256) void k_route_count(RouteArgs a) {
   const int beg = b * ROUTE_BLK, cnt = min(ROUTE_BLK, n - beg);
   for (int i = threadIdx.x; i < cnt; i += 256) ex[i] = a.topk_id[beg + i];
   __syncthreads();
-  const int e = threadIdx.x;
+  const int e = threadIdx.x;   // ids outside [0, E) match no expert
   if (e >= a.E) return;
   int c = 0;
   for (int i = 0; i < cnt; ++i) c += (ex[i] == e);
