@@ -72,7 +72,7 @@ struct Plan {
   int64_t rq, canvas, argmax, lock, entropy, pmax, info, h, u, q, o, part_o, part_ml, rlog, topk_id,
       topk_gate, blk_cnt, seg_off, row_map, slot, tiles, n_tiles, aperm, yperm, sact, logits, spart, rope,
       kcache, vcache, zero, xpart;
-  int64_t max_rows, max_tiles, n_blk_max, n_chunks;
+  int64_t max_rows, max_tiles, n_blk_max, n_chunks, xpart_elems;
   int64_t kv_req_stride, kv_layer_stride;   // elements
   int64_t state_bytes;
 };
@@ -185,8 +185,11 @@ Plan make_plan(const cd_config& c) {
   p.sact = s.take((int64_t)ae * T * std::max(c.shared_hidden, 1));
   p.logits = s.take(4LL * R * C * c.vocab);
   {
+    // fp32 split partials of the per-layer dense GEMMs; wider layers (the LM
+    // head) use fewer splits so that ks * M * Npad always fits
     const int64_t np = std::max(std::max(p.qkv_npad, p.wo_npad), std::max(p.sgu_npad, p.sdn_npad));
-    p.xpart = s.take(4LL * MAX_XSPLIT * 256 * np);
+    p.xpart_elems = (int64_t)MAX_XSPLIT * 256 * np;
+    p.xpart = s.take(4LL * p.xpart_elems);
   }
   p.spart = s.take(16LL * R * C * p.n_chunks);
   p.rope = s.take(8LL * p.ctx * (dh / 2));
@@ -288,9 +291,7 @@ int router_split(const cd_config& g, int T) {
   return sp;
 }
 
-// The LDS-staged dense path is switched off: on the GPU it gave wrong
-// results from the second denoise pass on, with no cause shown yet.
-constexpr bool USE_LDS_DENSE = false;
+constexpr bool USE_LDS_DENSE = true;
 
 // Dense GEMM.  Up to 256 rows: one workgroup per 128 output columns holds
 // all rows, activations staged in LDS; a narrow layer splits its contraction
@@ -300,13 +301,15 @@ void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_
   if (USE_LDS_DENSE && M <= 256 && a.ksplit <= 1) {
     a.M = M;
     const int kt = a.K / kfrag(wdt);
+    const int npad = a.Nt * 16;
     int ks = 1;
     while (ks < MAX_XSPLIT && a.n_chunks * ks * 2 <= 256 && kt / (ks * 2) >= 4) ks *= 2;
+    // the fp32 partials of every split must fit the partial buffer
+    while (ks > 1 && (int64_t)ks * M * npad > c->p.xpart_elems) ks /= 2;
     if (ks == 1) {
       launch_gemm_x(wdt, c->p.adt, epi, a, s);
       return;
     }
-    const int npad = a.Nt * 16;
     GemmArgs pa = a;
     pa.ksplit = ks;
     pa.Y = c->st<float>(c->p.xpart);
