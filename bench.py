@@ -55,31 +55,35 @@ def gpu_part(w, steps, warmup, prof_steps, do_block=True):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    C, L, E, k, d, fe = w["C"], w["L"], w["E"], w["k"], w["d"], w["fe"]
-    eng = Engine(w, device=dev, max_ctx=w["P0"] + C)
+    C, L, E, k, R = w["C"], w["L"], w["E"], w["k"], w["R"]
+    n_blocks = w.get("blocks", 1)
+    eng = Engine(w, device=dev, max_ctx=w["P0"] + n_blocks * C)
     ctx = eng.ctx
     B.cd_synth_weights(ctx, w["weight_seed"])
     torch.cuda.synchronize()
     log(f"weights synthesized ({eng.weights.numel() / 1e9:.1f} GB)")
-    prefix = torch.from_numpy(synth_inputs.prefix_ids(w["V"], w["P0"], w["prefix_seed"])).to(dev)
     t0 = time.perf_counter()
-    B.cd_prefill(ctx, 0, prefix)
+    for r in range(R):
+        prefix = torch.from_numpy(synth_inputs.prefix_ids(w["V"], w["P0"], w["prefix_seed"], r)).to(dev)
+        B.cd_prefill(ctx, r, prefix)
     torch.cuda.synchronize()
     prefill_ms = (time.perf_counter() - t0) * 1e3
-    log(f"prefill of {w['P0']} tokens: {prefill_ms:.1f} ms")
+    log(f"prefill of {R} x {w['P0']} tokens: {prefill_ms:.1f} ms")
     seed = w["gen_seed"]
     state = {"t": 0}
 
     def fresh():
-        B.cd_init_canvas(ctx, 0, seed, 0)
+        for r in range(R):
+            B.cd_init_canvas(ctx, r, seed, 0)
         state["t"] = 0
 
     def one_step():
         if state["t"] >= w["max_steps"]:
-            B.cd_abort_canvas(ctx, 0)
+            for r in range(R):
+                B.cd_abort_canvas(ctx, r)
             fresh()
-        B.cd_denoise_step(ctx, 1, eng.info)
-        info = B.cd_read_step_info(ctx, eng.info, 1)[0]       # the loop's stop-flag read-back
+        B.cd_denoise_step(ctx, R, eng.info)
+        info = B.cd_read_step_info(ctx, eng.info, R)          # the loop's stop-flag read-back
         state["t"] += 1
         return info
 
@@ -103,8 +107,9 @@ def gpu_part(w, steps, warmup, prof_steps, do_block=True):
     B.cd_profile(ctx, 0)
 
     # routing of one pass: experts actually streamed per layer
-    tid = torch.zeros(L, C, k, dtype=torch.int32, device=dev)
-    tg = torch.zeros(L, C, k, dtype=torch.float32, device=dev)
+    T = R * C
+    tid = torch.zeros(L, T, k, dtype=torch.int32, device=dev)
+    tg = torch.zeros(L, T, k, dtype=torch.float32, device=dev)
     B.cd_set_trace(ctx, None, tid, tg)
     one_step()
     B.cd_set_trace(ctx)
@@ -114,31 +119,37 @@ def gpu_part(w, steps, warmup, prof_steps, do_block=True):
     route = {"max_tokens_per_expert": int(counts.max()),
              "mean_max_tokens_per_expert": float(counts.max(axis=1).mean()),
              "mean_row_tiles": float(np.mean([(np.ceil(c / 32)).sum() for c in counts]))}
-
+    out = dict(elapsed=el, prof=prof, active=active, route=route, prefill_ms=prefill_ms, block_s=float("nan"),
+               block_passes=0, blocks=[], device=torch.cuda.get_device_name(dev))
     if not do_block:
         eng.close()
-        return dict(elapsed=el, prof=prof, active=active, route=route, prefill_ms=prefill_ms, block_s=float("nan"),
-                    block_passes=0, device=torch.cuda.get_device_name(dev))
-    # one full block: canvas start, passes to the stop, commit
-    B.cd_abort_canvas(ctx, 0)
-    out = torch.empty(C, dtype=torch.int32, device=dev)
+        return out
+    # full blocks: every request starts a canvas, passes run until each request
+    # has met its stop (at the latest all at the pass cap), then every request commits
+    for r in range(R):
+        B.cd_abort_canvas(ctx, r)
+    ids_out = torch.empty(C, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    B.cd_init_canvas(ctx, 0, seed, 0)
-    passes = 0
-    while True:
-        B.cd_denoise_step(ctx, 1, eng.info)
-        info = B.cd_read_step_info(ctx, eng.info, 1)[0]
-        passes += 1
-        if info.stop:
-            break
-    B.cd_commit_block(ctx, 0, out)
-    torch.cuda.synchronize()
-    block_s = time.perf_counter() - t0
-    log(f"block of {passes} passes + commit: {block_s * 1e3:.1f} ms")
+    t_all = time.perf_counter()
+    for b in range(n_blocks):
+        t0 = time.perf_counter()
+        for r in range(R):
+            B.cd_init_canvas(ctx, r, seed, b)
+        passes, stopped = 0, np.zeros(R, dtype=bool)
+        while not stopped.all():
+            B.cd_denoise_step(ctx, R, eng.info)
+            infos = B.cd_read_step_info(ctx, eng.info, R)
+            passes += 1
+            stopped |= np.array([bool(i.stop) for i in infos])
+        for r in range(R):
+            B.cd_commit_block(ctx, r, ids_out)
+        torch.cuda.synchronize()
+        out["blocks"].append({"passes": passes, "ms": round((time.perf_counter() - t0) * 1e3, 2)})
+    out["block_s"] = (time.perf_counter() - t_all) / n_blocks
+    out["block_passes"] = out["blocks"][0]["passes"]
+    log(f"{n_blocks} block(s) of passes + commit: {out['blocks']}")
     eng.close()
-    return dict(elapsed=el, prof=prof, active=active, route=route, prefill_ms=prefill_ms, block_s=block_s,
-                block_passes=passes, device=torch.cuda.get_device_name(dev))
+    return out
 
 
 def measured_traffic(kernel_part):
@@ -161,14 +172,20 @@ def measured_traffic(kernel_part):
 
 
 def expert_bytes(w, active, part):
-    """Algorithmic HBM bytes of one grouped expert GEMM launch (bf16): the
-    weights of every expert that received tokens, the gathered activation
-    rows read and the output rows written."""
-    T, k, d, fe = w["C"], w["k"], w["d"], w["fe"]
-    es = 2
+    """Algorithmic HBM bytes of one grouped expert GEMM launch: the weights of
+    every expert that received tokens (bf16, or fp8 plus fp32 row scales), the
+    gathered bf16 activation rows read and the output rows written."""
+    T, k, d, fe = w["R"] * w["C"], w["k"], w["d"], w["fe"]
+    wes = 1 if w["wdtype"] == "fp8" else 2
+    scale = 4 if w["wdtype"] == "fp8" else 0
     if part == "gate_up":
-        return active * (2 * fe * d * es) + T * k * d * es + T * k * fe * es
-    return active * (d * fe * es) + T * k * fe * es + T * k * d * es
+        return active * (2 * fe * d * wes + 2 * fe * scale) + T * k * d * 2 + T * k * fe * 2
+    return active * (d * fe * wes + d * scale) + T * k * fe * 2 + T * k * d * 2
+
+
+def expert_flops(w, part):
+    T, k, d, fe = w["R"] * w["C"], w["k"], w["d"], w["fe"]
+    return 2 * T * k * d * (2 * fe if part == "gate_up" else fe)
 
 
 def cpu_baseline(w):
@@ -263,29 +280,44 @@ def main():
     part = "gate_up" if dom == "expert_gate_up" else "down"
     byts = expert_bytes(w, g["active"], part)
     achieved = byts / (per[dom] * 1e-3) / 1e9
+    R, C = w["R"], w["C"]
+    gen = w.get("blocks", 1) > 1
+    committed = (R * C / g["block_s"]) if g["block_passes"] else None
+    wl = (f"{args.workload}: {w['L']} MoE layers, d={w['d']}, {w['Hq']}/{w['Hkv']} heads x {w['dh']}, "
+          f"{w['E']} experts top-{w['k']} (hidden {w['fe']}) + shared {w['fs']}, vocab {w['V']}, "
+          f"{w['wdtype']} weights, {R} request(s) x prefix {w['P0']}, canvas {C}")
+    if gen:
+        wl += f", {w['blocks']} blocks"
+    roof = {"kernel": f"grouped expert GEMM ({part.replace('_', '/')})", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(part) if args.workload == "step_bf16" else None,
+            "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5), "active_experts": g["active"]}
+    if R * C * w["k"] / w["E"] >= 256:
+        # many rows per expert: the grouped GEMM runs on the bf16 MFMA pipe
+        tf = expert_flops(w, part) / (per[dom] * 1e-3) / 1e12
+        roof = {"kernel": roof["kernel"], "bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": int(expert_flops(w, part)), "avg_launch_ms": round(per[dom], 5),
+                "hbm_gbs": round(achieved, 1)}
     line = {
         "metric": "canvas denoise steps/s + committed tok/s (256-tok block), % MFMA/HBM peak",
-        "value": round(1e3 / ms, 3), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(committed, 3) if gen else round(1e3 / ms, 3),
+        "unit": "committed tok/s" if gen else "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w["wdtype"], "data": "synthetic",
-        "config": {"workload": (f"{args.workload}: {w['L']} MoE layers, d={w['d']}, {w['Hq']}/{w['Hkv']} heads x "
-                                f"{w['dh']}, {w['E']} experts top-{w['k']} (hidden {w['fe']}) + shared {w['fs']}, "
-                                f"vocab {w['V']}, prefix {w['P0']}, canvas {w['C']}"),
-                   "requests": w["R"], "canvas": w["C"], "prefix": w["P0"]},
-        "committed_tok_s": round(w["C"] / g["block_s"], 2) if g["block_passes"] else None,
-        "block_passes": g["block_passes"], "block_ms": round(g["block_s"] * 1e3, 2),
+        "vs_baseline": None, "dtype": "f32" if w["wdtype"] == "f32" else "bf16", "data": "synthetic",
+        "config": {"workload": wl, "weights": w["wdtype"], "requests": R, "canvas": C, "prefix": w["P0"], "blocks": w.get("blocks", 1)},
+        "steps_per_s": round(1e3 / ms, 3),
+        "canvas_tok_s": round(R * C * 1e3 / ms, 1),
+        "committed_tok_s": round(committed, 2) if committed else None,
+        "block_passes": g["block_passes"], "blocks": g["blocks"],
         "prefill_ms": round(g["prefill_ms"], 2),
-        "roofline": {"kernel": f"grouped expert GEMM ({part.replace('_', '/')})", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(part) if args.workload == "step_bf16" else None,
-                     "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5),
-                     "active_experts": g["active"]},
+        "roofline": roof,
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items() if v > 0},
         "routing": g["route"],
         "device": g["device"],
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "step_bf16":
         log("cpu baseline (oracle sample)")
         cb = cpu_baseline(w)
         cb.pop("est_step_s")
