@@ -40,7 +40,7 @@ int32_t hip_status(const char* where) {
 
 constexpr int64_t ALIGN = 256;
 constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows
-constexpr int MAX_SPLIT = 16;          // attention key splits
+constexpr int MAX_SPLIT = ATT_MAX_SPLIT;   // attention key splits
 constexpr int MAX_RSPLIT = 16;         // router contraction splits
 constexpr int MAX_XSPLIT = 16;         // dense contraction splits (M <= 256)
 
@@ -86,7 +86,8 @@ int32_t validate_config(const cd_config* c) {
   if (c->weight_dtype < CD_F32 || c->weight_dtype > CD_FP8) return fail(CD_ERR_INVALID_ARG, "bad weight_dtype");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(CD_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c->n_q_heads % c->n_kv_heads) return fail(CD_ERR_INVALID_ARG, "n_q_heads %% n_kv_heads != 0");
-  if (c->n_q_heads / c->n_kv_heads > 4) return fail(CD_ERR_UNSUPPORTED, "at most 4 query heads per KV head");
+  if (c->n_q_heads / c->n_kv_heads > 4 || c->n_q_heads / c->n_kv_heads == 3)
+    return fail(CD_ERR_UNSUPPORTED, "1, 2 or 4 query heads per KV head");
   if (c->d_model % 64 || c->expert_hidden % 64 || c->shared_hidden % 64 || (c->n_q_heads * c->head_dim) % 64)
     return fail(CD_ERR_UNSUPPORTED, "d_model, expert_hidden, shared_hidden, n_q_heads*head_dim must be multiples of 64");
   if (c->n_experts > 256 || c->top_k > 16 || c->top_k > c->n_experts)
@@ -361,7 +362,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
   int nkeys_max = 0;
   for (int r = r0; r < r0 + n_req; ++r) nkeys_max = std::max(nkeys_max, c->req[r].P + rows_per_req);
   const int G = g.n_q_heads / g.n_kv_heads;
-  const int TB = 128 / G;
+  const int TB = ATT_QR / G;
   AttnArgs at;
   memset(&at, 0, sizeof at);
   at.Q = Q; at.O = O;
@@ -371,11 +372,13 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
   at.pos0 = pos0; at.pos0_stride = pos_stride;
   at.causal = causal ? 1 : 0;
   at.q_blocks = (rows_per_req + TB - 1) / TB;
+  // key splits: enough work items for one per CU, each split at least two
+  // 64-key blocks
   const int base_wg = n_req * g.n_kv_heads * at.q_blocks;
-  int ns = std::max(1, (512 + base_wg - 1) / base_wg);
+  int ns = std::max(1, (256 + base_wg - 1) / base_wg);
   ns = std::min(ns, MAX_SPLIT);
-  ns = std::min(ns, std::max(1, (nkeys_max + 63) / 64));
-  at.split_len = (int)round_up((nkeys_max + ns - 1) / ns, 32);
+  ns = std::min(ns, std::max(1, (nkeys_max + 2 * ATT_KB - 1) / (2 * ATT_KB)));
+  at.split_len = (int)round_up((nkeys_max + ns - 1) / ns, ATT_KB);
   at.n_split = (nkeys_max + at.split_len - 1) / at.split_len;
   at.part_o = c->st<float>(p.part_o);
   at.part_ml = c->st<float>(p.part_ml);

@@ -13,11 +13,13 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
 // ---- bf16 -------------------------------------------------------------
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-// fp32 -> bf16, round to nearest even (finite inputs)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (the hardware conversion)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two fp32 -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---- E4M3FN (OCP) -> fp32, exact ----------------------------------------
@@ -52,6 +54,17 @@ __device__ __forceinline__ int32_t canvas_token(uint64_t seed, uint32_t pos, uin
   u4 c = {pos, step, block, req};
   u4 r = philox(c, (uint32_t)seed, (uint32_t)(seed >> 32));
   return (int32_t)(((uint64_t)r.x * V) >> 32);
+}
+
+// ---- LDS staging ----------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).  Loads
+// that copy global memory straight into LDS (global_load_lds) count in vmcnt.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // ---- wave reductions -----------------------------------------------------

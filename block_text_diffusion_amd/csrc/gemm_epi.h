@@ -12,8 +12,8 @@ __device__ __forceinline__ void store4(void* base, int64_t idx, float v0, float 
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(v0, v1, v2, v3);
   } else {
     uint2 p;
-    p.x = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
-    p.y = (uint32_t)f2bf(v2) | ((uint32_t)f2bf(v3) << 16);
+    p.x = pack_bf16(v0, v1);
+    p.y = pack_bf16(v2, v3);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = p;
   }
 }
@@ -23,7 +23,7 @@ __device__ __forceinline__ void store2(void* base, int64_t idx, float v0, float 
     *reinterpret_cast<float2*>(reinterpret_cast<float*>(base) + idx) = make_float2(v0, v1);
   } else {
     *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(base) + idx) =
-        (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+        pack_bf16(v0, v1);
   }
 }
 template <int AT>

@@ -1,21 +1,31 @@
 // Canvas attention: softmax(Q K^T / sqrt(dh)) V over the committed KV cache
 // plus the canvas itself, with no mask (every canvas token sees every other
-// canvas token and the whole committed history); the same kernel with a
-// causal mask serves the prompt prefill.
+// canvas token and the whole committed history: the bidirectional denoising
+// pass of the DiffusionGemma pages, canvas explainer step ③); the same kernel
+// with a causal mask serves the prompt prefill (step ①).
 //
-// Work item = (request, KV head, block of 128 query rows, key split).  The
-// 128 query rows are the Hq/Hkv query heads that share one KV head times
-// 128/(Hq/Hkv) tokens, so each K/V fragment feeds every head of its group
-// (grouped-query reuse).  Each wave owns 32 query rows (two 16-row tiles):
-//  * S^T = K Q^T on MFMA (A = key tile, B = query tile), so a lane holds 4
-//    keys of one query and the P fragment of the next product is already in
-//    its registers (no shuffle or LDS round trip between the two MFMAs);
+// Work item = (request, KV head, block of 256 query rows, key split).  The
+// 256 query rows are the Hq/Hkv query heads that share one KV head times
+// 256/(Hq/Hkv) tokens, so every K/V byte feeds all heads of its group.  Each
+// of the 8 waves owns 32 query rows (two 16-row tiles); two waves share a
+// SIMD, so one's softmax (VALU, exp) overlaps the other's MFMAs.
+//  * Keys go in blocks of 64.  The block's K tile and V^T tile are copied
+//    from global memory straight into LDS (global_load_lds, 16 bytes a lane),
+//    already cut into 1 KB MFMA operand fragments, shared by the 8 waves and
+//    prefetched DIST blocks ahead, so the cache is read once per work item
+//    and every LDS read is one conflict-free 1 KB wave access.
+//  * S^T = K Q^T on MFMA (A = key fragment from LDS, B = query fragment held
+//    in registers for the whole loop): a lane ends with keys of one query.
+//    The 16 key rows of a K fragment are taken in the order that leaves each
+//    lane holding 8 consecutive keys of a 32-key chunk, which is exactly the
+//    P^T operand of the next product, so P never leaves registers.
 //  * online softmax in base 2 with the 1/sqrt(dh) scale folded in; row max
 //    and sum reduce across the 4 lane groups with two xor shuffles;
 //  * O^T += V^T P^T on MFMA; V is cached transposed ([dh][ctx]) so its
 //    fragments are contiguous in the key index.
-// Each split writes an unnormalised partial (O, max, sum); a merge kernel
-// combines the splits, which fills the chip at one request's 8 KV heads.
+// With one key split the kernel normalises and writes O itself; otherwise
+// each split writes an unnormalised partial (O, max, sum) and a merge kernel
+// combines them.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,20 +35,43 @@ template <int AT>
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t elem) {
   return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(base) + elem * (AT == DT_F32 ? 4 : 2));
 }
-template <int AT>
-__device__ __forceinline__ uint2 ld8(const void* base, int64_t elem) {
-  return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(base) + elem * (AT == DT_F32 ? 4 : 2));
+
+template <int AT, int DH>
+struct AttnShape {
+  static constexpr int ES = (AT == DT_F32) ? 4 : 2;
+  static constexpr int KF = (AT == DT_F32) ? 16 : 32;   // contraction elements per fragment
+  static constexpr int KQ = KF / 4;                     // per lane
+  static constexpr int NK = DH / KF;                    // K fragments across dh
+  static constexpr int ND = DH / 16;                    // 16-wide dh tiles
+  static constexpr int VF = (AT == DT_F32) ? 4 : 2;     // V fragments per dh tile and key block
+  static constexpr int NFK = 4 * NK, NFV = ND * VF, NF = NFK + NFV;
+  static constexpr int NW = 8;                          // waves per workgroup
+  static constexpr int QTW = 2;                         // 16-row query tiles per wave
+  static constexpr int FPW = NF / NW;                   // fragments each wave copies
+  static constexpr int STAGE = NF * 1024;
+  static constexpr int NBUF = (STAGE * 4 <= 128 * 1024) ? 4 : 2;
+  static constexpr int DIST = NBUF - 1;
+  static_assert(NF % NW == 0 && NW * QTW * 16 == ATT_QR, "work split");
+};
+
+// key held by row i (0..15) of K fragment subtile st (0..3) of a 64-key block:
+// subtiles 2c and 2c+1 interleave the 32 keys of chunk c in groups of four
+__device__ __forceinline__ int att_key(int st, int i) {
+  return 32 * (st >> 1) + 8 * (i >> 2) + 4 * (st & 1) + (i & 3);
 }
 
 template <int AT, int DH>
-__global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
-  constexpr int KF = (AT == DT_F32) ? 16 : 32;   // contraction elements per fragment
-  constexpr int KQ = KF / 4;                     // per lane
-  constexpr int NK = DH / KF;                    // fragments across dh
-  constexpr int ND = DH / 16;                    // 16-wide d tiles of the output
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
+  using S = AttnShape<AT, DH>;
+  constexpr int KF = S::KF, KQ = S::KQ, NK = S::NK, ND = S::ND, NFK = S::NFK, FPW = S::FPW, QTW = S::QTW;
+  constexpr int WR = QTW * 16;                   // query rows per wave
+  constexpr int NBUF = S::NBUF, DIST = S::DIST, STAGE = S::STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.Hq / a.Hkv;
-  const int TB = 128 / G;                        // tokens per query block
+  const int TB = ATT_QR / G;                     // tokens per query block
 
   int bid = blockIdx.x;
   const int s = bid % a.n_split; bid /= a.n_split;
@@ -50,143 +83,225 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
   const int pos0 = a.pos0[r * a.pos0_stride];
   const int nrows = a.rows_per_req;
   const int nkeys = pos0 + nrows;
-  const int hh = (wave * 32) / TB;               // head within group
+  const int hh = (wave * WR) / TB;               // head within group
   const int h = g * G + hh;
-  const int tok0 = qb * TB + (wave * 32) % TB;   // first token of this wave
+  const int tok0 = qb * TB + (wave * WR) % TB;   // first token of this wave
 
   const int kbeg = s * a.split_len;
   int kend = min(kbeg + a.split_len, nkeys);
-  if (a.causal) kend = min(kend, pos0 + min(tok0 + 32, nrows));
+  if (a.causal) kend = min(kend, pos0 + min((qb + 1) * TB, nrows));   // last token of the work item
+  const int nblk = kend > kbeg ? (kend - kbeg + ATT_KB - 1) / ATT_KB : 0;
 
-  const int64_t ld = (int64_t)a.Hq * DH;
-  const void* kc = reinterpret_cast<const uint8_t*>(a.kc) + (int64_t)r * a.kv_req_stride * (AT == DT_F32 ? 4 : 2);
-  const void* vc = reinterpret_cast<const uint8_t*>(a.vc) + (int64_t)r * a.kv_req_stride * (AT == DT_F32 ? 4 : 2);
-  const int64_t khead = (int64_t)g * a.max_ctx * DH;   // [Hkv][ctx][dh]
-  const int64_t vhead = (int64_t)g * DH * a.max_ctx;   // [Hkv][dh][ctx]
+  const int ae = S::ES;
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.kc) + ((int64_t)r * a.kv_req_stride + (int64_t)g * a.max_ctx * DH) * ae;
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.vc) + ((int64_t)r * a.kv_req_stride + (int64_t)g * DH * a.max_ctx) * ae;
+  // last key a copy may start at: K rows up to kend-1; V^T groups of 4 (fp32)
+  // or 8 (bf16) keys starting at or below kend-1 (the cache length is a
+  // multiple of 64, so such a group stays inside the row)
+  constexpr int VG = (AT == DT_F32) ? 4 : 8;
+  const int klast = max(kend - 1, 0);
+  const int vlast = (klast / VG) * VG;
+
+  // copy of key block b (clamped to the last block) into its LDS buffer
+  auto issue = [&](int b) {
+    const int bc = min(b, nblk - 1);
+    const int kb0 = kbeg + bc * ATT_KB;
+    uint8_t* buf = lds + (b % NBUF) * STAGE;
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+      const int f = wave * FPW + i;
+      const uint8_t* src;
+      if (f < NFK) {
+        const int st = f / NK, kk = f % NK;
+        const int key = min(kb0 + att_key(st, lane & 15), klast);
+        src = kc + ((int64_t)key * DH + kk * KF + (lane >> 4) * KQ) * ae;
+      } else {
+        const int fv = f - NFK;
+        int dt, vk;
+        if constexpr (AT == DT_F32) { dt = fv / 4; const int st = fv % 4; vk = kb0 + 32 * (st >> 1) + 8 * (lane >> 4) + 4 * (st & 1); }
+        else { dt = fv / 2; const int c = fv % 2; vk = kb0 + 32 * c + 8 * (lane >> 4); }
+        vk = min(vk, vlast);
+        src = vc + ((int64_t)(dt * 16 + (lane & 15)) * a.max_ctx + vk) * ae;
+      }
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_void*)(buf + f * 1024), 16, 0, 0);
+    }
+  };
 
   // query fragments, resident for the whole key loop
-  u32x4 qf[2][NK];
-  int qtok[2];
+  const int64_t ld = (int64_t)a.Hq * DH;
+  u32x4 qf[QTW][NK];
+  int qpos[QTW];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    int tok = tok0 + qt * 16 + (lane & 15);
-    qtok[qt] = tok;
-    int tc = min(tok, nrows - 1);
-    int64_t row = (int64_t)r * nrows + tc;
+  for (int qt = 0; qt < QTW; ++qt) {
+    const int tok = tok0 + qt * 16 + (lane & 15);
+    qpos[qt] = pos0 + tok;
+    const int tc = min(tok, nrows - 1);
+    const int64_t row = (int64_t)r * nrows + tc;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) qf[qt][kk] = ld16<AT>(a.Q, row * ld + h * DH + kk * KF + (lane >> 4) * KQ);
   }
 
   const float sl2 = 1.4426950408889634f / sqrtf((float)DH);
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x4 o[2][ND];
+  float m[QTW], l[QTW];
+  f32x4 o[QTW][ND];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < QTW; ++qt) {
+    m[qt] = -INFINITY; l[qt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[qt][dt] = f32x4{0, 0, 0, 0};
+  }
 
-  for (int key0 = kbeg; key0 < kend; key0 += 32) {
-    // S^T tiles: [subtile st: keys key0+16st..][query tile qt]
-    f32x4 sacc[2][2];
+  if (nblk > 0) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      u32x4 kf[NK];
-      const int64_t krow = khead + (int64_t)(key0 + st * 16 + (lane & 15)) * DH;
+    for (int j = 0; j < DIST; ++j) issue(j);
+  }
+  for (int b = 0; b < nblk; ++b) {
+    // block b has landed for this wave; after the barrier for all waves, and
+    // every wave is done with block b-1, whose buffer the next copy reuses
+    wait_vmcnt<(DIST - 1) * FPW>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b + DIST);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* buf = lds + (b % NBUF) * STAGE + lane * 16;
+    const int kb0 = kbeg + b * ATT_KB;
+
+    // S^T[st][qt]: keys of subtile st x query tile qt
+    f32x4 sacc[4][QTW];
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) kf[kk] = ld16<AT>(kc, krow + kk * KF + (lane >> 4) * KQ);
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x4 acc = {0, 0, 0, 0};
+      for (int qt = 0; qt < QTW; ++qt) sacc[st][qt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
+      for (int kk = 0; kk < NK; ++kk) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(buf + (st * NK + kk) * 1024);
+#pragma unroll
+        for (int qt = 0; qt < QTW; ++qt) {
           if constexpr (AT == DT_F32) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf[kk][j]), __uint_as_float(qf[qt][kk][j]), acc, 0, 0, 0);
+              sacc[st][qt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf[j]), __uint_as_float(qf[qt][kk][j]),
+                                                                  sacc[st][qt], 0, 0, 0);
           } else {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kk]),
-                                                          __builtin_bit_cast(bf16x8, qf[qt][kk]), acc, 0, 0, 0);
+            sacc[st][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                                   __builtin_bit_cast(bf16x8, qf[qt][kk]), sacc[st][qt], 0, 0, 0);
           }
         }
-        sacc[st][qt] = acc;
       }
     }
-    // mask, online softmax (base 2)
-    float p[2][2][4];
+    // mask and online softmax (base 2); lane holds keys kb0 + 32c + 8*(lane/16) + 4*half + q.
+    // A block whose keys are all visible to every row of the wave skips the mask.
+    const bool full = kb0 + ATT_KB <= kend && (!a.causal || kb0 + ATT_KB - 1 <= pos0 + tok0);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int qpos = pos0 + qtok[qt];
+    for (int qt = 0; qt < QTW; ++qt) {
       float mt = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int kidx = key0 + st * 16 + (lane >> 4) * 4 + q;
-          bool ok = kidx < kend && (!a.causal || kidx <= qpos);
-          float v = ok ? sacc[st][qt][q] * sl2 : -INFINITY;
-          p[qt][st][q] = v;
-          mt = fmaxf(mt, v);
-        }
+          for (int q = 0; q < 4; ++q) mt = fmaxf(mt, sacc[st][qt][q]);
+      } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int kidx = kb0 + 32 * (st >> 1) + 8 * (lane >> 4) + 4 * (st & 1) + q;
+            const bool ok = kidx < kend && (!a.causal || kidx <= qpos[qt]);
+            const float v = ok ? sacc[st][qt][q] : -INFINITY;
+            sacc[st][qt][q] = v;
+            mt = fmaxf(mt, v);
+          }
+      }
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m[qt], mt);
-      const float alpha = (mn == -INFINITY) ? 1.0f : exp2f(m[qt] - mn);
+      // scores scale by sl2 > 0, so the scaled max is the max of the scaled scores
+      const float mn = fmaxf(m[qt], mt * sl2);
+      const float nmn = (mn == -INFINITY) ? 0.f : -mn;
+      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[qt] - mn);
       float sum = 0.f;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float e = (mn == -INFINITY) ? 0.f : exp2f(p[qt][st][q] - mn);
-          p[qt][st][q] = e;
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[st][qt][q], sl2, nmn));   // masked: exp2(-inf) = 0
+          sacc[st][qt][q] = e;
           sum += e;
         }
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
       l[qt] = l[qt] * alpha + sum;
       m[qt] = mn;
+      // the running max of a row rarely moves once a few blocks are in: skip
+      // the (exact, times one) rescale when no row of the tile needs it
+      if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        o[qt][dt][0] *= alpha; o[qt][dt][1] *= alpha; o[qt][dt][2] *= alpha; o[qt][dt][3] *= alpha;
+        for (int dt = 0; dt < ND; ++dt) {
+          o[qt][dt][0] *= alpha; o[qt][dt][1] *= alpha; o[qt][dt][2] *= alpha; o[qt][dt][3] *= alpha;
+        }
       }
     }
     // O^T += V^T P^T
+    if constexpr (AT == DT_F32) {
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      const int64_t vrow = vhead + (int64_t)(dt * 16 + (lane & 15)) * a.max_ctx + key0 + (lane >> 4) * 4;
-      if constexpr (AT == DT_F32) {
+      for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          u32x4 vf = ld16<AT>(vc, vrow + st * 16);
+        for (int st = 0; st < 4; ++st) {
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(buf + (NFK + dt * 4 + st) * 1024);
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
+          for (int qt = 0; qt < QTW; ++qt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vf[j]), p[qt][st][j], o[qt][dt], 0, 0, 0);
+              o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vf[j]), sacc[st][qt][j], o[qt][dt], 0, 0, 0);
         }
-      } else {
-        uint2 v0 = ld8<AT>(vc, vrow), v1 = ld8<AT>(vc, vrow + 16);
-        u32x4 vf = {v0.x, v0.y, v1.x, v1.y};
+    } else {
+      u32x4 pf[QTW][2];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          u32x4 pf;
-          pf[0] = (uint32_t)f2bf(p[qt][0][0]) | ((uint32_t)f2bf(p[qt][0][1]) << 16);
-          pf[1] = (uint32_t)f2bf(p[qt][0][2]) | ((uint32_t)f2bf(p[qt][0][3]) << 16);
-          pf[2] = (uint32_t)f2bf(p[qt][1][0]) | ((uint32_t)f2bf(p[qt][1][1]) << 16);
-          pf[3] = (uint32_t)f2bf(p[qt][1][2]) | ((uint32_t)f2bf(p[qt][1][3]) << 16);
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf),
-                                                              __builtin_bit_cast(bf16x8, pf), o[qt][dt], 0, 0, 0);
+      for (int qt = 0; qt < QTW; ++qt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          pf[qt][c][0] = pack_bf16(sacc[2 * c][qt][0], sacc[2 * c][qt][1]);
+          pf[qt][c][1] = pack_bf16(sacc[2 * c][qt][2], sacc[2 * c][qt][3]);
+          pf[qt][c][2] = pack_bf16(sacc[2 * c + 1][qt][0], sacc[2 * c + 1][qt][1]);
+          pf[qt][c][3] = pack_bf16(sacc[2 * c + 1][qt][2], sacc[2 * c + 1][qt][3]);
         }
-      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(buf + (NFK + dt * 2 + c) * 1024);
+#pragma unroll
+          for (int qt = 0; qt < QTW; ++qt)
+            o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf),
+                                                                __builtin_bit_cast(bf16x8, pf[qt][c]), o[qt][dt], 0, 0, 0);
+        }
     }
   }
+  wait_vmcnt<0>();   // no copy into LDS may be in flight when the workgroup exits
 
-  // partial results: O^T lane holds d = dt*16 + 4*(lane/16) + q of query lane%16
+  // O^T lane holds d = dt*16 + 4*(lane/16) + q of query lane%16
   const int64_t rows_total = (int64_t)a.n_req * nrows;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int tok = qtok[qt];
+  for (int qt = 0; qt < QTW; ++qt) {
+    const int tok = tok0 + qt * 16 + (lane & 15);
     if (tok >= nrows) continue;
     const int64_t row = (int64_t)r * nrows + tok;
+    if (a.n_split == 1) {
+      const float inv = 1.0f / l[qt];
+      const int64_t ob = row * ld + (int64_t)h * DH + (lane >> 4) * 4;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const float v0 = o[qt][dt][0] * inv, v1 = o[qt][dt][1] * inv, v2 = o[qt][dt][2] * inv, v3 = o[qt][dt][3] * inv;
+        if constexpr (AT == DT_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.O) + ob + dt * 16) = make_float4(v0, v1, v2, v3);
+        } else {
+          uint2 pk;
+          pk.x = pack_bf16(v0, v1);
+          pk.y = pack_bf16(v2, v3);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.O) + ob + dt * 16) = pk;
+        }
+      }
+      continue;
+    }
     const int64_t base = (((int64_t)s * rows_total + row) * a.Hq + h);
     float* po = a.part_o + base * DH;
 #pragma unroll
@@ -200,26 +315,43 @@ __global__ __launch_bounds__(256) void k_attn(const AttnArgs a) {
   }
 }
 
-// combine key splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// combine key splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One thread per (row, head, 4 dims); every split's partial is loaded before
+// any is used, so the loads overlap instead of queueing one split at a time.
 template <int AT>
-__global__ void k_attn_merge(const AttnArgs a, int dh) {
-  const int64_t row = blockIdx.x;
+__global__ __launch_bounds__(256) void k_attn_merge(const AttnArgs a, int dh) {
+  constexpr int MS = ATT_MAX_SPLIT;
   const int64_t rows_total = (int64_t)a.n_req * a.rows_per_req;
-  const int idx = threadIdx.x * 4;
-  if (idx >= a.Hq * dh) return;
+  const int quads = a.Hq * dh / 4;
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= rows_total * quads) return;
+  const int64_t row = t / quads;
+  const int idx = (int)(t % quads) * 4;
   const int h = idx / dh, d = idx % dh;
+  float ms[MS], ls[MS];
+  float4 os[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    if (s < a.n_split) {
+      const int64_t base = ((int64_t)s * rows_total + row) * a.Hq + h;
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + base * 2);
+      ms[s] = ml.x; ls[s] = ml.y;
+      os[s] = *reinterpret_cast<const float4*>(a.part_o + base * dh + d);
+    } else {
+      ms[s] = -INFINITY; ls[s] = 0.f; os[s] = make_float4(0, 0, 0, 0);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.part_ml[(((int64_t)s * rows_total + row) * a.Hq + h) * 2]);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) M = fmaxf(M, ms[s]);
   float L = 0.f;
   float4 acc = make_float4(0, 0, 0, 0);
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t base = ((int64_t)s * rows_total + row) * a.Hq + h;
-    const float ms = a.part_ml[base * 2];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - M);
-    L += w * a.part_ml[base * 2 + 1];
-    float4 v = *reinterpret_cast<const float4*>(a.part_o + base * dh + d);
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    if (ms[s] == -INFINITY) continue;
+    const float w = exp2f(ms[s] - M);
+    L += w * ls[s];
+    acc.x += w * os[s].x; acc.y += w * os[s].y; acc.z += w * os[s].z; acc.w += w * os[s].w;
   }
   const float inv = 1.0f / L;
   const int64_t o = row * (int64_t)a.Hq * dh + idx;
@@ -228,8 +360,8 @@ __global__ void k_attn_merge(const AttnArgs a, int dh) {
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   } else {
     uint2 p;
-    p.x = (uint32_t)f2bf(acc.x * inv) | ((uint32_t)f2bf(acc.y * inv) << 16);
-    p.y = (uint32_t)f2bf(acc.z * inv) | ((uint32_t)f2bf(acc.w * inv) << 16);
+    p.x = pack_bf16(acc.x * inv, acc.y * inv);
+    p.y = pack_bf16(acc.z * inv, acc.w * inv);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.O) + o) = p;
   }
 }
@@ -237,19 +369,20 @@ __global__ void k_attn_merge(const AttnArgs a, int dh) {
 void launch_attention(int adt, const AttnArgs& a, hipStream_t s) {
   const int blocks = a.n_req * a.Hkv * a.q_blocks * a.n_split;
   if (adt == DT_F32) {
-    if (a.dh == 64) hipLaunchKernelGGL((k_attn<DT_F32, 64>), dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn<DT_F32, 128>), dim3(blocks), dim3(256), 0, s, a);
+    if (a.dh == 64) hipLaunchKernelGGL((k_attn<DT_F32, 64>), dim3(blocks), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<DT_F32, 128>), dim3(blocks), dim3(512), 0, s, a);
   } else {
-    if (a.dh == 64) hipLaunchKernelGGL((k_attn<DT_BF16, 64>), dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn<DT_BF16, 128>), dim3(blocks), dim3(256), 0, s, a);
+    if (a.dh == 64) hipLaunchKernelGGL((k_attn<DT_BF16, 64>), dim3(blocks), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_attn<DT_BF16, 128>), dim3(blocks), dim3(512), 0, s, a);
   }
 }
 
 void launch_attn_merge(int adt, const AttnArgs& a, hipStream_t s) {
-  const int rows = a.n_req * a.rows_per_req;
-  const int threads = (a.Hq * a.dh / 4 + 63) / 64 * 64;
-  if (adt == DT_F32) hipLaunchKernelGGL(k_attn_merge<DT_F32>, dim3(rows), dim3(threads), 0, s, a, a.dh);
-  else hipLaunchKernelGGL(k_attn_merge<DT_BF16>, dim3(rows), dim3(threads), 0, s, a, a.dh);
+  if (a.n_split <= 1) return;   // the attention kernel wrote O itself
+  const int64_t threads = (int64_t)a.n_req * a.rows_per_req * (a.Hq * a.dh / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (adt == DT_F32) hipLaunchKernelGGL(k_attn_merge<DT_F32>, grid, dim3(256), 0, s, a, a.dh);
+  else hipLaunchKernelGGL(k_attn_merge<DT_BF16>, grid, dim3(256), 0, s, a, a.dh);
 }
 
 }  // namespace cd

@@ -43,13 +43,31 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
   // order: their real tiles come first and must spread over all XCDs.
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
-  int logical = a.chunk_major ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
   const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
-  const int ks = logical % ksplit;
-  logical /= ksplit;
-  int tile, chunk;
-  if (a.chunk_major) { chunk = logical / a.max_tiles; tile = logical - chunk * a.max_tiles; }
-  else { tile = logical / a.n_chunks; chunk = logical - tile * a.n_chunks; }
+  int ks, tile, chunk;
+  if (a.tiles) {
+    // Grouped: the grid is sized for the most tiles routing can produce; the
+    // real work (n_tiles x chunks) is dealt evenly to the 8 XCDs, and inside
+    // an XCD the row tiles of one weight chunk run back to back, so a hot
+    // expert's second and later row tiles re-read its weights from that
+    // XCD's L2 instead of from HBM.
+    const int nt = *a.n_tiles;
+    const int work = nt * a.n_chunks * ksplit;
+    const int w8 = (work + 7) & ~7;
+    if (bid >= w8) return;
+    int logical = (bid & 7) * (w8 >> 3) + (bid >> 3);
+    if (logical >= work) return;
+    ks = logical % ksplit;
+    logical /= ksplit;
+    chunk = logical / nt;
+    tile = logical - chunk * nt;
+  } else {
+    int logical = a.chunk_major ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
+    ks = logical % ksplit;
+    logical /= ksplit;
+    if (a.chunk_major) { chunk = logical / a.max_tiles; tile = logical - chunk * a.max_tiles; }
+    else { tile = logical / a.n_chunks; chunk = logical - tile * a.n_chunks; }
+  }
   if (tile >= a.max_tiles || chunk >= a.n_chunks) return;
 
   int group, row0, rows;

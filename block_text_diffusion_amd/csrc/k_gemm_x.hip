@@ -27,15 +27,6 @@ namespace cd {
 
 constexpr int XMT = 16;   // 16-row tiles: 256 rows
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <int WT, int AT, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_x(const GemmArgs a) {
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);

@@ -43,8 +43,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int d, float ep
           make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
     } else {
       uint2 p;
-      p.x = (uint32_t)f2bf(v.x * inv) | ((uint32_t)f2bf(v.y * inv) << 16);
-      p.y = (uint32_t)f2bf(v.z * inv) | ((uint32_t)f2bf(v.w * inv) << 16);
+      p.x = pack_bf16(v.x * inv, v.y * inv);
+      p.y = pack_bf16(v.z * inv, v.w * inv);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(u) + (int64_t)t * d + c) = p;
     }
   }

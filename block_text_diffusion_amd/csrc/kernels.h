@@ -85,6 +85,9 @@ void launch_pack(const PackDesc& d, const float* src0, const float* src1, const 
 void launch_unpack(const PackDesc& d, float* out0, float* out1, float* out2, hipStream_t s);
 
 // ---- attention ---------------------------------------------------------------
+// attention work item: 256 query rows (heads of a KV group x tokens), keys in
+// blocks of 64, at most 16 key splits
+constexpr int ATT_QR = 256, ATT_KB = 64, ATT_MAX_SPLIT = 16;
 struct AttnArgs {
   const void* Q;          // [rows][Hq*dh] act
   void* O;                // [rows][Hq*dh] act
@@ -99,7 +102,7 @@ struct AttnArgs {
   int n_split, split_len; // key range split
   float* part_o;          // [n_split][rows_total][Hq][dh] f32
   float* part_ml;         // [n_split][rows_total][Hq][2] f32
-  int q_blocks;           // query blocks of 64 tokens per request
+  int q_blocks;           // query blocks of ATT_QR/(Hq/Hkv) tokens per request
 };
 void launch_attention(int adt, const AttnArgs& a, hipStream_t s);
 
