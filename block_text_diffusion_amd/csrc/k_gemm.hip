@@ -8,16 +8,20 @@
 //    registers (no LDS round trip for the streamed operand);
 //  * a workgroup is 4 waves; each wave owns two 16-column weight tiles and
 //    MT 16-row activation tiles, so every weight byte is read by exactly one
-//    wave per row block; activation fragments (small, L2 resident) are loaded
-//    per lane from row-major X, optionally through a row map (MoE gather);
-//  * the k loop is software pipelined in stages of 4 tiles with two register
-//    sets, keeping 8 KB of weight loads in flight per wave;
+//    wave per row block;
+//  * the activation fragments of a stage (rows of row-major X, optionally
+//    through a row map for the MoE gather) are copied once per workgroup
+//    straight into LDS (global_load_lds) and read there by all 4 waves,
+//    instead of each wave fetching the same fragments from L2;
+//  * the k loop is software pipelined in stages of 4 k-tiles, issued two
+//    stages ahead (two weight register sets, three LDS buffers), keeping
+//    8-16 KB of weight loads in flight per wave;
 //  * the product is computed transposed (A = weight tile, B = activation
 //    tile), so each lane ends with 4 consecutive output columns of one row
 //    and the epilogues store 8-16 contiguous bytes per lane;
 //  * dense launches remap block ids so that the row blocks of one weight
-//    slice run on the same XCD and share its L2; grouped launches keep the
-//    dispatcher's round-robin so the real tiles spread over all 8 XCDs.
+//    slice run on the same XCD and share its L2; grouped launches deal their
+//    real tiles evenly to the 8 XCDs.
 // Epilogues: fp32 store (router / LM head logits), row store (expert
 // outputs), fp32 residual add, SwiGLU of interleaved gate/up tiles, and
 // QKV with rotary embedding scattering K/V into the cache.
@@ -34,13 +38,19 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
   constexpr int XW = (WT == DT_FP8) ? 2 : 1;        // 16-byte activation loads per k-tile
   constexpr int XSTEP = (WT == DT_FP8) ? 128 : 64;  // activation bytes per k-tile
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
+  constexpr int NFR = MT * U * XW;        // 1 KB activation fragments per stage
+  constexpr int FPW = NFR / 4;            // fragments each wave copies
+  constexpr int STG = NFR * 1024;
+  constexpr int XBUF = 3;
+  constexpr int LPS = FPW + 2 * U;        // vector loads per wave per stage
+  static_assert(NFR % 4 == 0, "stage fragments");
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[XBUF * STG];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // Dense launches (chunk-major) remap block ids so the row blocks that share
   // a weight slice run on one XCD (the dispatcher deals workgroups to the 8
-  // XCDs round-robin) and share its L2.  Grouped launches keep the natural
-  // order: their real tiles come first and must spread over all XCDs.
+  // XCDs round-robin) and share its L2.
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
   const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
@@ -82,98 +92,99 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     rows = min(MROWS, a.M - row0);
     if (rows <= 0) return;
   }
+  // a wave past the last weight tile still copies its share of the
+  // activations and meets every barrier; it computes on a valid tile and
+  // stores nothing
   const int nt0 = chunk * 8 + wave * 2;
-  if (nt0 >= a.Nt) return;
+  const bool active = nt0 < a.Nt;
+  const int ntc = active ? nt0 : 0;
 
   const int KTall = a.K / KF;
   const int kt_beg = (int)((int64_t)KTall * ks / ksplit);
   const int KT = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt_beg;   // k-tiles of this split
-  const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)nt0 * KTall + kt_beg) * 1024 + lane * 16;
+  const int nst = (KT + U - 1) / U;                                      // stages of U k-tiles
+  const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)ntc * KTall + kt_beg) * 1024 + lane * 16;
   const uint8_t* wp1 = wp0 + (int64_t)KTall * 1024;
   const int esa = (AT == DT_F32) ? 4 : 2;
-  const uint8_t* xp[MT];
+  // this wave's share of the activation fragments of a stage: fragment
+  // f = (mt*U + u)*XW + h holds rows mt*16.. at k-tile u (half h for fp8)
+  const uint8_t* xsrc[FPW];
+  int xu[FPW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int r = mt * 16 + (lane & 15);
+  for (int i = 0; i < FPW; ++i) {
+    const int f = wave * FPW + i;
+    const int h = f % XW, u = (f / XW) % U, mt = f / (XW * U);
+    const int r = mt * 16 + (lane & 15);
     int src = 0;
     if (r < rows) src = a.row_map ? a.row_map[row0 + r] : row0 + r;
     if (src < 0) src = 0;
-    xp[mt] = reinterpret_cast<const uint8_t*>(a.X) + ((int64_t)src * a.ldx) * esa + (lane >> 4) * 16 * XW +
-             (int64_t)kt_beg * XSTEP;
+    xsrc[i] = reinterpret_cast<const uint8_t*>(a.X) + ((int64_t)src * a.ldx) * esa + (lane >> 4) * 16 * XW + h * 16 +
+              (int64_t)kt_beg * XSTEP;
+    xu[i] = u;
   }
 
   f32x4 acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) { acc[mt][0] = f32x4{0, 0, 0, 0}; acc[mt][1] = f32x4{0, 0, 0, 0}; }
 
-  u32x4 wA[2][U], wB[2][U];
-  u32x4 xA[MT][U][XW], xB[MT][U][XW];
+  u32x4 wA[2][U], wB[2][U];   // two register stages of the two weight tiles
 
-  auto load = [&](u32x4 (&w)[2][U], u32x4 (&x)[MT][U][XW], int kt) {
+  // loads of stage st (k-tiles st*U ..), clamped to the last k-tile: weights
+  // into register set ww, activations straight into LDS buffer st%XBUF
+  auto issue = [&](u32x4 (&ww)[2][U], int st) {
+    const int kt = st * U;
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+      const int kk = min(kt + xu[i], KT - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xsrc[i] + (int64_t)kk * XSTEP),
+                                       (lds_void*)(xs + (st % XBUF) * STG + (wave * FPW + i) * 1024), 16, 0, 0);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      w[0][u] = *reinterpret_cast<const u32x4*>(wp0 + (int64_t)(kt + u) * 1024);
-      w[1][u] = *reinterpret_cast<const u32x4*>(wp1 + (int64_t)(kt + u) * 1024);
+      const int kk = min(kt + u, KT - 1);
+      ww[0][u] = *reinterpret_cast<const u32x4*>(wp0 + (int64_t)kk * 1024);
+      ww[1][u] = *reinterpret_cast<const u32x4*>(wp1 + (int64_t)kk * 1024);
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int h = 0; h < XW; ++h)
-          x[mt][u][h] = *reinterpret_cast<const u32x4*>(xp[mt] + (int64_t)(kt + u) * XSTEP + h * 16);
   };
-  auto compute = [&](const u32x4 (&w)[2][U], const u32x4 (&x)[MT][U][XW]) {
+  auto compute = [&](const u32x4 (&ww)[2][U], int st) {
+    const uint8_t* buf = xs + (st % XBUF) * STG + lane * 16;
+    const int nu = min(U, KT - st * U);   // k-tiles of a short last stage
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (u < nu) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][0] = mma_tile<WT>(w[0][u], x[mt][u], acc[mt][0]);
-        acc[mt][1] = mma_tile<WT>(w[1][u], x[mt][u], acc[mt][1]);
+        for (int mt = 0; mt < MT; ++mt) {
+          u32x4 x[XW];
+#pragma unroll
+          for (int h = 0; h < XW; ++h) x[h] = *reinterpret_cast<const u32x4*>(buf + ((mt * U + u) * XW + h) * 1024);
+          acc[mt][0] = mma_tile<WT>(ww[0][u], x, acc[mt][0]);
+          acc[mt][1] = mma_tile<WT>(ww[1][u], x, acc[mt][1]);
+        }
       }
+    }
   };
-
-  // Two register stages; inside the loop every load is unconditional so the
-  // compiler's wait counts keep the next stage's loads in flight while the
-  // current stage's MFMAs run.
-  // sched_barrier keeps the scheduler from sinking the prefetch loads next to
-  // their uses, which would serialise the stages again.
-  const int nfull = KT / U;
-  if (nfull > 0) {
-    load(wA, xA, 0);
-    int b = 0;
-    for (; b + 2 < nfull; b += 2) {
-      load(wB, xB, (b + 1) * U);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wA, xA);
-      __builtin_amdgcn_sched_barrier(0);
-      load(wA, xA, (b + 2) * U);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wB, xB);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (b + 1 < nfull) {
-      load(wB, xB, (b + 1) * U);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wA, xA);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wB, xB);
-    } else {
-      compute(wA, xA);
-    }
+  // Stage st's loads are issued two stages ahead.  At the top of stage st the
+  // wave waits until only stage st+1's loads are outstanding (loads complete
+  // in order), then the barrier makes every wave's activation copies of stage
+  // st visible; the copy into the buffer of stage st+2 is issued only after
+  // that barrier, when every wave is done with stage st-1, its last reader.
+  auto step = [&](u32x4 (&ww)[2][U], int st) {
+    if (st + 1 < nst) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ww, st);
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 2 < nst) issue(ww, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (nst > 0) issue(wA, 0);
+  if (nst > 1) issue(wB, 1);
+  for (int st = 0; st < nst; st += 2) {
+    step(wA, st);
+    if (st + 1 < nst) step(wB, st + 1);
   }
-  for (int kt = nfull * U; kt < KT; ++kt) {
-    u32x4 w0 = *reinterpret_cast<const u32x4*>(wp0 + (int64_t)kt * 1024);
-    u32x4 w1 = *reinterpret_cast<const u32x4*>(wp1 + (int64_t)kt * 1024);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      u32x4 xx[XW];
-#pragma unroll
-      for (int h = 0; h < XW; ++h) xx[h] = *reinterpret_cast<const u32x4*>(xp[mt] + (int64_t)kt * XSTEP + h * 16);
-      acc[mt][0] = mma_tile<WT>(w0, xx, acc[mt][0]);
-      acc[mt][1] = mma_tile<WT>(w1, xx, acc[mt][1]);
-    }
-  }
+  if (!active) return;
 
   // ---- epilogue: lane holds Y[row][n..n+3] of tile (mt, nw) ----
   const int nq = (lane >> 4) * 4;
