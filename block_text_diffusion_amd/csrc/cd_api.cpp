@@ -42,7 +42,6 @@ constexpr int64_t ALIGN = 256;
 constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows
 constexpr int MAX_SPLIT = ATT_MAX_SPLIT;   // attention key splits
 constexpr int MAX_RSPLIT = 16;         // router contraction splits
-constexpr int MAX_XSPLIT = 16;         // dense contraction splits (M <= 256)
 
 struct Carve {
   int64_t off = 0;
@@ -71,8 +70,8 @@ struct Plan {
   // state
   int64_t rq, canvas, argmax, lock, entropy, pmax, info, h, u, q, o, part_o, part_ml, rlog, topk_id,
       topk_gate, blk_cnt, seg_off, row_map, slot, tiles, n_tiles, aperm, yperm, sact, logits, spart, rope,
-      kcache, vcache, zero, xpart;
-  int64_t max_rows, max_tiles, n_blk_max, n_chunks, xpart_elems;
+      kcache, vcache, zero;
+  int64_t max_rows, max_tiles, n_blk_max, n_chunks;
   int64_t kv_req_stride, kv_layer_stride;   // elements
   int64_t state_bytes;
 };
@@ -185,13 +184,6 @@ Plan make_plan(const cd_config& c) {
   p.yperm = s.take((int64_t)ae * p.max_rows * d);
   p.sact = s.take((int64_t)ae * T * std::max(c.shared_hidden, 1));
   p.logits = s.take(4LL * R * C * c.vocab);
-  {
-    // fp32 split partials of the per-layer dense GEMMs; wider layers (the LM
-    // head) use fewer splits so that ks * M * Npad always fits
-    const int64_t np = std::max(std::max(p.qkv_npad, p.wo_npad), std::max(p.sgu_npad, p.sdn_npad));
-    p.xpart_elems = (int64_t)MAX_XSPLIT * 256 * np;
-    p.xpart = s.take(4LL * p.xpart_elems);
-  }
   p.spart = s.take(16LL * R * C * p.n_chunks);
   p.rope = s.take(8LL * p.ctx * (dh / 2));
   p.kcache = s.take((int64_t)ae * p.kv_req_stride * R);
@@ -292,36 +284,19 @@ int router_split(const cd_config& g, int T) {
   return sp;
 }
 
-constexpr bool USE_LDS_DENSE = true;
-
-// Dense GEMM.  Up to 256 rows: one workgroup per 128 output columns holds
-// all rows, activations staged in LDS; a narrow layer splits its contraction
-// over workgroups into fp32 partials that a second kernel sums and finishes.
-// Larger row counts (prefill, many requests) take the row-tiled kernel.
+// Dense GEMM.  The LM head (thousands of 128-column chunks) at up to 256
+// rows takes the LDS-staged kernel: one workgroup per chunk holds all rows,
+// so the activations are read once per chunk.  Every other layer takes the
+// row-tiled kernel: at the canvas batch, 32-row tiles give each weight chunk
+// 8 workgroups on one XCD (one HBM read, the rest from its L2) and fill the
+// chip without splitting the contraction.
 void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
-  if (USE_LDS_DENSE && M <= 256 && a.ksplit <= 1) {
+  if (M <= 256 && a.n_chunks >= 512 && a.ksplit <= 1) {
     a.M = M;
-    const int kt = a.K / kfrag(wdt);
-    const int npad = a.Nt * 16;
-    int ks = 1;
-    while (ks < MAX_XSPLIT && a.n_chunks * ks * 2 <= 256 && kt / (ks * 2) >= 4) ks *= 2;
-    // the fp32 partials of every split must fit the partial buffer
-    while (ks > 1 && (int64_t)ks * M * npad > c->p.xpart_elems) ks /= 2;
-    if (ks == 1) {
-      launch_gemm_x(wdt, c->p.adt, epi, a, s);
-      return;
-    }
-    GemmArgs pa = a;
-    pa.ksplit = ks;
-    pa.Y = c->st<float>(c->p.xpart);
-    pa.ldy = npad;
-    pa.N = npad;
-    pa.y_kstride = (int64_t)M * npad;
-    launch_gemm_x(wdt, c->p.adt, EPI_F32, pa, s);
-    launch_splitk_epi(c->p.adt, epi, a, c->st<float>(c->p.xpart), ks, (int64_t)M * npad, npad, s);
+    launch_gemm_x(wdt, c->p.adt, epi, a, s);
     return;
   }
-  const int mt = M >= 64 ? 4 : (M > 16 ? 2 : 1);
+  const int mt = M > 256 ? 4 : (M > 16 ? 2 : 1);
   a.M = M;
   a.max_tiles = (M + 16 * mt - 1) / (16 * mt);
   a.chunk_major = 1;

@@ -16,9 +16,9 @@
 //  * activations and weights are both prefetched DIST stages ahead (4 LDS
 //    buffers of 16 KB, 3 register slots), so the one in-order vmcnt counter
 //    covers both streams with a single wait per stage;
-//  * a contraction split across workgroups supplies the parallelism that
-//    narrow layers (N of a few thousand) lack; its fp32 partials are summed
-//    in split order by k_splitk_epi, which then applies the epilogue.
+//  * used for the LM head, whose thousands of column chunks fill the chip
+//    (the kernel can also split the contraction into fp32 partials, EPI_F32
+//    with ksplit > 1).
 #include "common.h"
 #include "gemm_epi.h"
 #include "kernels.h"
@@ -158,38 +158,6 @@ __global__ __launch_bounds__(256) void k_gemm_x(const GemmArgs a) {
   }
 }
 
-// Sum of the contraction splits (in split order) and the epilogue.  One
-// thread per row and four output columns (hidden columns for SwiGLU).
-template <int AT, int EPI>
-__global__ __launch_bounds__(256) void k_splitk_epi(const GemmArgs a, const float* part, int ksplit, int64_t pstride,
-                                                    int ldp, int quads) {
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int row = (int)(idx / quads), qd = (int)(idx % quads);
-  if (row >= a.M) return;
-  const float* sc = nullptr;   // fp8 row scales were applied to the partials
-  if constexpr (EPI == EPI_SWIGLU) {
-    const int j = qd * 4;
-    const int ng = (j >> 4) * 32 + (j & 15);
-    float g[4] = {0, 0, 0, 0}, u[4] = {0, 0, 0, 0};
-    for (int s = 0; s < ksplit; ++s) {
-      const float* p = part + s * pstride + (int64_t)row * ldp;
-      const float4 gv = *reinterpret_cast<const float4*>(p + ng);
-      const float4 uv = *reinterpret_cast<const float4*>(p + ng + 16);
-      g[0] += gv.x; g[1] += gv.y; g[2] += gv.z; g[3] += gv.w;
-      u[0] += uv.x; u[1] += uv.y; u[2] += uv.z; u[3] += uv.w;
-    }
-    epi_swiglu<AT>(a, sc, row, ng, g, u);
-  } else {
-    const int n = qd * 4;
-    float v[4] = {0, 0, 0, 0};
-    for (int s = 0; s < ksplit; ++s) {
-      const float4 pv = *reinterpret_cast<const float4*>(part + s * pstride + (int64_t)row * ldp + n);
-      v[0] += pv.x; v[1] += pv.y; v[2] += pv.z; v[3] += pv.w;
-    }
-    epi_store<AT, EPI>(a, nullptr, row, n, v, 0);
-  }
-}
-
 template <int WT, int AT, int EPI>
 static void run_x(const GemmArgs& a, hipStream_t s) {
   const int blocks = a.n_chunks * (a.ksplit > 1 ? a.ksplit : 1);
@@ -211,26 +179,6 @@ void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s) 
   if (wdt == DT_F32) run_x_epi<DT_F32, DT_F32>(epi, a, s);
   else if (wdt == DT_BF16) run_x_epi<DT_BF16, DT_BF16>(epi, a, s);
   else run_x_epi<DT_FP8, DT_BF16>(epi, a, s);
-}
-
-template <int AT>
-static void run_sk(int epi, const GemmArgs& a, const float* part, int ksplit, int64_t pstride, int ldp, hipStream_t s) {
-  const int quads = (epi == EPI_SWIGLU) ? a.ldy / 4 : (a.Nt * 16) / 4;
-  const int64_t threads = (int64_t)a.M * quads;
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  switch (epi) {
-    case EPI_RESID: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_RESID>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_SWIGLU>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_QKV>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
-    case EPI_ROWS: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_ROWS>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
-    default: hipLaunchKernelGGL((k_splitk_epi<AT, EPI_F32>), grid, dim3(256), 0, s, a, part, ksplit, pstride, ldp, quads); break;
-  }
-}
-
-void launch_splitk_epi(int adt, int epi, const GemmArgs& a, const float* part, int ksplit, int64_t pstride, int ldp,
-                       hipStream_t s) {
-  if (adt == DT_F32) run_sk<DT_F32>(epi, a, part, ksplit, pstride, ldp, s);
-  else run_sk<DT_BF16>(epi, a, part, ksplit, pstride, ldp, s);
 }
 
 }  // namespace cd

@@ -62,9 +62,6 @@ struct GemmArgs {
 void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
 // dense, M <= 256, activations staged in LDS (a.ksplit > 1: EPI_F32 partials)
 void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s);
-void launch_splitk_epi(int adt, int epi, const GemmArgs& a, const float* part, int ksplit, int64_t pstride, int ldp,
-                       hipStream_t s);
-
 // ---- weight synthesis / packing --------------------------------------------
 struct PackDesc {
   uint8_t* dst;        // packed tiles (or row-major for embedding)
