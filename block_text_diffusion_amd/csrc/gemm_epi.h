@@ -34,6 +34,28 @@ __device__ __forceinline__ void store1(void* base, int64_t idx, float v) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
+// fp8 weight fragment (16 E4M3 bytes) -> two bf16 operand fragments.  E4M3
+// values are exact in bf16; the hardware conversion (scale 1) turns bytes
+// 2q, 2q+1 of each 8-byte half into one packed bf16 pair.
+__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true));
+}
+__device__ __forceinline__ void widen_fp8(const u32x4& w, u32x4 (&wb)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    wb[h][0] = fp8x2_lo(w[2 * h]);
+    wb[h][1] = fp8x2_hi(w[2 * h]);
+    wb[h][2] = fp8x2_lo(w[2 * h + 1]);
+    wb[h][3] = fp8x2_hi(w[2 * h + 1]);
+  }
+}
+__device__ __forceinline__ f32x4 mma_bf16(const u32x4& a, const u32x4& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
 // one k-tile of MFMA work: acc += W_tile(16 x KF) * X_tile(16 x KF)^T
 template <int WT>
 __device__ __forceinline__ f32x4 mma_tile(const u32x4& w, const u32x4* x, f32x4 acc) {
@@ -45,20 +67,10 @@ __device__ __forceinline__ f32x4 mma_tile(const u32x4& w, const u32x4* x, f32x4 
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                   __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
   } else {
-    // E4M3 has 4 significant bits, so its bf16 image is exact (top half of fp32)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 wb;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = w[2 * h + (q >> 1)];
-        uint32_t b0 = (word >> (16 * (q & 1))) & 0xFFu;
-        uint32_t b1 = (word >> (16 * (q & 1) + 8)) & 0xFFu;
-        wb[q] = (__float_as_uint(e4m3_to_f32(b0)) >> 16) | (__float_as_uint(e4m3_to_f32(b1)) & 0xFFFF0000u);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wb),
-                                                    __builtin_bit_cast(bf16x8, x[h]), acc, 0, 0, 0);
-    }
+    u32x4 wb[2];
+    widen_fp8(w, wb);
+    acc = mma_bf16(wb[0], x[0], acc);
+    acc = mma_bf16(wb[1], x[1], acc);
   }
   return acc;
 }

@@ -152,13 +152,28 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u < nu) {
+        if constexpr (WT == DT_FP8) {
+          // widen the two fp8 weight fragments once for all row tiles
+          u32x4 wb0[2], wb1[2];
+          widen_fp8(ww[0][u], wb0);
+          widen_fp8(ww[1][u], wb1);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          u32x4 x[XW];
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int h = 0; h < XW; ++h) x[h] = *reinterpret_cast<const u32x4*>(buf + ((mt * U + u) * XW + h) * 1024);
-          acc[mt][0] = mma_tile<WT>(ww[0][u], x, acc[mt][0]);
-          acc[mt][1] = mma_tile<WT>(ww[1][u], x, acc[mt][1]);
+            for (int h = 0; h < 2; ++h) {
+              const u32x4 x = *reinterpret_cast<const u32x4*>(buf + ((mt * U + u) * XW + h) * 1024);
+              acc[mt][0] = mma_bf16(wb0[h], x, acc[mt][0]);
+              acc[mt][1] = mma_bf16(wb1[h], x, acc[mt][1]);
+            }
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            u32x4 x[XW];
+#pragma unroll
+            for (int h = 0; h < XW; ++h) x[h] = *reinterpret_cast<const u32x4*>(buf + ((mt * U + u) * XW + h) * 1024);
+            acc[mt][0] = mma_tile<WT>(ww[0][u], x, acc[mt][0]);
+            acc[mt][1] = mma_tile<WT>(ww[1][u], x, acc[mt][1]);
+          }
         }
       }
     }
