@@ -217,6 +217,14 @@ struct cd_ctx {
   float* trace_h = nullptr;
   int32_t* trace_ids = nullptr;
   float* trace_gates = nullptr;
+  // a second stream (default priority) of the library's own: the shared FFN's
+  // gate/up projection runs there while the router, routing and expert GEMMs
+  // run on the caller's stream; the two join before the shared down
+  // projection, inside the same call.  Created on first use; if that fails
+  // the projection runs on the caller's stream.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  bool side_tried = false;
   template <class T> T* st(int64_t off) const { return reinterpret_cast<T*>(S + off); }
   template <class T> T* wt(int64_t off) const { return off < 0 ? nullptr : reinterpret_cast<T*>(W + off); }
 };
@@ -232,6 +240,20 @@ hipEvent_t pool_event(cd_ctx* c) {
     c->pool.push_back(e);
   }
   return c->pool[c->pool_used++];
+}
+
+bool ensure_side(cd_ctx* c) {
+  if (!c->side_tried) {
+    c->side_tried = true;
+    if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) c->side = nullptr;
+    if (c->side && (hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+                    hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess)) {
+      hipStreamDestroy(c->side);
+      c->side = nullptr;
+    }
+    (void)hipGetLastError();
+  }
+  return c->side != nullptr;
 }
 
 // Records events around one launch when profiling is on.
@@ -383,6 +405,21 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
     { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
+    // The shared FFN's gate/up projection depends only on u: it runs on the
+    // side stream while the router, the routing and the expert GEMMs (mostly
+    // latency-bound at the canvas batch) run here.
+    const bool fork = g.shared_hidden && ensure_side(c);
+    if (g.shared_hidden) {
+      hipStream_t ss = fork ? c->side : s;
+      if (fork) {
+        hipEventRecord(c->ev_fork, s);
+        hipStreamWaitEvent(c->side, c->ev_fork, 0);
+      }
+      GemmArgs a = gemm_base(u, d, c->W + lw.sgu, nullptr, d, p.sgu_npad, 2 * g.shared_hidden,
+                             c->st<void>(p.sact), g.shared_hidden);
+      { Prof pg(c, CD_PROF_SHARED_GU, ss); gemm_dense(c, p.wdt_other, EPI_SWIGLU, a, T, ss); }
+      if (fork) hipEventRecord(c->ev_join, c->side);
+    }
     // router logits as fp32 partial sums over a split contraction (the
     // top-k kernel adds them in split order): the router weight is small, so
     // splitting K is what gives the launch enough waves
@@ -422,15 +459,19 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       PROF(CD_PROF_EXPERT_DOWN);
       gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, s);
     }
-    { PROF(CD_PROF_COMBINE); launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate), T, k, d, h, s); }
-    if (g.shared_hidden) {
-      GemmArgs a = gemm_base(u, d, c->W + lw.sgu, nullptr, d, p.sgu_npad, 2 * g.shared_hidden,
-                             c->st<void>(p.sact), g.shared_hidden);
-      { PROF(CD_PROF_SHARED_GU); gemm_dense(c, p.wdt_other, EPI_SWIGLU, a, T, s); }
+    if (!g.shared_hidden) {
+      PROF(CD_PROF_COMBINE);
+      launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate), T, k, d, h, s);
+    } else {
+      if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
+      // the shared FFN's down projection also adds the routed experts'
+      // outputs (the combine step) into the residual
       GemmArgs b = gemm_base(c->st<void>(p.sact), g.shared_hidden, c->W + lw.sdn, nullptr, g.shared_hidden,
                              p.sdn_npad, d, h, d);
+      b.moe_y = c->st<void>(p.yperm); b.moe_slot = c->st<int32_t>(p.slot); b.moe_gate = c->st<float>(p.topk_gate);
+      b.moe_k = k; b.moe_ld = d;
       PROF(CD_PROF_SHARED_DOWN);
-      gemm_dense(c, p.wdt_other, EPI_RESID, b, T, s);
+      gemm_dense(c, p.wdt_other, EPI_RESID_MOE, b, T, s);
     }
   }
   if (head) {
@@ -581,8 +622,15 @@ int32_t cd_ctx_create(const cd_config* cfg, void* d_weights, void* d_state, cd_c
 }
 
 int32_t cd_ctx_destroy(cd_ctx* ctx) {
-  if (ctx)
+  if (ctx) {
+    if (ctx->side) {
+      hipStreamSynchronize(ctx->side);
+      hipStreamDestroy(ctx->side);
+    }
+    if (ctx->ev_fork) hipEventDestroy(ctx->ev_fork);
+    if (ctx->ev_join) hipEventDestroy(ctx->ev_join);
     for (hipEvent_t e : ctx->pool) hipEventDestroy(e);
+  }
   delete ctx;
   return CD_OK;
 }

@@ -94,6 +94,26 @@ __device__ __forceinline__ void epi_store(const GemmArgs& a, const float* sc, in
     float4 o = *p;
     o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
     *p = o;
+  } else if constexpr (EPI == EPI_RESID_MOE) {
+    // residual + routed experts (in slot order) + this GEMM (the shared FFN)
+    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + (int64_t)row * a.ldy + n);
+    float4 o = *p;
+    const int64_t tk = (int64_t)row * a.moe_k;
+    for (int j = 0; j < a.moe_k; ++j) {
+      const float g = a.moe_gate[tk + j];
+      const int64_t yr = a.moe_slot[tk + j];
+      float y0, y1, y2, y3;
+      if constexpr (AT == DT_F32) {
+        const float4 y = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.moe_y) + yr * a.moe_ld + n);
+        y0 = y.x; y1 = y.y; y2 = y.z; y3 = y.w;
+      } else {
+        const uint2 y = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.moe_y) + yr * a.moe_ld + n);
+        y0 = bf2f(y.x & 0xFFFF); y1 = bf2f(y.x >> 16); y2 = bf2f(y.y & 0xFFFF); y3 = bf2f(y.y >> 16);
+      }
+      o.x += g * y0; o.y += g * y1; o.z += g * y2; o.w += g * y3;
+    }
+    o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
+    *p = o;
   } else if constexpr (EPI == EPI_QKV) {
     const int dh = a.dh, half = dh >> 1;
     const int req = row / a.rows_per_req;

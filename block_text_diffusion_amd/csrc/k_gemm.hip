@@ -236,6 +236,7 @@ static void run_epi(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_RESID: run<WT, AT, MT, EPI_RESID>(a, s); break;
     case EPI_SWIGLU: run<WT, AT, MT, EPI_SWIGLU>(a, s); break;
     case EPI_QKV: run<WT, AT, MT, EPI_QKV>(a, s); break;
+    case EPI_RESID_MOE: run<WT, AT, MT, EPI_RESID_MOE>(a, s); break;
   }
 }
 

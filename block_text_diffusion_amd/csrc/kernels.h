@@ -24,7 +24,7 @@ __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + 
 // Row permutations applied when packing.
 enum { PERM_NONE = 0, PERM_QKV = 1, PERM_GU = 2 };
 
-enum { EPI_F32 = 0, EPI_ROWS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
+enum { EPI_F32 = 0, EPI_ROWS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4, EPI_RESID_MOE = 5 };
 
 struct GemmArgs {
   // activations: row-major [rows][ldx], element type = act dtype
@@ -57,6 +57,13 @@ struct GemmArgs {
   const int32_t* pos0;     // per request: position of its row 0
   int pos0_stride;         // int32 stride between requests in pos0
   const float* rope_cs;    // [max_ctx][dh/2] (cos, sin) pairs, or null
+  // EPI_RESID_MOE: the routed experts' outputs are added with the residual,
+  // h[row] += sum_j gate[row][j] * moe_y[slot[row][j]] + this GEMM's row
+  const void* moe_y;       // [T*k][moe_ld] act
+  const int32_t* moe_slot; // [T][k]
+  const float* moe_gate;   // [T][k]
+  int moe_k;
+  int64_t moe_ld;
 };
 
 void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);

@@ -22,7 +22,12 @@
  *    cd_state_bytes report.  Pointers marked d_ are device pointers, h_ host.
  *  - Streams: every call enqueues on the caller's hipStream_t (passed as
  *    void*) and returns without waiting, except where stated (cd_commit_block,
- *    cd_generate and cd_read_step_info synchronise the stream).
+ *    cd_generate and cd_read_step_info synchronise the stream).  A forward
+ *    (prefill, denoise pass, commit) with a shared FFN also uses a second
+ *    stream that the context owns (default priority): it forks from the
+ *    caller's stream with an event and joins back into it within the same
+ *    call, so work enqueued later on the caller's stream sees every result.
+ *    A context is therefore used from one stream at a time.
  *  - Errors: every function returns CD_OK (0) or a negative code.  All
  *    arguments and the request state are checked before anything is
  *    enqueued, so a failing call changes nothing.  A kernel fault surfaces as
