@@ -41,7 +41,7 @@ int32_t hip_status(const char* where) {
 constexpr int64_t ALIGN = 256;
 constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows
 constexpr int MAX_SPLIT = ATT_MAX_SPLIT;   // attention key splits
-constexpr int MAX_RSPLIT = 16;         // router contraction splits
+constexpr int MAX_RSPLIT = MAX_ROUTER_SPLIT;         // router contraction splits
 
 struct Carve {
   int64_t off = 0;

@@ -24,14 +24,22 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
+  // logit = sum of the router's split partials, added in split order; all
+  // partials of a lane are loaded before the first add so the loads overlap
   float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     float x = -INFINITY;
     if (e < a.E) {
+      float part[MAX_ROUTER_SPLIT];
+#pragma unroll
+      for (int s = 0; s < MAX_ROUTER_SPLIT; ++s)
+        part[s] = s < a.nsplit ? a.logits[((int64_t)s * a.T + t) * a.E + e] : 0.f;
       x = 0.f;
-      for (int s = 0; s < a.nsplit; ++s) x += a.logits[((int64_t)s * a.T + t) * a.E + e];
+#pragma unroll
+      for (int s = 0; s < MAX_ROUTER_SPLIT; ++s)
+        if (s < a.nsplit) x += part[s];
       if (x != x) x = -INFINITY;
     }
     v[i] = x;

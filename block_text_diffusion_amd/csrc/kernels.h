@@ -111,6 +111,7 @@ struct AttnArgs {
 void launch_attention(int adt, const AttnArgs& a, hipStream_t s);
 
 // ---- MoE routing ----------------------------------------------------------------
+constexpr int MAX_ROUTER_SPLIT = 16;   // contraction splits of the router GEMM
 struct RouteArgs {
   const float* logits;   // [nsplit][T][E] router logit partials (summed in split order)
   int nsplit;
