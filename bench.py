@@ -48,6 +48,25 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def measured_copy_gbs(nbytes=1 << 30, reps=10):
+    """Read+write bandwidth of a plain 1 GiB device-to-device copy on this
+    GPU: the practical HBM ceiling the kernels are also compared against."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def gpu_part(w, steps, warmup, prof_steps, do_block=True):
     import torch
     from block_text_diffusion_amd import binding as B
@@ -91,9 +110,12 @@ def gpu_part(w, steps, warmup, prof_steps, do_block=True):
     for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
+    step_ms = []
     t0 = time.perf_counter()
     for _ in range(steps):
-        one_step()
+        ts = time.perf_counter()
+        one_step()                     # ends with the stop-flag read-back, so the pass is complete
+        step_ms.append((time.perf_counter() - ts) * 1e3)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     log(f"timed {steps} steps: {el / steps * 1e3:.3f} ms/step")
@@ -120,7 +142,8 @@ def gpu_part(w, steps, warmup, prof_steps, do_block=True):
              "mean_max_tokens_per_expert": float(counts.max(axis=1).mean()),
              "mean_row_tiles": float(np.mean([(np.ceil(c / 32)).sum() for c in counts]))}
     out = dict(elapsed=el, prof=prof, active=active, route=route, prefill_ms=prefill_ms, block_s=float("nan"),
-               block_passes=0, blocks=[], device=torch.cuda.get_device_name(dev))
+               block_passes=0, blocks=[], device=torch.cuda.get_device_name(dev), step_ms=step_ms,
+               copy_gbs=measured_copy_gbs())
     if not do_block:
         eng.close()
         return out
@@ -188,6 +211,26 @@ def expert_flops(w, part):
     return 2 * T * k * d * (2 * fe if part == "gate_up" else fe)
 
 
+def kernel_fractions(w, per, per_step):
+    """MFMA fractions of the compute-shaped kernels at this workload (bf16
+    dense peak; fp8 weights are widened to bf16 for the MFMA): canvas
+    attention and the LM head, from their event-timed durations."""
+    R, C, L = w["R"], w["C"], w["L"]
+    T = R * C
+    nk = w["P0"] + C
+    attn_fl = 4.0 * T * w["Hq"] * nk * w["dh"]                   # QK^T and PV per layer
+    lm_fl = 2.0 * T * w["d"] * w["V"]
+    out = {}
+    t_attn = (per_step.get("attention", 0) + per_step.get("attn_merge", 0)) / L
+    if t_attn > 0:
+        out["attention_tflops"] = round(attn_fl / (t_attn * 1e-3) / 1e12, 1)
+        out["attention_frac_bf16_peak"] = round(attn_fl / (t_attn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    if per.get("lm_head", 0) > 0:
+        out["lm_head_tflops"] = round(lm_fl / (per["lm_head"] * 1e-3) / 1e12, 1)
+        out["lm_head_frac_bf16_peak"] = round(lm_fl / (per["lm_head"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    return out
+
+
 def cpu_baseline(w):
     """The oracle, as it stands, on exact work units of the same step, each
     timed once and scaled by how often the step contains it."""
@@ -221,17 +264,19 @@ def cpu_baseline(w):
     ids, gates = model.topk_route(u2 @ W.get("wr", 0).T, w["k"])
     t_attn = time.perf_counter() - t0
 
-    rows = np.nonzero(ids == 0)[0]                 # one routed expert over its rows
+    n_exp = 16                                     # routed experts 0..15, each over its own rows
     t0 = time.perf_counter()
-    model.swiglu(u2[rows], W.get("wg", 0, 0), W.get("wu", 0, 0), W.get("wd", 0, 0))
-    t_expert = time.perf_counter() - t0
+    for e in range(n_exp):
+        rows = np.nonzero(ids == e)[0]
+        model.swiglu(u2[rows], W.get("wg", 0, e), W.get("wu", 0, e), W.get("wd", 0, e))
+    t_expert = (time.perf_counter() - t0) / n_exp
 
     t0 = time.perf_counter()
     if w["fs"]:
         model.swiglu(u2, W.get("sg", 0), W.get("su", 0), W.get("sd", 0))
     t_shared = time.perf_counter() - t0
 
-    n_slice = 1024                                 # a vocabulary slice of the LM head
+    n_slice = 4096                                 # a vocabulary slice of the LM head
     t0 = time.perf_counter()
     model.lm_head(w, W, h2, vocab_rows=np.arange(n_slice))
     t_lm = time.perf_counter() - t0
@@ -242,10 +287,10 @@ def cpu_baseline(w):
     t_samp = time.perf_counter() - t0
 
     step_s = w["L"] * (t_attn + w["E"] * t_expert + t_shared) + (w["V"] / n_slice) * t_lm + t_samp
-    sample_s = t_attn + t_expert + t_shared + t_lm + t_samp
+    sample_s = t_attn + n_exp * t_expert + t_shared + t_lm + t_samp
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(blas), "kind": "oracle",
             "sample": (f"fp64 numpy oracle incl. its weight generation; timed once each: layer-0 attention+router "
-                       f"({t_attn:.2f}s), one routed expert ({t_expert:.2f}s), shared FFN ({t_shared:.2f}s), "
+                       f"({t_attn:.2f}s), {n_exp} routed experts ({t_expert:.2f}s each), shared FFN ({t_shared:.2f}s), "
                        f"LM head on {n_slice} of {w['V']} vocab rows ({t_lm:.2f}s), sampler on 256x{w['V']} "
                        f"({t_samp:.2f}s); step = {w['L']}x(attn+{w['E']}xexpert+shared) + "
                        f"{w['V'] // n_slice}xLM slice + sampler = {step_s:.0f}s; {sample_s:.1f}s of CPU work; "
@@ -292,7 +337,9 @@ def main():
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(part) if args.workload == "step_bf16" else None,
-            "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5), "active_experts": g["active"]}
+            "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5), "active_experts": g["active"],
+            # the same bytes against the read+write rate of a plain 1 GiB copy on this GPU
+            "measured_copy_gbs": round(g["copy_gbs"], 1), "frac_of_measured_copy": round(achieved / g["copy_gbs"], 4)}
     if R * C * w["k"] / w["E"] >= 256:
         # many rows per expert: the grouped GEMM runs on the bf16 MFMA pipe
         tf = expert_flops(w, part) / (per[dom] * 1e-3) / 1e12
@@ -313,6 +360,9 @@ def main():
         "block_passes": g["block_passes"], "blocks": g["blocks"],
         "prefill_ms": round(g["prefill_ms"], 2),
         "roofline": roof,
+        "ms_per_step_median": round(float(np.median(g["step_ms"])), 4),
+        "ms_per_step_p95": round(float(np.percentile(g["step_ms"], 95)), 4),
+        "kernel_fractions": kernel_fractions(w, per, per_step),
         "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items() if v > 0},
         "routing": g["route"],
         "device": g["device"],
