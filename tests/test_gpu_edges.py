@@ -1,0 +1,126 @@
+"""Edge cases of the GPU path through the C ABI:
+
+* determinism and caller streams: the same prefill and passes on a
+  non-default stream (the shared-FFN side stream forks from and joins into
+  it) give bit-identical logits, canvases and K/V;
+* batch invariance: a request denoised inside a two-request batch equals the
+  same request alone (fp32, tolerance 1e-5: split counts depend on the batch);
+* capacity boundary: a prefill of exactly max_prefill ids and blocks that fill
+  the cache to exactly max_ctx run on the GPU and match the oracle; one more
+  canvas is refused with CD_ERR_CAPACITY and changes nothing."""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs
+from block_text_diffusion_amd import binding as B
+from block_text_diffusion_amd.engine import Engine
+from oracle import loop
+from oracle.weights import Weights
+from tests.gpu_util import TOL, announce, rel_l2_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def small(wdtype, **kw):
+    base = dict(wdtype=wdtype, dh=128, Hq=4, Hkv=2, E=16, k=4, fe=256, fs=128, V=4096, P0=100)
+    base.update(kw)
+    return synth_inputs.workload("tiny", **base)
+
+
+def _run(w, stream):
+    """Prefill two requests, start canvases and run two passes on `stream`;
+    return logits, canvases and the K/V cache."""
+    C = w["C"]
+    eng = Engine(w, max_requests=2, max_ctx=w["P0"] + C, max_prefill=w["P0"])
+    with torch.cuda.stream(stream):
+        B.cd_synth_weights(eng.ctx, w["weight_seed"])
+        for r, n in enumerate((w["P0"], 37)):
+            pre = synth_inputs.prefix_ids(w["V"], n, 7, r)
+            B.cd_prefill(eng.ctx, r, torch.from_numpy(pre).cuda())
+            B.cd_init_canvas(eng.ctx, r, 11, 0)
+        for _ in range(2):
+            B.cd_denoise_step(eng.ctx, 2, eng.info)
+            eng.step_info(2)
+        out = (eng.logits(2).clone(), eng.canvas().clone(), eng.kcache().clone(), eng.vcache().clone())
+    stream.synchronize()
+    eng.close()
+    return [t.cpu() for t in out]
+
+
+def test_user_stream_bit_identical_to_default_stream():
+    w = small("bf16", C=200)
+    announce("edges_stream_determinism")
+    a = _run(w, torch.cuda.current_stream())
+    b = _run(w, torch.cuda.Stream())
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_request_in_batch_equals_request_alone():
+    w = small("f32", C=128)
+    announce("edges_batch_invariance")
+    C = w["C"]
+    pres = [synth_inputs.prefix_ids(w["V"], n, 5, r) for r, n in enumerate((w["P0"], 60))]
+
+    def one_pass(n_req):
+        eng = Engine(w, max_requests=2, max_ctx=w["P0"] + C, max_prefill=w["P0"])
+        B.cd_synth_weights(eng.ctx, w["weight_seed"])
+        for r in range(n_req):
+            B.cd_prefill(eng.ctx, r, torch.from_numpy(pres[r]).cuda())
+            B.cd_init_canvas(eng.ctx, r, 3, 0)
+        B.cd_denoise_step(eng.ctx, n_req, eng.info)
+        info = eng.step_info(n_req)[0]
+        z = to_np(eng.logits(n_req))[:C]
+        x = eng.canvas()[0].cpu().numpy()
+        eng.close()
+        return z, x, info
+
+    z2, x2, i2 = one_pass(2)     # request 0 inside a two-request batch
+    z1, x1, i1 = one_pass(1)     # request 0 alone
+    assert rel_l2_rows(z2, z1).max() <= TOL["f32"]
+    assert np.array_equal(x2, x1)
+    assert i2.step == i1.step == 1 and i2.n_locked == i1.n_locked
+    assert abs(i2.mean_entropy - i1.mean_entropy) <= 1e-6 * i1.mean_entropy
+
+
+def test_capacity_boundary_prefill_and_blocks_fill_cache_exactly():
+    w = synth_inputs.workload("tiny", max_steps=2)
+    announce("edges_capacity_boundary")
+    C, P0 = w["C"], 64
+    max_ctx = P0 + 2 * C
+    eng = Engine(w, max_ctx=max_ctx, max_prefill=P0)
+    B.cd_synth_weights(eng.ctx, w["weight_seed"])
+    pre = synth_inputs.prefix_ids(w["V"], P0, 9, 0)
+    too_long = torch.zeros(P0 + 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.CDError):
+        B.cd_prefill(eng.ctx, 0, too_long)
+    assert B.cd_get_length(eng.ctx, 0) == 0
+    out = torch.empty(2 * C, dtype=torch.int32, device="cuda")
+    steps = B.cd_generate(eng.ctx, 0, torch.from_numpy(pre).cuda(), 2, 13, out)
+    assert steps == [2, 2]
+    assert B.cd_get_length(eng.ctx, 0) == max_ctx
+    with pytest.raises(B.CDError) as ei:
+        B.cd_init_canvas(eng.ctx, 0, 13, 2)
+    assert ei.value.code == B.CD_ERR_CAPACITY
+    assert B.cd_get_length(eng.ctx, 0) == max_ctx
+    # the last committed block's keys, at the last cache slots, against the oracle
+    got_ids = out.cpu().numpy().astype(np.int64)
+    K = to_np(eng.kcache()[0, :, :, :max_ctx, :])
+    eng.close()
+    W = Weights(w)
+    req = loop.Request(w)
+    loop.prefill(w, W, req, pre)
+    for b in range(2):
+        x = loop.init_canvas(w, 13, b, 0)
+        for t in (1, 2):
+            ref = loop.denoise_pass(w, W, req, x, t, b, 13)
+            x = ref["x_next"]
+        srt = np.sort(ref["z"], axis=1)
+        clear = srt[:, -1] - srt[:, -2] > 1e-4
+        assert np.array_equal(got_ids[b * C:(b + 1) * C][clear], ref["a"][clear])
+        loop.commit(w, W, req, got_ids[b * C:(b + 1) * C])
+    for l in range(w["L"]):
+        Ko = req.cache[l][0][:, P0 + C:max_ctx]
+        Kg = K[l][:, P0 + C:max_ctx]
+        assert rel_l2_rows(Kg.reshape(-1, w["dh"]), Ko.reshape(-1, w["dh"])).max() <= TOL["f32"], l
