@@ -26,32 +26,40 @@
 namespace cd {
 
 constexpr int XMT = 16;   // 16-row tiles: 256 rows
+constexpr int XWAVES = 8; // two waves per SIMD: one's waits overlap the other's MFMAs
+constexpr int XMTW = 8;   // row tiles per wave (waves 0-3: rows 0-127, waves 4-7: rows 128-255)
+constexpr int XNTW = 4;   // weight tiles per wave: a workgroup covers 256 columns, so the
+                          // activations are re-read from L2 once per 256 output columns
 
 template <int WT, int AT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_x(const GemmArgs a) {
+__global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
   constexpr int XW = (WT == DT_FP8) ? 2 : 1;          // 1 KB activation fragments per k-tile and row tile
   constexpr int XSTEP = (WT == DT_FP8) ? 128 : 64;    // activation bytes per k-tile (per lane group)
   constexpr int NBUF = (WT == DT_FP8) ? 2 : 4;
   constexpr int DIST = NBUF - 1;
   constexpr int BLK = XMT * XW;                       // fragments per stage
-  constexpr int BPW = BLK / 4;                        // fragments each wave copies
-  constexpr int LPS = BPW + 2;                        // vector loads per wave per stage
+  constexpr int BPW = BLK / XWAVES;                   // fragments each wave copies
+  constexpr int LPS = BPW + XNTW;                     // vector loads per wave per stage
   __shared__ __attribute__((aligned(1024))) uint8_t xs[NBUF][BLK * 1024];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;         // row half, column pair
   const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
   const int ks = blockIdx.x % ksplit, chunk = blockIdx.x / ksplit;
   const int KTall = a.K / KF;
   const int kt0 = (int)((int64_t)KTall * ks / ksplit);
   const int nst = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt0;
-  const int nt0 = chunk * 8 + wave * 2;
-  const bool active = nt0 < a.Nt;          // idle waves still copy activations and meet the barriers
-  const int ntc = active ? nt0 : 0;
+  // tiles past Nt load a valid tile and store nothing; idle waves still
+  // copy activations and meet the barriers
+  const int nt0 = chunk * 4 * XNTW + wn * XNTW;
   const int esa = (AT == DT_F32) ? 4 : 2;
 
-  const uint8_t* wp0 = a.W + ((int64_t)ntc * KTall + kt0) * 1024 + lane * 16;
-  const uint8_t* wp1 = wp0 + (int64_t)KTall * 1024;
+  const uint8_t* wp[XNTW];
+#pragma unroll
+  for (int j = 0; j < XNTW; ++j)
+    wp[j] = a.W + ((int64_t)min(nt0 + j, a.Nt - 1) * KTall + kt0) * 1024 + lane * 16;
   const uint8_t* xsrc[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
@@ -62,10 +70,12 @@ __global__ __launch_bounds__(256) void k_gemm_x(const GemmArgs a) {
               (int64_t)kt0 * XSTEP;
   }
 
-  f32x4 acc[XMT][2];
+  f32x4 acc[XMTW][XNTW];
 #pragma unroll
-  for (int mt = 0; mt < XMT; ++mt) { acc[mt][0] = f32x4{0, 0, 0, 0}; acc[mt][1] = f32x4{0, 0, 0, 0}; }
-  u32x4 w[DIST][2];
+  for (int mt = 0; mt < XMTW; ++mt)
+#pragma unroll
+    for (int j = 0; j < XNTW; ++j) acc[mt][j] = f32x4{0, 0, 0, 0};
+  u32x4 w[DIST][XNTW];
 
   // stage indices past the end are clamped to the last stage: the copies
   // stay in bounds and land in buffers no later stage reads
@@ -77,36 +87,37 @@ __global__ __launch_bounds__(256) void k_gemm_x(const GemmArgs a) {
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xsrc[i] + (int64_t)sc * XSTEP),
                                        (lds_void*)(dst + i * 1024), 16, 0, 0);
   };
-  auto issue_w = [&](u32x4 (&ww)[2], int s) {
+  auto issue_w = [&](u32x4 (&ww)[XNTW], int s) {
     const int sc = min(s, nst - 1);
-    ww[0] = *reinterpret_cast<const u32x4*>(wp0 + (int64_t)sc * 1024);
-    ww[1] = *reinterpret_cast<const u32x4*>(wp1 + (int64_t)sc * 1024);
+#pragma unroll
+    for (int j = 0; j < XNTW; ++j) ww[j] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)sc * 1024);
   };
   // all 16 row tiles are computed: rows past M hold copies of row M-1 (finite)
   // and their results are dropped, which keeps the loop free of branches
   // LDS fragment reads run one row tile ahead of the MFMAs that use them
-  auto compute = [&](const u32x4 (&ww)[2], const uint8_t* buf) {
+  auto compute = [&](const u32x4 (&ww)[XNTW], const uint8_t* buf) {
     u32x4 xa[XW], xb[XW];
     auto rd = [&](u32x4 (&x)[XW], int mt) {
 #pragma unroll
-      for (int h = 0; h < XW; ++h) x[h] = *reinterpret_cast<const u32x4*>(buf + ((mt * XW + h) * 64 + lane) * 16);
+      for (int h = 0; h < XW; ++h)
+        x[h] = *reinterpret_cast<const u32x4*>(buf + (((wm * XMTW + mt) * XW + h) * 64 + lane) * 16);
     };
     rd(xa, 0);
 #pragma unroll
-    for (int mt = 0; mt < XMT; mt += 2) {
+    for (int mt = 0; mt < XMTW; mt += 2) {
       rd(xb, mt + 1);
-      acc[mt][0] = mma_tile<WT>(ww[0], xa, acc[mt][0]);
-      acc[mt][1] = mma_tile<WT>(ww[1], xa, acc[mt][1]);
-      if (mt + 2 < XMT) rd(xa, mt + 2);
-      acc[mt + 1][0] = mma_tile<WT>(ww[0], xb, acc[mt + 1][0]);
-      acc[mt + 1][1] = mma_tile<WT>(ww[1], xb, acc[mt + 1][1]);
+#pragma unroll
+      for (int j = 0; j < XNTW; ++j) acc[mt][j] = mma_tile<WT>(ww[j], xa, acc[mt][j]);
+      if (mt + 2 < XMTW) rd(xa, mt + 2);
+#pragma unroll
+      for (int j = 0; j < XNTW; ++j) acc[mt + 1][j] = mma_tile<WT>(ww[j], xb, acc[mt + 1][j]);
     }
     // order: reads of tile 0, then (reads of tile mt+1, MFMAs of tile mt)
     constexpr int RD = XW;                                                     // DS reads per tile
-    constexpr int MF = 2 * (WT == DT_F32 ? 4 : (WT == DT_FP8 ? 2 : 1));        // MFMAs per tile
+    constexpr int MF = XNTW * (WT == DT_F32 ? 4 : (WT == DT_FP8 ? 2 : 1));     // MFMAs per tile
     __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
 #pragma unroll
-    for (int mt = 0; mt + 1 < XMT; ++mt) {
+    for (int mt = 0; mt + 1 < XMTW; ++mt) {
       __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
     }
@@ -138,30 +149,34 @@ __global__ __launch_bounds__(256) void k_gemm_x(const GemmArgs a) {
     }
   }
   wait_vmcnt<0>();   // no LDS copy may still be in flight when the workgroup exits
-  if (!active) return;
 
   const int nq = (lane >> 4) * 4;
   const float* sc = a.wscale;
 #pragma unroll
-  for (int mt = 0; mt < XMT; ++mt) {
-    const int row = mt * 16 + (lane & 15);
+  for (int mt = 0; mt < XMTW; ++mt) {
+    const int row = (wm * XMTW + mt) * 16 + (lane & 15);
     if (row >= a.M) continue;
-    float v0[4], v1[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) { v0[q] = acc[mt][0][q]; v1[q] = acc[mt][1][q]; }
-    if constexpr (EPI == EPI_SWIGLU) {
-      epi_swiglu<AT>(a, sc, row, nt0 * 16 + nq, v0, v1);
-    } else {
-      epi_store<AT, EPI>(a, sc, row, nt0 * 16 + nq, v0, ks);
-      epi_store<AT, EPI>(a, sc, row, (nt0 + 1) * 16 + nq, v1, ks);
+    for (int j = 0; j < XNTW; j += 2) {
+      if (nt0 + j >= a.Nt) break;     // Nt is even: tiles come in valid pairs
+      float v0[4], v1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v0[q] = acc[mt][j][q]; v1[q] = acc[mt][j + 1][q]; }
+      if constexpr (EPI == EPI_SWIGLU) {
+        epi_swiglu<AT>(a, sc, row, (nt0 + j) * 16 + nq, v0, v1);
+      } else {
+        epi_store<AT, EPI>(a, sc, row, (nt0 + j) * 16 + nq, v0, ks);
+        epi_store<AT, EPI>(a, sc, row, (nt0 + j + 1) * 16 + nq, v1, ks);
+      }
     }
   }
 }
 
 template <int WT, int AT, int EPI>
 static void run_x(const GemmArgs& a, hipStream_t s) {
-  const int blocks = a.n_chunks * (a.ksplit > 1 ? a.ksplit : 1);
-  hipLaunchKernelGGL((k_gemm_x<WT, AT, EPI>), dim3(blocks), dim3(256), 0, s, a);
+  const int chunks = (a.Nt + 4 * XNTW - 1) / (4 * XNTW);
+  const int blocks = chunks * (a.ksplit > 1 ? a.ksplit : 1);
+  hipLaunchKernelGGL((k_gemm_x<WT, AT, EPI>), dim3(blocks), dim3(64 * XWAVES), 0, s, a);
 }
 
 template <int WT, int AT>
