@@ -31,23 +31,31 @@
 
 namespace cd {
 
-template <int WT, int AT, int MT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
+// NW waves per workgroup, NTW = 8/NW weight tiles per wave: a workgroup
+// always covers 8 weight tiles (128 columns).  Four waves of two tiles suit
+// launches with several workgroups per CU and the SwiGLU epilogue (gate and
+// up tiles in one wave); eight waves of one tile put two waves on each SIMD
+// when a dense launch has only about one workgroup per CU.
+template <int WT, int AT, int MT, int EPI, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
+  constexpr int NTW = 8 / NW;
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(EPI != EPI_SWIGLU || NTW == 2, "SwiGLU needs gate and up tiles in one wave");
   constexpr int MROWS = 16 * MT;
   constexpr int U = 4;
   constexpr int XW = (WT == DT_FP8) ? 2 : 1;        // 16-byte activation loads per k-tile
   constexpr int XSTEP = (WT == DT_FP8) ? 128 : 64;  // activation bytes per k-tile
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
   constexpr int NFR = MT * U * XW;        // 1 KB activation fragments per stage
-  constexpr int FPW = NFR / 4;            // fragments each wave copies
+  constexpr int FPW = NFR / NW;           // fragments each wave copies
   constexpr int STG = NFR * 1024;
   constexpr int XBUF = 3;
-  constexpr int LPS = FPW + 2 * U;        // vector loads per wave per stage
-  static_assert(NFR % 4 == 0, "stage fragments");
+  constexpr int LPS = FPW + NTW * U;      // vector loads per wave per stage
+  static_assert(NFR % NW == 0, "stage fragments");
   __shared__ __attribute__((aligned(1024))) uint8_t xs[XBUF * STG];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Dense launches (chunk-major) remap block ids so the row blocks that share
   // a weight slice run on one XCD (the dispatcher deals workgroups to the 8
   // XCDs round-robin) and share its L2.
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
   // a wave past the last weight tile still copies its share of the
   // activations and meets every barrier; it computes on a valid tile and
   // stores nothing
-  const int nt0 = chunk * 8 + wave * 2;
+  const int nt0 = chunk * 8 + wave * NTW;
   const bool active = nt0 < a.Nt;
   const int ntc = active ? nt0 : 0;
 
@@ -104,7 +112,6 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
   const int KT = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt_beg;   // k-tiles of this split
   const int nst = (KT + U - 1) / U;                                      // stages of U k-tiles
   const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)ntc * KTall + kt_beg) * 1024 + lane * 16;
-  const uint8_t* wp1 = wp0 + (int64_t)KTall * 1024;
   const int esa = (AT == DT_F32) ? 4 : 2;
   // this wave's share of the activation fragments of a stage: fragment
   // f = (mt*U + u)*XW + h holds rows mt*16.. at k-tile u (half h for fp8)
@@ -123,15 +130,17 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     xu[i] = u;
   }
 
-  f32x4 acc[MT][2];
+  f32x4 acc[MT][NTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) { acc[mt][0] = f32x4{0, 0, 0, 0}; acc[mt][1] = f32x4{0, 0, 0, 0}; }
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[mt][j] = f32x4{0, 0, 0, 0};
 
-  u32x4 wA[2][U], wB[2][U];   // two register stages of the two weight tiles
+  u32x4 wA[NTW][U], wB[NTW][U];   // two register stages of the wave's weight tiles
 
   // loads of stage st (k-tiles st*U ..), clamped to the last k-tile: weights
   // into register set ww, activations straight into LDS buffer st%XBUF
-  auto issue = [&](u32x4 (&ww)[2][U], int st) {
+  auto issue = [&](u32x4 (&ww)[NTW][U], int st) {
     const int kt = st * U;
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
@@ -142,28 +151,29 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kk = min(kt + u, KT - 1);
-      ww[0][u] = *reinterpret_cast<const u32x4*>(wp0 + (int64_t)kk * 1024);
-      ww[1][u] = *reinterpret_cast<const u32x4*>(wp1 + (int64_t)kk * 1024);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        ww[j][u] = *reinterpret_cast<const u32x4*>(wp0 + ((int64_t)j * KTall + kk) * 1024);
     }
   };
-  auto compute = [&](const u32x4 (&ww)[2][U], int st) {
+  auto compute = [&](const u32x4 (&ww)[NTW][U], int st) {
     const uint8_t* buf = xs + (st % XBUF) * STG + lane * 16;
     const int nu = min(U, KT - st * U);   // k-tiles of a short last stage
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u < nu) {
         if constexpr (WT == DT_FP8) {
-          // widen the two fp8 weight fragments once for all row tiles
-          u32x4 wb0[2], wb1[2];
-          widen_fp8(ww[0][u], wb0);
-          widen_fp8(ww[1][u], wb1);
+          // widen the fp8 weight fragments once for all row tiles
+          u32x4 wb[NTW][2];
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) widen_fp8(ww[j][u], wb[j]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const u32x4 x = *reinterpret_cast<const u32x4*>(buf + ((mt * U + u) * XW + h) * 1024);
-              acc[mt][0] = mma_bf16(wb0[h], x, acc[mt][0]);
-              acc[mt][1] = mma_bf16(wb1[h], x, acc[mt][1]);
+#pragma unroll
+              for (int j = 0; j < NTW; ++j) acc[mt][j] = mma_bf16(wb[j][h], x, acc[mt][j]);
             }
         } else {
 #pragma unroll
@@ -171,8 +181,8 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
             u32x4 x[XW];
 #pragma unroll
             for (int h = 0; h < XW; ++h) x[h] = *reinterpret_cast<const u32x4*>(buf + ((mt * U + u) * XW + h) * 1024);
-            acc[mt][0] = mma_tile<WT>(ww[0][u], x, acc[mt][0]);
-            acc[mt][1] = mma_tile<WT>(ww[1][u], x, acc[mt][1]);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[mt][j] = mma_tile<WT>(ww[j][u], x, acc[mt][j]);
           }
         }
       }
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
   // in order), then the barrier makes every wave's activation copies of stage
   // st visible; the copy into the buffer of stage st+2 is issued only after
   // that barrier, when every wave is done with stage st-1, its last reader.
-  auto step = [&](u32x4 (&ww)[2][U], int st) {
+  auto step = [&](u32x4 (&ww)[NTW][U], int st) {
     if (st + 1 < nst) wait_vmcnt<LPS>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -209,34 +219,48 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs a) {
     const int r = mt * 16 + (lane & 15);
     if (r >= rows) continue;
     const int row = row0 + r;
-    float v0[4], v1[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { v0[q] = acc[mt][0][q]; v1[q] = acc[mt][1][q]; }
     if constexpr (EPI == EPI_SWIGLU) {
-      epi_swiglu<AT>(a, sc, row, nt0 * 16 + nq, v0, v1);
+      float g[4], u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { g[q] = acc[mt][0][q]; u[q] = acc[mt][1][q]; }
+      epi_swiglu<AT>(a, sc, row, nt0 * 16 + nq, g, u);
     } else {
-      epi_store<AT, EPI>(a, sc, row, nt0 * 16 + nq, v0, ks);
-      epi_store<AT, EPI>(a, sc, row, (nt0 + 1) * 16 + nq, v1, ks);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[mt][j][q];
+        epi_store<AT, EPI>(a, sc, row, (nt0 + j) * 16 + nq, v, ks);
+      }
     }
   }
 }
 
-template <int WT, int AT, int MT, int EPI>
+template <int WT, int AT, int MT, int EPI, int NW>
 static void run(const GemmArgs& a, hipStream_t s) {
   int64_t blocks = (int64_t)a.max_tiles * a.n_chunks * (a.ksplit > 1 ? a.ksplit : 1);
   blocks = round_up(blocks, 8);
-  hipLaunchKernelGGL((k_gemm<WT, AT, MT, EPI>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_gemm<WT, AT, MT, EPI, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a);
+}
+
+// eight waves for dense launches of at least 32-row tiles, except SwiGLU
+template <int WT, int AT, int MT, int EPI>
+static void run_nw(const GemmArgs& a, hipStream_t s) {
+  if constexpr (EPI != EPI_SWIGLU && MT >= 2) {
+    if (!a.tiles) { run<WT, AT, MT, EPI, 8>(a, s); return; }
+  }
+  run<WT, AT, MT, EPI, 4>(a, s);
 }
 
 template <int WT, int AT, int MT>
 static void run_epi(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
-    case EPI_F32: run<WT, AT, MT, EPI_F32>(a, s); break;
-    case EPI_ROWS: run<WT, AT, MT, EPI_ROWS>(a, s); break;
-    case EPI_RESID: run<WT, AT, MT, EPI_RESID>(a, s); break;
-    case EPI_SWIGLU: run<WT, AT, MT, EPI_SWIGLU>(a, s); break;
-    case EPI_QKV: run<WT, AT, MT, EPI_QKV>(a, s); break;
-    case EPI_RESID_MOE: run<WT, AT, MT, EPI_RESID_MOE>(a, s); break;
+    case EPI_F32: run_nw<WT, AT, MT, EPI_F32>(a, s); break;
+    case EPI_ROWS: run_nw<WT, AT, MT, EPI_ROWS>(a, s); break;
+    case EPI_RESID: run_nw<WT, AT, MT, EPI_RESID>(a, s); break;
+    case EPI_SWIGLU: run_nw<WT, AT, MT, EPI_SWIGLU>(a, s); break;
+    case EPI_QKV: run_nw<WT, AT, MT, EPI_QKV>(a, s); break;
+    case EPI_RESID_MOE: run_nw<WT, AT, MT, EPI_RESID_MOE>(a, s); break;
   }
 }
 
