@@ -39,7 +39,12 @@ int32_t hip_status(const char* where) {
 }
 
 constexpr int64_t ALIGN = 256;
-constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows
+constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows (few rows per expert)
+constexpr int BIG_TILE_ROWS = 256;     // expert row tile of the LDS-staged kernel (many rows per expert)
+
+// Many rows per expert (batched canvases, prefill): 256-row expert tiles on
+// the LDS-staged kernel, which reuses every weight byte 256 times.
+bool big_expert_tiles(int64_t assignments, int E) { return assignments >= (int64_t)BIG_TILE_ROWS * E; }
 constexpr int MAX_SPLIT = ATT_MAX_SPLIT;   // attention key splits
 constexpr int MAX_RSPLIT = MAX_ROUTER_SPLIT;         // router contraction splits
 
@@ -149,7 +154,10 @@ Plan make_plan(const cd_config& c) {
 
   const int R = c.max_requests, T = p.Tmax, k = c.top_k, ae = esize(p.adt);
   const int mrows = 16 * GROUPED_MT;
-  p.max_rows = round_up((int64_t)T * k + (int64_t)E * mrows, 64);
+  // expert segments are padded to the row tile: size for the larger tile
+  // when the largest forward can take it
+  const int pad_rows = big_expert_tiles((int64_t)T * k, E) ? BIG_TILE_ROWS : mrows;
+  p.max_rows = round_up((int64_t)T * k + (int64_t)E * pad_rows, 64);
   p.max_tiles = ((int64_t)T * k + mrows - 1) / mrows + E;
   p.n_blk_max = ((int64_t)T * k + 511) / 512;
   p.n_chunks = sampler_chunks(c.vocab);
@@ -313,8 +321,14 @@ int router_split(const cd_config& g, int T) {
 // 8 workgroups on one XCD (one HBM read, the rest from its L2) and fill the
 // chip without splitting the contraction.
 void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
-  if (M <= 256 && a.n_chunks >= 512 && a.ksplit <= 1) {
+  // the LDS-staged kernel needs enough (256-row slab, 256-column chunk)
+  // items to fill the chip; the expert-combining epilogue gathers 8 rows per
+  // output and prefers the many workgroups of the row-tiled kernel
+  const int64_t x_items = (int64_t)((M + 255) / 256) * ((a.Nt + 15) / 16);
+  const bool lds_staged = a.ksplit <= 1 && epi != EPI_RESID_MOE && ((M > 256 && x_items >= 256) || a.n_chunks >= 512);
+  if (lds_staged) {
     a.M = M;
+    a.tiles = nullptr;
     launch_gemm_x(wdt, c->p.adt, epi, a, s);
     return;
   }
@@ -329,9 +343,15 @@ void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_
 // rows: assignments of this forward (T * top_k); the grid is sized for the
 // most tiles they can form, so idle workgroups stay few
 void gemm_grouped(const cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, hipStream_t s) {
-  const int mrows = 16 * GROUPED_MT;
   a.tiles = c->st<int32_t>(c->p.tiles);
   a.n_tiles = c->st<int32_t>(c->p.n_tiles);
+  if (big_expert_tiles(rows, c->p.c.n_experts)) {
+    a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + BIG_TILE_ROWS - 1) / BIG_TILE_ROWS +
+                                                            std::min<int64_t>(rows, c->p.c.n_experts));
+    launch_gemm_x(wdt, c->p.adt, epi, a, s);
+    return;
+  }
+  const int mrows = 16 * GROUPED_MT;
   a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + mrows - 1) / mrows + std::min<int64_t>(rows, c->p.c.n_experts));
   a.chunk_major = 0;
   launch_gemm(wdt, c->p.adt, GROUPED_MT, epi, a, s);
@@ -438,7 +458,8 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
     ra.blk_cnt = c->st<int32_t>(p.blk_cnt); ra.seg_off = c->st<int32_t>(p.seg_off);
     ra.row_map = c->st<int32_t>(p.row_map); ra.slot = c->st<int32_t>(p.slot);
     ra.tiles = c->st<int32_t>(p.tiles); ra.n_tiles = c->st<int32_t>(p.n_tiles);
-    ra.mrows = 16 * GROUPED_MT; ra.max_rows = (int)p.max_rows; ra.max_tiles = (int)p.max_tiles;
+    ra.mrows = big_expert_tiles((int64_t)T * k, E) ? BIG_TILE_ROWS : 16 * GROUPED_MT;
+    ra.max_rows = (int)p.max_rows; ra.max_tiles = (int)p.max_tiles;
     if (trace && c->trace_ids) {
       ra.trace_ids = c->trace_ids + (int64_t)l * T * k;
       ra.trace_gates = c->trace_gates + (int64_t)l * T * k;
@@ -459,19 +480,25 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       PROF(CD_PROF_EXPERT_DOWN);
       gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, s);
     }
-    if (!g.shared_hidden) {
+    // At canvas-batch sizes the shared FFN's down projection also adds the
+    // routed experts' outputs (the combine step) into the residual, saving a
+    // launch; for thousands of rows the separate combine kernel gathers the
+    // expert rows more efficiently than the GEMM epilogue.
+    const bool fuse_combine = g.shared_hidden && T <= 1024;
+    if (!fuse_combine) {
       PROF(CD_PROF_COMBINE);
       launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate), T, k, d, h, s);
-    } else {
+    }
+    if (g.shared_hidden) {
       if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
-      // the shared FFN's down projection also adds the routed experts'
-      // outputs (the combine step) into the residual
       GemmArgs b = gemm_base(c->st<void>(p.sact), g.shared_hidden, c->W + lw.sdn, nullptr, g.shared_hidden,
                              p.sdn_npad, d, h, d);
-      b.moe_y = c->st<void>(p.yperm); b.moe_slot = c->st<int32_t>(p.slot); b.moe_gate = c->st<float>(p.topk_gate);
-      b.moe_k = k; b.moe_ld = d;
+      if (fuse_combine) {
+        b.moe_y = c->st<void>(p.yperm); b.moe_slot = c->st<int32_t>(p.slot); b.moe_gate = c->st<float>(p.topk_gate);
+        b.moe_k = k; b.moe_ld = d;
+      }
       PROF(CD_PROF_SHARED_DOWN);
-      gemm_dense(c, p.wdt_other, EPI_RESID_MOE, b, T, s);
+      gemm_dense(c, p.wdt_other, fuse_combine ? EPI_RESID_MOE : EPI_RESID, b, T, s);
     }
   }
   if (head) {

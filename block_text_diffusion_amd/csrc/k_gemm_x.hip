@@ -47,7 +47,36 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 2, wn = wave & 3;         // row half, column pair
   const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
-  const int ks = blockIdx.x % ksplit, chunk = blockIdx.x / ksplit;
+  const int nchunks = (a.Nt + 4 * XNTW - 1) / (4 * XNTW);
+  // Work item = (row tile of up to 256 rows, 256-column chunk, k split).
+  // Items are dealt to the 8 XCDs in contiguous runs (the dispatcher deals
+  // workgroups round-robin), chunk-major: the row tiles of one weight chunk
+  // run back to back on one XCD and share that chunk through its L2.
+  int ks, chunk, tile;
+  {
+    int nt;
+    if (a.tiles) nt = *a.n_tiles;
+    else nt = (a.M + XMT * 16 - 1) / (XMT * 16);
+    const int work = nt * nchunks * ksplit;
+    const int w8 = (work + 7) & ~7;
+    const int bid = blockIdx.x;
+    if (bid >= w8) return;
+    int logical = (bid & 7) * (w8 >> 3) + (bid >> 3);
+    if (logical >= work) return;
+    ks = logical % ksplit;
+    logical /= ksplit;
+    chunk = logical / nt;
+    tile = logical - chunk * nt;
+  }
+  int group = 0, row0, rows;
+  if (a.tiles) {
+    group = a.tiles[4 * tile];
+    row0 = a.tiles[4 * tile + 1];
+    rows = a.tiles[4 * tile + 2];
+  } else {
+    row0 = tile * XMT * 16;
+    rows = min(XMT * 16, a.M - row0);
+  }
   const int KTall = a.K / KF;
   const int kt0 = (int)((int64_t)KTall * ks / ksplit);
   const int nst = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt0;
@@ -56,17 +85,21 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   const int nt0 = chunk * 4 * XNTW + wn * XNTW;
   const int esa = (AT == DT_F32) ? 4 : 2;
 
+  const uint8_t* wbase = a.W + (int64_t)group * a.w_gstride;
   const uint8_t* wp[XNTW];
 #pragma unroll
   for (int j = 0; j < XNTW; ++j)
-    wp[j] = a.W + ((int64_t)min(nt0 + j, a.Nt - 1) * KTall + kt0) * 1024 + lane * 16;
+    wp[j] = wbase + ((int64_t)min(nt0 + j, a.Nt - 1) * KTall + kt0) * 1024 + lane * 16;
+  // rows past the tile's end read its last row (finite); their results are dropped
   const uint8_t* xsrc[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int b = wave * BPW + i;
     const int mt = b / XW, h = b % XW;
-    const int row = min(mt * 16 + (lane & 15), a.M - 1);
-    xsrc[i] = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)row * a.ldx * esa + (lane >> 4) * 16 * XW + h * 16 +
+    const int r = min(mt * 16 + (lane & 15), rows - 1);
+    int src = a.row_map ? a.row_map[row0 + r] : row0 + r;
+    if (src < 0) src = 0;
+    xsrc[i] = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)src * a.ldx * esa + (lane >> 4) * 16 * XW + h * 16 +
               (int64_t)kt0 * XSTEP;
   }
 
@@ -103,14 +136,36 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
         x[h] = *reinterpret_cast<const u32x4*>(buf + (((wm * XMTW + mt) * XW + h) * 64 + lane) * 16);
     };
     rd(xa, 0);
+    if constexpr (WT == DT_FP8) {
+      // widen the fp8 weight fragments once for all row tiles
+      u32x4 wb[XNTW][2];
 #pragma unroll
-    for (int mt = 0; mt < XMTW; mt += 2) {
-      rd(xb, mt + 1);
+      for (int j = 0; j < XNTW; ++j) widen_fp8(ww[j], wb[j]);
 #pragma unroll
-      for (int j = 0; j < XNTW; ++j) acc[mt][j] = mma_tile<WT>(ww[j], xa, acc[mt][j]);
-      if (mt + 2 < XMTW) rd(xa, mt + 2);
+      for (int mt = 0; mt < XMTW; mt += 2) {
+        rd(xb, mt + 1);
 #pragma unroll
-      for (int j = 0; j < XNTW; ++j) acc[mt + 1][j] = mma_tile<WT>(ww[j], xb, acc[mt + 1][j]);
+        for (int j = 0; j < XNTW; ++j) {
+          acc[mt][j] = mma_bf16(wb[j][0], xa[0], acc[mt][j]);
+          acc[mt][j] = mma_bf16(wb[j][1], xa[1], acc[mt][j]);
+        }
+        if (mt + 2 < XMTW) rd(xa, mt + 2);
+#pragma unroll
+        for (int j = 0; j < XNTW; ++j) {
+          acc[mt + 1][j] = mma_bf16(wb[j][0], xb[0], acc[mt + 1][j]);
+          acc[mt + 1][j] = mma_bf16(wb[j][1], xb[1], acc[mt + 1][j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < XMTW; mt += 2) {
+        rd(xb, mt + 1);
+#pragma unroll
+        for (int j = 0; j < XNTW; ++j) acc[mt][j] = mma_tile<WT>(ww[j], xa, acc[mt][j]);
+        if (mt + 2 < XMTW) rd(xa, mt + 2);
+#pragma unroll
+        for (int j = 0; j < XNTW; ++j) acc[mt + 1][j] = mma_tile<WT>(ww[j], xb, acc[mt + 1][j]);
+      }
     }
     // order: reads of tile 0, then (reads of tile mt+1, MFMAs of tile mt)
     constexpr int RD = XW;                                                     // DS reads per tile
@@ -151,11 +206,12 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   wait_vmcnt<0>();   // no LDS copy may still be in flight when the workgroup exits
 
   const int nq = (lane >> 4) * 4;
-  const float* sc = a.wscale;
+  const float* sc = a.wscale ? a.wscale + (int64_t)group * a.s_gstride : nullptr;
 #pragma unroll
   for (int mt = 0; mt < XMTW; ++mt) {
-    const int row = (wm * XMTW + mt) * 16 + (lane & 15);
-    if (row >= a.M) continue;
+    const int r = (wm * XMTW + mt) * 16 + (lane & 15);
+    if (r >= rows) continue;
+    const int row = row0 + r;
 #pragma unroll
     for (int j = 0; j < XNTW; j += 2) {
       if (nt0 + j >= a.Nt) break;     // Nt is even: tiles come in valid pairs
@@ -174,8 +230,11 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
 
 template <int WT, int AT, int EPI>
 static void run_x(const GemmArgs& a, hipStream_t s) {
+  // grid sized for the most row tiles (grouped: max_tiles; dense: M/256),
+  // rounded to the 8 XCDs; surplus workgroups return at once
   const int chunks = (a.Nt + 4 * XNTW - 1) / (4 * XNTW);
-  const int blocks = chunks * (a.ksplit > 1 ? a.ksplit : 1);
+  const int tiles = a.tiles ? a.max_tiles : (a.M + XMT * 16 - 1) / (XMT * 16);
+  const int blocks = (int)round_up((int64_t)tiles * chunks * (a.ksplit > 1 ? a.ksplit : 1), 8);
   hipLaunchKernelGGL((k_gemm_x<WT, AT, EPI>), dim3(blocks), dim3(64 * XWAVES), 0, s, a);
 }
 

@@ -199,10 +199,16 @@ __global__ __launch_bounds__(256) void k_route_scan(RouteArgs a, int n_blk) {
   const int e = threadIdx.x;
   int total = 0;
   if (e < a.E) {
-    for (int b = 0; b < n_blk; ++b) {
-      int c = a.blk_cnt[(int64_t)b * a.E + e];
-      a.blk_cnt[(int64_t)b * a.E + e] = total;   // exclusive base within the expert
-      total += c;
+    // counts are loaded 16 blocks at a time so the loads overlap
+    for (int b0 = 0; b0 < n_blk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = b0 + j < n_blk ? a.blk_cnt[(int64_t)(b0 + j) * a.E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < n_blk) a.blk_cnt[(int64_t)(b0 + j) * a.E + e] = total;   // exclusive base within the expert
+        total += c[j];
+      }
     }
   }
   const int pad = (total + a.mrows - 1) / a.mrows * a.mrows;

@@ -124,3 +124,39 @@ def test_capacity_boundary_prefill_and_blocks_fill_cache_exactly():
         Ko = req.cache[l][0][:, P0 + C:max_ctx]
         Kg = K[l][:, P0 + C:max_ctx]
         assert rel_l2_rows(Kg.reshape(-1, w["dh"]), Ko.reshape(-1, w["dh"])).max() <= TOL["f32"], l
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16"])
+def test_prefill_with_large_expert_tiles(wdtype):
+    # 1024 prompt tokens x top-2 over 8 experts: 256 or more rows per expert,
+    # so the expert GEMMs take 256-row tiles on the LDS-staged kernel and the
+    # dense layers (more than 256 rows) run on it in 256-row slabs
+    w = synth_inputs.workload("tiny", wdtype=wdtype, P0=1024)
+    tol = TOL[wdtype]
+    announce("edges_prefill_large_tiles", wdtype=wdtype)
+    n = 1000                                      # a ragged last slab and ragged expert tiles
+    eng = Engine(w, max_ctx=n + w["C"], max_prefill=n)
+    B.cd_synth_weights(eng.ctx, w["weight_seed"])
+    L, k = w["L"], w["k"]
+    tid = torch.zeros(L, n, k, dtype=torch.int32, device="cuda")
+    tg = torch.zeros(L, n, k, dtype=torch.float32, device="cuda")
+    B.cd_set_trace(eng.ctx, None, tid, tg)
+    pre = synth_inputs.prefix_ids(w["V"], n, 21, 0)
+    B.cd_prefill(eng.ctx, 0, torch.from_numpy(pre).cuda())
+    torch.cuda.synchronize()
+    gid = [to_np(tid[l]) for l in range(L)]
+    K = to_np(eng.kcache()[0, :, :, :n, :])
+    V = to_np(eng.vcache()[0, :, :, :, :n]).transpose(0, 1, 3, 2)
+    eng.close()
+    W = Weights(w)
+    req = loop.Request(w)
+    tr = []
+    from oracle import model
+    _, kv, _ = model.forward(w, W, pre, np.arange(n), req.cache, causal=True, head=False, trace=tr,
+                             forced_routing=gid)
+    from tests.gpu_util import check_routing
+    check_routing(gid, tr, k, tol)
+    for l in range(L):
+        Ko, Vo = kv[l]
+        assert rel_l2_rows(K[l].reshape(-1, w["dh"]), Ko.reshape(-1, w["dh"])).max() <= tol, ("K", l)
+        assert rel_l2_rows(V[l].reshape(-1, w["dh"]), Vo.reshape(-1, w["dh"])).max() <= tol, ("V", l)
