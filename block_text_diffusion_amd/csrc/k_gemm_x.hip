@@ -1,24 +1,24 @@
-// Dense GEMM for up to 256 activation rows (the canvas batch) with the
-// activations staged in LDS:  Y[m][n] = sum_k X[m][k] * W[n][k].
-//
-// At 256 rows a weight byte feeds 256 MACs, so splitting the rows across
-// workgroups (as the grouped kernel does for small tiles) would make every
-// workgroup re-stream the same weight slice.  Here one workgroup owns all
-// rows of a 128-column slice:
+// GEMM on 256-row work items with the activations staged in LDS:
+// Y[m][n] = sum_k X[m][k] * W[n][k].  A work item is a 256-row slab of a
+// dense launch, or a 256-row tile of one expert (grouped launch), times a
+// 256-column chunk, so every weight byte feeds 256 rows and every activation
+// byte 256 columns.  Used for the LM head at the canvas batch and for every
+// GEMM at more than 256 rows (batched canvases, prefill).
 //  * per k-tile stage the workgroup copies the 16 activation fragments
 //    (16 rows x KF columns each, 1 KB, already in MFMA operand order) from
 //    global memory straight into LDS with global_load_lds_dwordx4 -- each
 //    lane's 16 bytes land at the wave's LDS base + lane*16, which is exactly
 //    the fragment layout -- so staging costs no VGPRs;
-//  * each wave streams its two 16-column weight tiles into registers and
-//    reads all 16 activation fragments of the stage from LDS (one contiguous
-//    1 KB ds_read per fragment, conflict-free);
-//  * activations and weights are both prefetched DIST stages ahead (4 LDS
-//    buffers of 16 KB, 3 register slots), so the one in-order vmcnt counter
-//    covers both streams with a single wait per stage;
-//  * used for the LM head, whose thousands of column chunks fill the chip
-//    (the kernel can also split the contraction into fp32 partials, EPI_F32
-//    with ksplit > 1).
+//  * eight waves, two per SIMD: waves 0-3 take rows 0-127 and waves 4-7 rows
+//    128-255, each streaming four 16-column weight tiles into registers and
+//    reading its eight activation fragments of the stage from LDS (one
+//    contiguous, conflict-free 1 KB ds_read each);
+//  * activations and weights are both prefetched DIST stages ahead (LDS
+//    buffers and register slots), so the one in-order vmcnt counter covers
+//    both streams with a single wait per stage;
+//  * fp8 weights are widened to bf16 once per stage for all row tiles;
+//  * the contraction can also be split into fp32 partials (EPI_F32 with
+//    ksplit > 1).
 #include "common.h"
 #include "gemm_epi.h"
 #include "kernels.h"
