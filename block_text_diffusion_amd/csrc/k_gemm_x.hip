@@ -85,6 +85,9 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   const int nt0 = chunk * 4 * XNTW + wn * XNTW;
   const int esa = (AT == DT_F32) ? 4 : 2;
 
+  // a wave whose 128 rows all lie past the tile's end skips the MFMAs (it
+  // still copies activations and meets every barrier)
+  const bool row_live = wm * XMTW * 16 < rows;
   const uint8_t* wbase = a.W + (int64_t)group * a.w_gstride;
   const uint8_t* wp[XNTW];
 #pragma unroll
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       issue_x(s + DIST);
       __builtin_amdgcn_sched_barrier(0);
-      if (s < nst) compute(w[j], xs[s % NBUF]);
+      if (s < nst && row_live) compute(w[j], xs[s % NBUF]);
       __builtin_amdgcn_sched_barrier(0);
       issue_w(w[j], s + DIST);
       __builtin_amdgcn_sched_barrier(0);
