@@ -36,10 +36,11 @@ namespace cd {
 // launches with several workgroups per CU and the SwiGLU epilogue (gate and
 // up tiles in one wave); eight waves of one tile put two waves on each SIMD
 // when a dense launch has only about one workgroup per CU.
-template <int WT, int AT, int MT, int EPI, int NW>
+template <int WT, int AT, int MT, int EPI, int NW, int CT = 8>
 __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
-  constexpr int NTW = 8 / NW;
+  constexpr int NTW = CT / NW;
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(NTW >= 1 && NTW * NW == CT, "weight tiles per wave");
   static_assert(EPI != EPI_SWIGLU || NTW == 2, "SwiGLU needs gate and up tiles in one wave");
   constexpr int MROWS = 16 * MT;
   constexpr int U = 4;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   // a wave past the last weight tile still copies its share of the
   // activations and meets every barrier; it computes on a valid tile and
   // stores nothing
-  const int nt0 = chunk * 8 + wave * NTW;
+  const int nt0 = chunk * CT + wave * NTW;
   const bool active = nt0 < a.Nt;
   const int ntc = active ? nt0 : 0;
 
@@ -193,21 +194,29 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   // in order), then the barrier makes every wave's activation copies of stage
   // st visible; the copy into the buffer of stage st+2 is issued only after
   // that barrier, when every wave is done with stage st-1, its last reader.
+  // Every stage issues its loads, past the end too (their k-tiles clamp to
+  // the last one and land in a buffer no later stage reads): with the same
+  // loads in flight on every path the compiler's own waits before the MFMAs
+  // stay at this stage's loads instead of draining the prefetch.
   auto step = [&](u32x4 (&ww)[NTW][U], int st) {
-    if (st + 1 < nst) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<LPS>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    compute(ww, st);
+    if (st < nst) compute(ww, st);
     __builtin_amdgcn_sched_barrier(0);
-    if (st + 2 < nst) issue(ww, st + 2);
+    issue(ww, st + 2);
     __builtin_amdgcn_sched_barrier(0);
   };
-  if (nst > 0) issue(wA, 0);
-  if (nst > 1) issue(wB, 1);
-  for (int st = 0; st < nst; st += 2) {
-    step(wA, st);
-    if (st + 1 < nst) step(wB, st + 1);
+  if (nst > 0) {
+    issue(wA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(wB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int st = 0; st < nst; st += 2) {
+      step(wA, st);
+      step(wB, st + 1);
+    }
+    wait_vmcnt<0>();   // no copy into LDS may be in flight when the wave moves on
   }
   if (!active) return;
 

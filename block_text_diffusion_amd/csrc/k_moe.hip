@@ -1,14 +1,18 @@
-// MoE routing: top-k over router logits, deterministic counting sort of the
-// (token, slot) assignments by expert, the tile table of the grouped GEMM,
-// and the gate-weighted combine back into the residual stream.
+// MoE routing: top-k over router logits, the sort of the (token, slot)
+// assignments by expert, the tile table of the grouped GEMM, and the
+// gate-weighted combine back into the residual stream.
 //
-// Top-k: one wave per token; k rounds of a wave-wide argmax (ties to the
-// lower expert id); gates = softmax over the k selected logits.
-// Sort: assignments (t, j) in order t*k + j are cut into blocks of 512; one
-// thread per expert counts its assignments per block, a single workgroup
-// turns the counts into per-block bases and expert segments padded to the
-// GEMM row tile, and the same per-expert scan places every assignment.  The
-// permuted order is therefore (expert, token, slot) regardless of timing.
+// Top-k: sixteen lanes (one DPP row) per token; k rounds of a row-wide argmax
+// (ties to the lower expert id); gates = softmax over the k selected logits.
+// Sort: an assignment's rank among the earlier assignments of its expert is
+// found per wave (wave_match_rank) plus per-expert prefixes over the waves.  Small batches (up to 4096 assignments): one workgroup ranks,
+// counts, scans the padded segments and places every assignment.  Larger
+// batches: blocks of 512 assignments rank and count, a single workgroup turns
+// the counts into per-block bases and expert segments padded to the GEMM row
+// tile, and the placement adds segment base, block base and rank.  Either way
+// the permuted order is (expert, token, slot) regardless of timing; every row
+// of a segment is computed on its own and the combine reads a token's slots
+// in choice order, so no result depends on the order inside a segment.
 #include "common.h"
 #include "kernels.h"
 
@@ -16,77 +20,126 @@ namespace cd {
 
 constexpr int ROUTE_BLK = 512;
 
-// One wave per token; lane j ends up holding the j-th choice.  Non-finite
-// logits cannot produce an invalid id: NaN ranks as -inf and every round
-// picks the best expert not yet taken (ties and -inf to the lowest id), so
-// the k ids are always distinct and inside [0, E).
+// Sixteen lanes (one DPP row) per token, four tokens per wave; lane j of the
+// row ends up holding the j-th choice (k <= 16).  Lane l holds experts
+// l, l+16, ...; each of the k rounds takes every lane's best expert not yet
+// taken and reduces the row with four DPP exchanges (quad swaps, then the
+// half-row and row mirrors), keeping the larger logit and on ties the lower
+// expert id.  Non-finite logits cannot produce an invalid id: NaN ranks as
+// -inf and every round picks the best expert not yet taken (ties and -inf to
+// the lowest id), so the k ids are always distinct and inside [0, E).
+template <int CTRL>
+__device__ __forceinline__ void row_best(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, 0xF, 0xF, false);
+  const bool b = (ov > bv) | ((ov == bv) & (oi < bi));
+  bv = b ? ov : bv;
+  bi = b ? oi : bi;
+}
+template <int CTRL>
+__device__ __forceinline__ void row_add(float& v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
+
+template <int NPL>   // experts per lane: E <= 16 * NPL
 __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  // logit = sum of the router's split partials, added in split order; all
-  // partials of a lane are loaded before the first add so the loads overlap
-  float v[4];
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
+  const int t = (blockIdx.x * 256 + threadIdx.x) >> 4;
+  if (t >= a.T) return;   // whole rows leave together
+  // logit = sum of the router's split partials, added in split order.  The
+  // partials come in chunks of four splits, every load of a chunk issued
+  // before the first add and none of them conditional (split and expert
+  // indices are clamped; the extra loads are not added), so they overlap.
+  float v[NPL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    float x = -INFINITY;
-    if (e < a.E) {
-      float part[MAX_ROUTER_SPLIT];
+  for (int i = 0; i < NPL; ++i) v[i] = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += 4) {
+    float part[NPL][4];
 #pragma unroll
-      for (int s = 0; s < MAX_ROUTER_SPLIT; ++s)
-        part[s] = s < a.nsplit ? a.logits[((int64_t)s * a.T + t) * a.E + e] : 0.f;
-      x = 0.f;
+    for (int i = 0; i < NPL; ++i) {
+      const int e = min(l16 + 16 * i, a.E - 1);
 #pragma unroll
-      for (int s = 0; s < MAX_ROUTER_SPLIT; ++s)
-        if (s < a.nsplit) x += part[s];
-      if (x != x) x = -INFINITY;
+      for (int q = 0; q < 4; ++q) {
+        const int sp = min(s0 + q, a.nsplit - 1);
+        part[i][q] = a.logits[((int64_t)sp * a.T + t) * a.E + e];
+      }
     }
-    v[i] = x;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (s0 + q < a.nsplit) v[i] += part[i][q];
   }
-  uint32_t taken = 0;
+  // candidate i of this lane: (logit, expert id); an expert past E or already
+  // taken is (-inf, INT_MAX), which no available expert ties with or loses to
+  int eid[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = l16 + 16 * i;
+    const bool live = e < a.E;
+    eid[i] = live ? e : 0x7FFFFFFF;
+    v[i] = (live && v[i] == v[i]) ? v[i] : -INFINITY;
+  }
   float my_v = -INFINITY;
   int my_id = 0;
   for (int j = 0; j < a.k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < a.E && !(taken & (1u << i)) && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+    for (int i = 0; i < NPL; ++i) {   // branch-free: bitwise, not short-circuit, conditions
+      const bool b = (v[i] > bv) | ((v[i] == bv) & (eid[i] < bi));
+      bv = b ? v[i] : bv;
+      bi = b ? eid[i] : bi;
     }
+    row_best<DPP_QUAD_XOR1>(bv, bi);
+    row_best<DPP_QUAD_XOR2>(bv, bi);
+    row_best<DPP_ROW_HALF_MIRROR>(bv, bi);
+    row_best<DPP_ROW_MIRROR>(bv, bi);
+    my_v = (l16 == j) ? bv : my_v;
+    my_id = (l16 == j) ? bi : my_id;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    for (int i = 0; i < NPL; ++i) {
+      const bool hit = eid[i] == bi;
+      v[i] = hit ? -INFINITY : v[i];
+      eid[i] = hit ? 0x7FFFFFFF : eid[i];
     }
-    if (lane == j) { my_v = bv; my_id = bi; }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == bi) taken |= 1u << i;
   }
-  // gates: softmax over the k selected logits (lane 0 holds the largest);
-  // uniform if every selected logit is -inf
-  const float mx = __shfl(my_v, 0, 64);
-  float g = lane < a.k ? (mx == -INFINITY ? 1.f : expf(my_v - mx)) : 0.f;
-  const float sum = wave_sum(g);
-  if (lane < a.k) {
+  // gates: softmax over the k selected logits (the row's lane 0 holds the
+  // largest); uniform if every selected logit is -inf
+  const float mx = __shfl(my_v, lane & ~15, 64);
+  float g = l16 < a.k ? (mx == -INFINITY ? 1.f : expf(my_v - mx)) : 0.f;
+  float sum = g;
+  row_add<DPP_QUAD_XOR1>(sum);
+  row_add<DPP_QUAD_XOR2>(sum);
+  row_add<DPP_ROW_HALF_MIRROR>(sum);
+  row_add<DPP_ROW_MIRROR>(sum);
+  if (l16 < a.k) {
     g = g / sum;
-    a.topk_id[(int64_t)t * a.k + lane] = my_id;
-    a.topk_gate[(int64_t)t * a.k + lane] = g;
-    if (a.trace_ids) a.trace_ids[(int64_t)t * a.k + lane] = my_id;
-    if (a.trace_gates) a.trace_gates[(int64_t)t * a.k + lane] = g;
+    a.topk_id[(int64_t)t * a.k + l16] = my_id;
+    a.topk_gate[(int64_t)t * a.k + l16] = g;
+    if (a.trace_ids) a.trace_ids[(int64_t)t * a.k + l16] = my_id;
+    if (a.trace_gates) a.trace_gates[(int64_t)t * a.k + l16] = g;
   }
 }
 
-// Small batches: count, scan, tile table and placement in one workgroup.
-// Thread g owns the 16 consecutive assignments of group g; cnt[e][g] counts
-// expert e in group g and becomes, after a per-expert prefix over groups, the
-// rank base of that group inside expert e's segment.  Ranks therefore follow
+// Small batches (at most 4096 assignments): count, scan, tile table and
+// placement in one workgroup of 1024 threads.  The assignments are taken in
+// chunks of 64 (one wave each); each chunk ranks and counts its assignments
+// per expert in its own row of an LDS table, and a per-expert prefix over the
+// chunks turns the counts into bases, so every segment lists its rows in
 // assignment order (token, slot).
-constexpr int RG = 16;
-constexpr int ROUTE_ONE_CNT = 24576;   // E * groups (uint16 LDS cells)
+constexpr int ROUTE_ONE_MAX = 4096;
+constexpr int ROUTE_CHUNKS = ROUTE_ONE_MAX / 64;
+
+// Rank of this lane's assignment (expert e, -1: none) among the earlier
+// assignments of its wave with the same expert, counted into the wave's own
+// LDS row by one LDS atomic per lane.  The LDS resolves the lanes of one
+// instruction that hit the same counter in lane order (as measured on gfx950;
+// no result depends on it, only the order of rows inside a segment does).
+__device__ __forceinline__ int wave_match_rank(int e, uint32_t* counts) {
+  return e >= 0 ? (int)atomicAdd(&counts[e], 1u) : 0;
+}
 
 __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
   int x = v;
@@ -97,34 +150,147 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
   }
   return x - v;
 }
-
-__global__ __launch_bounds__(256) void k_route_one(RouteArgs a) {
-  __shared__ uint16_t cnt[ROUTE_ONE_CNT];
-  __shared__ int32_t seg[256], tile0[256], tot[256];
+__global__ __launch_bounds__(1024) void k_route_one(RouteArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t ccnt[ROUTE_CHUNKS * 256];   // [chunk][expert]
+  __shared__ int32_t cnt[256], seg[256], tile0[256];
   __shared__ int32_t totals[2];
-  const int n = a.T * a.k, ng = (n + RG - 1) / RG, E = a.E;
-  const int tid = threadIdx.x, lane = tid & 63;
-  for (int i = tid; i < E * ng; i += 256) cnt[i] = 0;
-  __syncthreads();
-  int ex[RG];
+  constexpr int PT = ROUTE_ONE_MAX / 1024;   // assignments per thread
+  const int n = a.T * a.k, E = a.E;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nchunk = (n + 63) / 64;
+  int ex[PT];
 #pragma unroll
-  for (int j = 0; j < RG; ++j) {
-    const int i = tid * RG + j;
-    const int e = (tid < ng && i < n) ? a.topk_id[i] : -1;
-    ex[j] = (e >= 0 && e < E) ? e : -1;
+  for (int q = 0; q < PT; ++q) {
+    const int i = q * 1024 + tid;
+    const int e = i < n ? a.topk_id[i] : -1;
+    ex[q] = (e >= 0 && e < E) ? e : -1;
+  }
+  for (int i = tid * 4; i < nchunk * E; i += 1024 * 4) *reinterpret_cast<uint4*>(ccnt + i) = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  // chunk q*16 + wave holds assignments (q*16 + wave)*64 .. +63
+  int rk[PT];
+#pragma unroll
+  for (int q = 0; q < PT; ++q) rk[q] = wave_match_rank(ex[q], ccnt + (q * 16 + wave) * E);
+  __syncthreads();
+  if (tid < E) {
+    // exclusive prefix over the chunks, 16 cells loaded before any is used
+    int run = 0;
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = c0 + j < nchunk ? ccnt[(c0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (c0 + j < nchunk) {
+          ccnt[(c0 + j) * E + tid] = (uint32_t)run;
+          run += v[j];
+        }
+    }
+    cnt[tid] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < PT; ++q)
+    if (ex[q] >= 0) rk[q] += ccnt[(q * 16 + wave) * E + ex[q]];
+  if (tid < 64) {   // segment and tile offsets: wave-wide exclusive scans, 4 experts per lane
+    int pad[4], nt[4], sp = 0, st = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      const int t = e < E ? cnt[e] : 0;
+      pad[q] = (t + a.mrows - 1) / a.mrows * a.mrows;
+      nt[q] = pad[q] / a.mrows;
+      sp += pad[q];
+      st += nt[q];
+    }
+    int ep = wave_excl_scan(sp, lane), et = wave_excl_scan(st, lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      if (e < E) { seg[e] = ep; tile0[e] = et; }
+      ep += pad[q];
+      et += nt[q];
+    }
+    if (lane == 63) { totals[0] = ep; totals[1] = et; }
+  }
+  __syncthreads();
+  if (tid == 0) { a.seg_off[E] = totals[0]; *a.n_tiles = totals[1]; }
+  if (tid < E) {
+    const int off = seg[tid], total = cnt[tid];
+    a.seg_off[tid] = off;
+    for (int i = 0; i * a.mrows < total; ++i) {
+      int32_t* tl = a.tiles + 4 * (int64_t)(tile0[tid] + i);
+      tl[0] = tid;
+      tl[1] = off + i * a.mrows;
+      tl[2] = min(a.mrows, total - i * a.mrows);
+      tl[3] = 0;
+    }
+  }
+  // padding rows of every segment (fewer than mrows each): wave w takes
+  // experts w, w+16, ..., its lanes the rows
+  for (int e = tid >> 6; e < E; e += 16) {
+    const int total = cnt[e], pad = (total + a.mrows - 1) / a.mrows * a.mrows;
+    for (int r = total + lane; r < pad; r += 64) a.row_map[seg[e] + r] = -1;
   }
 #pragma unroll
-  for (int j = 0; j < RG; ++j)
-    if (ex[j] >= 0) cnt[ex[j] * ng + tid] += 1;          // column tid is this thread's alone
+  for (int q = 0; q < PT; ++q) {
+    if (ex[q] < 0) continue;
+    const int i = q * 1024 + tid;
+    const int slot = seg[ex[q]] + rk[q];
+    a.slot[i] = slot;
+    a.row_map[slot] = i / a.k;
+  }
+}
+
+// one assignment per thread: its rank inside (block, expert) -- the rank
+// inside its wave plus the per-expert prefix over the block's 8 waves, kept
+// in slot[] until the placement -- and the block's count per expert
+__global__ __launch_bounds__(ROUTE_BLK) void k_route_count(RouteArgs a) {
+  constexpr int NWB = ROUTE_BLK / 64;
+  __shared__ uint32_t wc[NWB * 256];   // [wave][expert]
+  const int b = blockIdx.x, n = a.T * a.k, E = a.E;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = b * ROUTE_BLK + tid;
+  for (int c = tid; c < NWB * E; c += ROUTE_BLK) wc[c] = 0;
+  const int e0 = i < n ? a.topk_id[i] : -1;
+  const int e = (e0 >= 0 && e0 < E) ? e0 : -1;   // ids outside [0, E) match no expert
+  __syncthreads();
+  int r = wave_match_rank(e, wc + wave * E);
   __syncthreads();
   if (tid < E) {
     int run = 0;
-    for (int c = 0; c < ng; ++c) {
-      const int v = cnt[tid * ng + c];
-      cnt[tid * ng + c] = (uint16_t)run;
-      run += v;
+#pragma unroll
+    for (int w = 0; w < NWB; ++w) {
+      const int c = wc[w * E + tid];
+      wc[w * E + tid] = (uint32_t)run;
+      run += c;
     }
-    tot[tid] = run;
+    a.blk_cnt[(int64_t)b * E + tid] = run;
+  }
+  __syncthreads();
+  if (e >= 0) r += wc[wave * E + e];
+  if (i < n) a.slot[i] = r;
+}
+
+// single workgroup: per-block bases, padded segments, tile table, pad rows
+__global__ __launch_bounds__(256) void k_route_scan(RouteArgs a, int n_blk) {
+  __shared__ int32_t tot[256], seg[256], tile0[256];
+  __shared__ int32_t totals[2];
+  const int tid = threadIdx.x, lane = tid & 63, E = a.E;
+  if (tid < E) {
+    // counts are loaded 16 blocks at a time so the loads overlap
+    int total = 0;
+    for (int b0 = 0; b0 < n_blk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = b0 + j < n_blk ? a.blk_cnt[(int64_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < n_blk) a.blk_cnt[(int64_t)(b0 + j) * E + tid] = total;   // exclusive base within the expert
+        total += c[j];
+      }
+    }
+    tot[tid] = total;
   }
   __syncthreads();
   if (tid < 64) {   // segment and tile offsets: wave-wide exclusive scans, 4 experts per lane
@@ -152,7 +318,6 @@ __global__ __launch_bounds__(256) void k_route_one(RouteArgs a) {
   if (tid == 0) { a.seg_off[E] = totals[0]; *a.n_tiles = totals[1]; }
   if (tid < E) {
     const int off = seg[tid], total = tot[tid];
-    const int pad = (total + a.mrows - 1) / a.mrows * a.mrows;
     a.seg_off[tid] = off;
     for (int i = 0; i * a.mrows < total; ++i) {
       int32_t* tl = a.tiles + 4 * (int64_t)(tile0[tid] + i);
@@ -161,116 +326,38 @@ __global__ __launch_bounds__(256) void k_route_one(RouteArgs a) {
       tl[2] = min(a.mrows, total - i * a.mrows);
       tl[3] = 0;
     }
-    for (int r = off + total; r < off + pad; ++r) a.row_map[r] = -1;
   }
-  if (tid < ng) {
-#pragma unroll
-    for (int j = 0; j < RG; ++j) {
-      const int e = ex[j];
-      if (e < 0) continue;
-      int r = 0;
-#pragma unroll
-      for (int jj = 0; jj < j; ++jj) r += (ex[jj] == e);
-      const int slot = seg[e] + cnt[e * ng + tid] + r;
-      const int i = tid * RG + j;
-      a.slot[i] = slot;
-      a.row_map[slot] = i / a.k;
-    }
+  // padding rows of every segment (fewer than mrows each): wave w takes
+  // experts w, w+4, ..., its lanes the rows
+  for (int e = tid >> 6; e < E; e += 4) {
+    const int total = tot[e], pad = (total + a.mrows - 1) / a.mrows * a.mrows;
+    for (int r = total + lane; r < pad; r += 64) a.row_map[seg[e] + r] = -1;
   }
 }
 
-__global__ __launch_bounds__(256) void k_route_count(RouteArgs a) {
-  __shared__ int32_t ex[ROUTE_BLK];
-  const int b = blockIdx.x;
-  const int n = a.T * a.k;
-  const int beg = b * ROUTE_BLK, cnt = min(ROUTE_BLK, n - beg);
-  for (int i = threadIdx.x; i < cnt; i += 256) ex[i] = a.topk_id[beg + i];
-  __syncthreads();
-  const int e = threadIdx.x;   // ids outside [0, E) match no expert
-  if (e >= a.E) return;
-  int c = 0;
-  for (int i = 0; i < cnt; ++i) c += (ex[i] == e);
-  a.blk_cnt[(int64_t)b * a.E + e] = c;
-}
-
-// single workgroup: per-block bases, padded segments, tile table, pad rows
-__global__ __launch_bounds__(256) void k_route_scan(RouteArgs a, int n_blk) {
-  __shared__ int32_t padded[256], tcount[256];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < a.E) {
-    // counts are loaded 16 blocks at a time so the loads overlap
-    for (int b0 = 0; b0 < n_blk; b0 += 16) {
-      int c[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) c[j] = b0 + j < n_blk ? a.blk_cnt[(int64_t)(b0 + j) * a.E + e] : 0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (b0 + j < n_blk) a.blk_cnt[(int64_t)(b0 + j) * a.E + e] = total;   // exclusive base within the expert
-        total += c[j];
-      }
-    }
-  }
-  const int pad = (total + a.mrows - 1) / a.mrows * a.mrows;
-  padded[e] = e < a.E ? pad : 0;
-  tcount[e] = e < a.E ? pad / a.mrows : 0;
-  __syncthreads();
-  if (e == 0) {
-    int acc = 0, tacc = 0;
-    for (int i = 0; i < a.E; ++i) {
-      int p = padded[i], tc = tcount[i];
-      padded[i] = acc; tcount[i] = tacc;
-      acc += p; tacc += tc;
-    }
-    a.seg_off[a.E] = acc;
-    *a.n_tiles = tacc;
-  }
-  __syncthreads();
-  if (e >= a.E) return;
-  const int off = padded[e];
-  a.seg_off[e] = off;
-  int t0 = tcount[e];
-  for (int i = 0; i * a.mrows < total; ++i) {
-    int32_t* tl = a.tiles + 4 * (int64_t)(t0 + i);
-    tl[0] = e;
-    tl[1] = off + i * a.mrows;
-    tl[2] = min(a.mrows, total - i * a.mrows);
-    tl[3] = 0;
-  }
-  for (int r = off + total; r < off + pad; ++r) a.row_map[r] = -1;
-}
-
-__global__ __launch_bounds__(256) void k_route_place(RouteArgs a) {
-  __shared__ int32_t ex[ROUTE_BLK];
-  const int b = blockIdx.x;
-  const int n = a.T * a.k;
-  const int beg = b * ROUTE_BLK, cnt = min(ROUTE_BLK, n - beg);
-  for (int i = threadIdx.x; i < cnt; i += 256) ex[i] = a.topk_id[beg + i];
-  __syncthreads();
-  const int e = threadIdx.x;
-  if (e >= a.E) return;
-  int slot = a.seg_off[e] + a.blk_cnt[(int64_t)b * a.E + e];
-  for (int i = 0; i < cnt; ++i) {
-    if (ex[i] == e) {
-      const int asg = beg + i;
-      a.slot[asg] = slot;
-      a.row_map[slot] = asg / a.k;
-      ++slot;
-    }
-  }
+// one assignment per thread: slot = segment base + block base + rank
+__global__ __launch_bounds__(ROUTE_BLK) void k_route_place(RouteArgs a) {
+  const int b = blockIdx.x, n = a.T * a.k;
+  const int i = b * ROUTE_BLK + threadIdx.x;
+  if (i >= n) return;
+  const int e = a.topk_id[i];
+  if (e < 0 || e >= a.E) return;
+  const int slot = a.seg_off[e] + a.blk_cnt[(int64_t)b * a.E + e] + a.slot[i];
+  a.slot[i] = slot;
+  a.row_map[slot] = i / a.k;
 }
 
 void launch_route(const RouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
-  const int ng = (a.T * a.k + RG - 1) / RG;
-  if (ng <= 256 && ng * a.E <= ROUTE_ONE_CNT) {
-    hipLaunchKernelGGL(k_route_one, dim3(1), dim3(256), 0, s, a);
+  if (a.E <= 128) hipLaunchKernelGGL(k_topk<8>, dim3((a.T + 15) / 16), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_topk<16>, dim3((a.T + 15) / 16), dim3(256), 0, s, a);
+  if (a.T * a.k <= ROUTE_ONE_MAX) {
+    hipLaunchKernelGGL(k_route_one, dim3(1), dim3(1024), 0, s, a);
     return;
   }
   const int n_blk = (a.T * a.k + ROUTE_BLK - 1) / ROUTE_BLK;
-  hipLaunchKernelGGL(k_route_count, dim3(n_blk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route_count, dim3(n_blk), dim3(ROUTE_BLK), 0, s, a);
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, s, a, n_blk);
-  hipLaunchKernelGGL(k_route_place, dim3(n_blk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route_place, dim3(n_blk), dim3(ROUTE_BLK), 0, s, a);
 }
 
 // h[t] += sum_j gate[t][j] * Y[slot[t][j]]   (j in order: deterministic)
