@@ -191,32 +191,45 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   };
   // Stage st's loads are issued two stages ahead.  At the top of stage st the
   // wave waits until only stage st+1's loads are outstanding (loads complete
-  // in order), then the barrier makes every wave's activation copies of stage
-  // st visible; the copy into the buffer of stage st+2 is issued only after
-  // that barrier, when every wave is done with stage st-1, its last reader.
-  // Every stage issues its loads, past the end too (their k-tiles clamp to
-  // the last one and land in a buffer no later stage reads): with the same
-  // loads in flight on every path the compiler's own waits before the MFMAs
-  // stay at this stage's loads instead of draining the prefetch.
-  auto step = [&](u32x4 (&ww)[NTW][U], int st) {
-    wait_vmcnt<LPS>();
+  // in order; at the last stage, until none are), then the barrier makes
+  // every wave's activation copies of stage st visible; the copy into the
+  // buffer of stage st+2 is issued only after that barrier, when every wave
+  // is done with stage st-1, its last reader.  Inside the loop every stage
+  // issues (the stages it issues exist), so the same loads are in flight on
+  // every path and the compiler's own waits before the MFMAs stay at this
+  // stage's loads instead of draining the prefetch; the last two or three
+  // stages are peeled off.
+  auto step = [&](u32x4 (&ww)[NTW][U], int st, bool more, bool next) {
+    if (next) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (st < nst) compute(ww, st);
+    compute(ww, st);
     __builtin_amdgcn_sched_barrier(0);
-    issue(ww, st + 2);
+    if (more) issue(ww, st + 2);
     __builtin_amdgcn_sched_barrier(0);
   };
   if (nst > 0) {
     issue(wA, 0);
     __builtin_amdgcn_sched_barrier(0);
-    issue(wB, 1);
+    issue(wB, 1);   // with a single stage its k-tiles clamp to the last one (unused)
     __builtin_amdgcn_sched_barrier(0);
-    for (int st = 0; st < nst; st += 2) {
-      step(wA, st);
-      step(wB, st + 1);
+    int st = 0;
+    for (; st + 3 < nst; st += 2) {
+      step(wA, st, true, true);
+      step(wB, st + 1, true, true);
     }
-    wait_vmcnt<0>();   // no copy into LDS may be in flight when the wave moves on
+    const int left = nst - st;   // 1, 2 or 3 stages; st and st+1 already issued
+    if (left == 3) {
+      step(wA, st, true, true);
+      step(wB, st + 1, false, true);
+      step(wA, st + 2, false, false);
+    } else if (left == 2) {
+      step(wA, st, false, true);
+      step(wB, st + 1, false, false);
+    } else {
+      step(wA, st, false, false);
+    }
   }
   if (!active) return;
 
