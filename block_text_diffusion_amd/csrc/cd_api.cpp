@@ -397,7 +397,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
   ns = std::min(ns, std::max(1, (nkeys_max + 2 * ATT_KB - 1) / (2 * ATT_KB)));
   at.split_len = (int)round_up((nkeys_max + ns - 1) / ns, ATT_KB);
   at.n_split = (nkeys_max + at.split_len - 1) / at.split_len;
-  at.part_o = c->st<float>(p.part_o);
+  at.part_o = c->st<void>(p.part_o);
   at.part_ml = c->st<float>(p.part_ml);
 
   { PROF(CD_PROF_EMBED); launch_embed(p.wdt_other, c->W + p.embed, ids, T, g.vocab, d, h, s); }

@@ -24,8 +24,8 @@
 //  * O^T += V^T P^T on MFMA; V is cached transposed ([dh][ctx]) so its
 //    fragments are contiguous in the key index.
 // With one key split the kernel normalises and writes O itself; otherwise
-// each split writes an unnormalised partial (O, max, sum) and a merge kernel
-// combines them.
+// each split writes an unnormalised partial (O in the activation type, max
+// and sum in fp32) and a merge kernel combines them in fp32.
 #include "common.h"
 #include "kernels.h"
 
@@ -303,11 +303,19 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
       continue;
     }
     const int64_t base = (((int64_t)s * rows_total + row) * a.Hq + h);
-    float* po = a.part_o + base * DH;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-      *reinterpret_cast<float4*>(po + dt * 16 + (lane >> 4) * 4) =
-          make_float4(o[qt][dt][0], o[qt][dt][1], o[qt][dt][2], o[qt][dt][3]);
+    for (int dt = 0; dt < ND; ++dt) {
+      const int64_t e = base * DH + dt * 16 + (lane >> 4) * 4;
+      if constexpr (AT == DT_F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.part_o) + e) =
+            make_float4(o[qt][dt][0], o[qt][dt][1], o[qt][dt][2], o[qt][dt][3]);
+      } else {   // the partials of the bf16 path are kept in bf16 as well
+        uint2 pk;
+        pk.x = pack_bf16(o[qt][dt][0], o[qt][dt][1]);
+        pk.y = pack_bf16(o[qt][dt][2], o[qt][dt][3]);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.part_o) + e) = pk;
+      }
+    }
     if ((lane >> 4) == 0) {
       a.part_ml[base * 2] = m[qt];
       a.part_ml[base * 2 + 1] = l[qt];
@@ -330,16 +338,23 @@ __global__ __launch_bounds__(256) void k_attn_merge(const AttnArgs a, int dh) {
   const int h = idx / dh, d = idx % dh;
   float ms[MS], ls[MS];
   float4 os[MS];
+  // no load is conditional: splits past n_split re-read the last one (their
+  // values are then dropped), so all of them are in flight at once
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
-    if (s < a.n_split) {
-      const int64_t base = ((int64_t)s * rows_total + row) * a.Hq + h;
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + base * 2);
-      ms[s] = ml.x; ls[s] = ml.y;
-      os[s] = *reinterpret_cast<const float4*>(a.part_o + base * dh + d);
+    const int64_t base = ((int64_t)min(s, a.n_split - 1) * rows_total + row) * a.Hq + h;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + base * 2);
+    float4 ov;
+    if constexpr (AT == DT_F32) {
+      ov = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.part_o) + base * dh + d);
     } else {
-      ms[s] = -INFINITY; ls[s] = 0.f; os[s] = make_float4(0, 0, 0, 0);
+      const uint2 pk = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.part_o) + base * dh + d);
+      ov = make_float4(bf2f(pk.x & 0xFFFF), bf2f(pk.x >> 16), bf2f(pk.y & 0xFFFF), bf2f(pk.y >> 16));
     }
+    const bool live = s < a.n_split;
+    ms[s] = live ? ml.x : -INFINITY;
+    ls[s] = live ? ml.y : 0.f;
+    os[s] = live ? ov : make_float4(0, 0, 0, 0);
   }
   float M = -INFINITY;
 #pragma unroll

@@ -20,24 +20,18 @@ void launch_embed(int edt, const void* E, const int32_t* ids, int T, int V, int 
   hipLaunchKernelGGL(k_embed, dim3(T), dim3(256), 0, s, edt, E, ids, V, d, h);
 }
 
-// u = h / sqrt(mean(h^2) + eps), one workgroup per row
+// u = h / sqrt(mean(h^2) + eps), one wave per row (four rows per workgroup).
+// Rows of up to 4096 values stay in registers between the sum of squares and
+// the scaling: every load of the row is issued before the first use, at
+// clamped addresses so none of them is conditional.
 template <int AT>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int d, float eps, void* u) {
-  __shared__ float sh[4];
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int T, int d, float eps, void* u) {
+  constexpr int NV = 16;   // float4 per lane held in registers
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
   const float* x = h + (int64_t)t * d;
-  float ss = 0.f;
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    float4 v = *reinterpret_cast<const float4*>(x + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = sh[0] + sh[1] + sh[2] + sh[3];
-  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    float4 v = *reinterpret_cast<const float4*>(x + c);
+  auto put = [&](int c, float4 v, float inv) {
     if constexpr (AT == DT_F32) {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(u) + (int64_t)t * d + c) =
           make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
@@ -47,11 +41,34 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int d, float ep
       p.y = pack_bf16(v.z * inv, v.w * inv);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(u) + (int64_t)t * d + c) = p;
     }
+  };
+  float ss = 0.f;
+  if (d <= 256 * NV) {
+    float4 v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = *reinterpret_cast<const float4*>(x + min((lane + 64 * j) * 4, d - 4));
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if ((lane + 64 * j) * 4 < d) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if ((lane + 64 * j) * 4 < d) put((lane + 64 * j) * 4, v[j], inv);
+  } else {
+    for (int c = lane * 4; c < d; c += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(x + c);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane * 4; c < d; c += 256) put(c, *reinterpret_cast<const float4*>(x + c), inv);
   }
 }
 void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s) {
-  if (adt == DT_F32) hipLaunchKernelGGL(k_rmsnorm<DT_F32>, dim3(T), dim3(256), 0, s, h, d, eps, u);
-  else hipLaunchKernelGGL(k_rmsnorm<DT_BF16>, dim3(T), dim3(256), 0, s, h, d, eps, u);
+  const dim3 grid((T + 3) / 4);
+  if (adt == DT_F32) hipLaunchKernelGGL(k_rmsnorm<DT_F32>, grid, dim3(256), 0, s, h, T, d, eps, u);
+  else hipLaunchKernelGGL(k_rmsnorm<DT_BF16>, grid, dim3(256), 0, s, h, T, d, eps, u);
 }
 
 // cs[pos][i] = (cos, sin)(pos * theta^(-2i/dh)), computed in fp64

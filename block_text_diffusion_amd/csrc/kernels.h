@@ -67,7 +67,7 @@ struct GemmArgs {
 };
 
 void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
-// dense, M <= 256, activations staged in LDS (a.ksplit > 1: EPI_F32 partials)
+// 256-row work items, activations staged in LDS (a.ksplit > 1: EPI_F32 partials)
 void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s);
 // ---- weight synthesis / packing --------------------------------------------
 struct PackDesc {
@@ -104,7 +104,8 @@ struct AttnArgs {
   int pos0_stride;
   int causal;             // 0: keys [0, pos0+rows) all visible; 1: key <= query pos
   int n_split, split_len; // key range split
-  float* part_o;          // [n_split][rows_total][Hq][dh] f32
+  void* part_o;           // [n_split][rows_total][Hq][dh] unnormalised partial O: f32, or bf16
+                          // when the activations are bf16
   float* part_ml;         // [n_split][rows_total][Hq][2] f32
   int q_blocks;           // query blocks of ATT_QR/(Hq/Hkv) tokens per request
 };
