@@ -360,25 +360,41 @@ void launch_route(const RouteArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_route_place, dim3(n_blk), dim3(ROUTE_BLK), 0, s, a);
 }
 
-// h[t] += sum_j gate[t][j] * Y[slot[t][j]]   (j in order: deterministic)
+// h[t] += sum_j gate[t][j] * Y[slot[t][j]]   (j in order: deterministic).
+// A token's gates and slots (k <= 16) are loaded once, and the k expert rows
+// of a column group in batches of 8 before any is added, so the loads overlap.
 template <int AT>
 __global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* slot, const float* gate, int k,
                                                  int d, float* h) {
   const int t = blockIdx.x;
+  float g[16];
+  int64_t yr[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int jc = min(j, k - 1);
+    g[j] = gate[(int64_t)t * k + jc];
+    yr[j] = slot[(int64_t)t * k + jc];
+  }
   for (int c = threadIdx.x * 4; c < d; c += 1024) {
     float4 acc = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
-    for (int j = 0; j < k; ++j) {
-      const float g = gate[(int64_t)t * k + j];
-      const int64_t row = slot[(int64_t)t * k + j];
-      float y0, y1, y2, y3;
-      if constexpr (AT == DT_F32) {
-        float4 y = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Yp) + row * d + c);
-        y0 = y.x; y1 = y.y; y2 = y.z; y3 = y.w;
-      } else {
-        uint2 y = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Yp) + row * d + c);
-        y0 = bf2f(y.x & 0xFFFF); y1 = bf2f(y.x >> 16); y2 = bf2f(y.y & 0xFFFF); y3 = bf2f(y.y >> 16);
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += 8) {
+      if (j0 >= k) break;
+      float4 y[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if constexpr (AT == DT_F32) {
+          y[q] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Yp) + yr[j0 + q] * d + c);
+        } else {
+          const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Yp) + yr[j0 + q] * d + c);
+          y[q] = make_float4(bf2f(b.x & 0xFFFF), bf2f(b.x >> 16), bf2f(b.y & 0xFFFF), bf2f(b.y >> 16));
+        }
       }
-      acc.x += g * y0; acc.y += g * y1; acc.z += g * y2; acc.w += g * y3;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j0 + q < k) {
+          acc.x += g[j0 + q] * y[q].x; acc.y += g[j0 + q] * y[q].y; acc.z += g[j0 + q] * y[q].z; acc.w += g[j0 + q] * y[q].w;
+        }
     }
     *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = acc;
   }
