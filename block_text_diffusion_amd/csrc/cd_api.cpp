@@ -74,7 +74,7 @@ struct Plan {
   int64_t weights_bytes;
   // state
   int64_t rq, canvas, argmax, lock, entropy, pmax, info, h, u, q, o, part_o, part_ml, rlog, topk_id,
-      topk_gate, blk_cnt, seg_off, row_map, slot, tiles, n_tiles, aperm, yperm, sact, logits, spart, rope,
+      topk_gate, blk_cnt, seg_off, row_map, slot, tiles, n_tiles, aperm, yperm, sact, sout, logits, spart, rope,
       kcache, vcache, zero;
   int64_t max_rows, max_tiles, n_blk_max, n_chunks;
   int64_t kv_req_stride, kv_layer_stride;   // elements
@@ -191,6 +191,7 @@ Plan make_plan(const cd_config& c) {
   p.aperm = s.take((int64_t)ae * p.max_rows * c.expert_hidden);
   p.yperm = s.take((int64_t)ae * p.max_rows * d);
   p.sact = s.take((int64_t)ae * T * std::max(c.shared_hidden, 1));
+  p.sout = s.take(4LL * T * (c.shared_hidden ? d : 1));
   p.logits = s.take(4LL * R * C * c.vocab);
   p.spart = s.take(16LL * R * C * p.n_chunks);
   p.rope = s.take(8LL * p.ctx * (dh / 2));
@@ -325,7 +326,7 @@ void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_
   // items to fill the chip; the expert-combining epilogue gathers 8 rows per
   // output and prefers the many workgroups of the row-tiled kernel
   const int64_t x_items = (int64_t)((M + 255) / 256) * ((a.Nt + 15) / 16);
-  const bool lds_staged = a.ksplit <= 1 && epi != EPI_RESID_MOE && ((M > 256 && x_items >= 256) || a.n_chunks >= 512);
+  const bool lds_staged = a.ksplit <= 1 && ((M > 256 && x_items >= 256) || a.n_chunks >= 512);
   if (lds_staged) {
     a.M = M;
     a.tiles = nullptr;
@@ -425,9 +426,10 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
     { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
-    // The shared FFN's gate/up projection depends only on u: it runs on the
-    // side stream while the router, the routing and the expert GEMMs (mostly
-    // latency-bound at the canvas batch) run here.
+    // The shared FFN depends only on u: both its projections run on the side
+    // stream (its fp32 output rows go to a buffer of their own) while the
+    // router, the routing and the expert GEMMs run here; the combine then adds
+    // the routed experts and the shared FFN into the residual.
     const bool fork = g.shared_hidden && ensure_side(c);
     if (g.shared_hidden) {
       hipStream_t ss = fork ? c->side : s;
@@ -438,6 +440,9 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       GemmArgs a = gemm_base(u, d, c->W + lw.sgu, nullptr, d, p.sgu_npad, 2 * g.shared_hidden,
                              c->st<void>(p.sact), g.shared_hidden);
       { Prof pg(c, CD_PROF_SHARED_GU, ss); gemm_dense(c, p.wdt_other, EPI_SWIGLU, a, T, ss); }
+      GemmArgs b = gemm_base(c->st<void>(p.sact), g.shared_hidden, c->W + lw.sdn, nullptr, g.shared_hidden,
+                             p.sdn_npad, d, c->st<float>(p.sout), d);
+      { Prof pd(c, CD_PROF_SHARED_DOWN, ss); gemm_dense(c, p.wdt_other, EPI_F32, b, T, ss); }
       if (fork) hipEventRecord(c->ev_join, c->side);
     }
     // router logits as fp32 partial sums over a split contraction (the
@@ -480,25 +485,12 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       PROF(CD_PROF_EXPERT_DOWN);
       gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, s);
     }
-    // At canvas-batch sizes the shared FFN's down projection also adds the
-    // routed experts' outputs (the combine step) into the residual, saving a
-    // launch; for thousands of rows the separate combine kernel gathers the
-    // expert rows more efficiently than the GEMM epilogue.
-    const bool fuse_combine = g.shared_hidden && T <= 1024;
-    if (!fuse_combine) {
+    // h += sum_j gate_j * y_j (choice order) + shared FFN row
+    if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
+    {
       PROF(CD_PROF_COMBINE);
-      launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate), T, k, d, h, s);
-    }
-    if (g.shared_hidden) {
-      if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
-      GemmArgs b = gemm_base(c->st<void>(p.sact), g.shared_hidden, c->W + lw.sdn, nullptr, g.shared_hidden,
-                             p.sdn_npad, d, h, d);
-      if (fuse_combine) {
-        b.moe_y = c->st<void>(p.yperm); b.moe_slot = c->st<int32_t>(p.slot); b.moe_gate = c->st<float>(p.topk_gate);
-        b.moe_k = k; b.moe_ld = d;
-      }
-      PROF(CD_PROF_SHARED_DOWN);
-      gemm_dense(c, p.wdt_other, fuse_combine ? EPI_RESID_MOE : EPI_RESID, b, T, s);
+      launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate),
+                     g.shared_hidden ? c->st<float>(p.sout) : nullptr, T, k, d, h, s);
     }
   }
   if (head) {

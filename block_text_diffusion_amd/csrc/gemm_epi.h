@@ -94,41 +94,6 @@ __device__ __forceinline__ void epi_store(const GemmArgs& a, const float* sc, in
     float4 o = *p;
     o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
     *p = o;
-  } else if constexpr (EPI == EPI_RESID_MOE) {
-    // residual + routed experts (in slot order) + this GEMM (the shared FFN)
-    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.Y) + (int64_t)row * a.ldy + n);
-    float4 o = *p;
-    const int64_t tk = (int64_t)row * a.moe_k;
-    // the choices go in batches of 8: all gates and slots of a batch, then all
-    // its expert rows, are loaded before the first use (indices clamped to the
-    // last choice, whose repeats are not added), then added in choice order
-    for (int j0 = 0; j0 < a.moe_k; j0 += 8) {
-      float g[8];
-      int64_t yr[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = min(j0 + q, a.moe_k - 1);
-        g[q] = a.moe_gate[tk + j];
-        yr[q] = a.moe_slot[tk + j];
-      }
-      float4 y[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if constexpr (AT == DT_F32) {
-          y[q] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.moe_y) + yr[q] * a.moe_ld + n);
-        } else {
-          const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.moe_y) + yr[q] * a.moe_ld + n);
-          y[q] = make_float4(bf2f(b.x & 0xFFFF), bf2f(b.x >> 16), bf2f(b.y & 0xFFFF), bf2f(b.y >> 16));
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (j0 + q < a.moe_k) {
-          o.x += g[q] * y[q].x; o.y += g[q] * y[q].y; o.z += g[q] * y[q].z; o.w += g[q] * y[q].w;
-        }
-    }
-    o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
-    *p = o;
   } else if constexpr (EPI == EPI_QKV) {
     const int dh = a.dh, half = dh >> 1;
     const int req = row / a.rows_per_req;

@@ -282,7 +282,6 @@ static void run_epi(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_RESID: run_nw<WT, AT, MT, EPI_RESID>(a, s); break;
     case EPI_SWIGLU: run_nw<WT, AT, MT, EPI_SWIGLU>(a, s); break;
     case EPI_QKV: run_nw<WT, AT, MT, EPI_QKV>(a, s); break;
-    case EPI_RESID_MOE: run_nw<WT, AT, MT, EPI_RESID_MOE>(a, s); break;
   }
 }
 

@@ -249,7 +249,6 @@ static void run_x_epi(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_SWIGLU: run_x<WT, AT, EPI_SWIGLU>(a, s); break;
     case EPI_QKV: run_x<WT, AT, EPI_QKV>(a, s); break;
     case EPI_ROWS: run_x<WT, AT, EPI_ROWS>(a, s); break;
-    case EPI_RESID_MOE: run_x<WT, AT, EPI_RESID_MOE>(a, s); break;
   }
 }
 

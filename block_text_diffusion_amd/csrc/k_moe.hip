@@ -360,12 +360,13 @@ void launch_route(const RouteArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_route_place, dim3(n_blk), dim3(ROUTE_BLK), 0, s, a);
 }
 
-// h[t] += sum_j gate[t][j] * Y[slot[t][j]]   (j in order: deterministic).
-// A token's gates and slots (k <= 16) are loaded once, and the k expert rows
-// of a column group in batches of 8 before any is added, so the loads overlap.
+// h[t] += sum_j gate[t][j] * Y[slot[t][j]] (j in order: deterministic), then
+// + add[t] (the shared FFN's fp32 row) when given.  A token's gates and slots
+// (k <= 16) are loaded once, and the k expert rows of a column group in
+// batches of 8 before any is added, so the loads overlap.
 template <int AT>
-__global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* slot, const float* gate, int k,
-                                                 int d, float* h) {
+__global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* slot, const float* gate,
+                                                 const float* add, int k, int d, float* h) {
   const int t = blockIdx.x;
   float g[16];
   int64_t yr[16];
@@ -396,14 +397,18 @@ __global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* 
           acc.x += g[j0 + q] * y[q].x; acc.y += g[j0 + q] * y[q].y; acc.z += g[j0 + q] * y[q].z; acc.w += g[j0 + q] * y[q].w;
         }
     }
+    if (add) {
+      const float4 v = *reinterpret_cast<const float4*>(add + (int64_t)t * d + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
     *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = acc;
   }
 }
 
-void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, int T, int k, int d, float* h,
-                    hipStream_t s) {
-  if (adt == DT_F32) hipLaunchKernelGGL(k_combine<DT_F32>, dim3(T), dim3(256), 0, s, Yp, slot, gate, k, d, h);
-  else hipLaunchKernelGGL(k_combine<DT_BF16>, dim3(T), dim3(256), 0, s, Yp, slot, gate, k, d, h);
+void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k,
+                    int d, float* h, hipStream_t s) {
+  if (adt == DT_F32) hipLaunchKernelGGL(k_combine<DT_F32>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h);
+  else hipLaunchKernelGGL(k_combine<DT_BF16>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h);
 }
 
 }  // namespace cd

@@ -24,7 +24,7 @@ __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + 
 // Row permutations applied when packing.
 enum { PERM_NONE = 0, PERM_QKV = 1, PERM_GU = 2 };
 
-enum { EPI_F32 = 0, EPI_ROWS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4, EPI_RESID_MOE = 5 };
+enum { EPI_F32 = 0, EPI_ROWS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
 
 struct GemmArgs {
   // activations: row-major [rows][ldx], element type = act dtype
@@ -57,13 +57,6 @@ struct GemmArgs {
   const int32_t* pos0;     // per request: position of its row 0
   int pos0_stride;         // int32 stride between requests in pos0
   const float* rope_cs;    // [max_ctx][dh/2] (cos, sin) pairs, or null
-  // EPI_RESID_MOE: the routed experts' outputs are added with the residual,
-  // h[row] += sum_j gate[row][j] * moe_y[slot[row][j]] + this GEMM's row
-  const void* moe_y;       // [T*k][moe_ld] act
-  const int32_t* moe_slot; // [T][k]
-  const float* moe_gate;   // [T][k]
-  int moe_k;
-  int64_t moe_ld;
 };
 
 void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
@@ -136,7 +129,8 @@ void launch_route(const RouteArgs& a, hipStream_t s);
 void launch_embed(int edt, const void* E, const int32_t* ids, int T, int V, int d, float* h, hipStream_t s);
 void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s);
 void launch_rope_table(float* cs, int max_ctx, int dh, float theta, hipStream_t s);
-void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, int T, int k,
+// h[t] += sum_j gate[t][j] * Yp[slot[t][j]] (choice order) + add[t] (fp32 row, or null)
+void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k,
                     int d, float* h, hipStream_t s);
 void launch_attn_merge(int adt, const AttnArgs& a, hipStream_t s);
 void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
