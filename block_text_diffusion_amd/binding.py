@@ -29,7 +29,8 @@ class cd_config(ctypes.Structure):
         "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
         "expert_hidden", "shared_hidden", "vocab", "canvas_len", "max_steps")] + [
         (n, c_float) for n in ("lock_threshold", "stop_entropy", "rms_eps", "rope_theta")] + [
-        (n, c_int32) for n in ("weight_dtype", "max_requests", "max_ctx", "max_prefill")]
+        (n, c_int32) for n in ("weight_dtype", "max_requests", "max_ctx", "max_prefill")] + [
+        ("attn_rescale_log2", c_float)]
 
 
 class cd_step_info(ctypes.Structure):
@@ -134,7 +135,7 @@ def make_config(w: dict, max_requests=None, max_ctx=None, max_prefill=None) -> c
         canvas_len=w["C"], max_steps=w["max_steps"], lock_threshold=w["lock"], stop_entropy=w["stop_H"],
         rms_eps=w["eps"], rope_theta=w["theta"], weight_dtype=dt, max_requests=R,
         max_ctx=max_ctx or (P0 + w.get("blocks", 1) * w["C"]),
-        max_prefill=max_prefill or max(P0, 1))
+        max_prefill=max_prefill or max(P0, 1), attn_rescale_log2=w.get("attn_rescale_log2", 0.0))
 
 
 def cd_weights_bytes(cfg):

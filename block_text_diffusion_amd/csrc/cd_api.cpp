@@ -101,6 +101,8 @@ int32_t validate_config(const cd_config* c) {
   if (!(c->lock_threshold >= 0.f && c->lock_threshold <= 1.f) || !(c->stop_entropy >= 0.f) || !(c->rms_eps >= 0.f) ||
       !(c->rope_theta >= 0.f))
     return fail(CD_ERR_INVALID_ARG, "bad sampler/norm constants");
+  if (!(c->attn_rescale_log2 >= 0.f && c->attn_rescale_log2 <= 64.f))
+    return fail(CD_ERR_INVALID_ARG, "attn_rescale_log2 must lie in [0, 64]");
   return CD_OK;
 }
 
@@ -389,6 +391,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
   at.rows_per_req = rows_per_req; at.n_req = n_req;
   at.pos0 = pos0; at.pos0_stride = pos_stride;
   at.causal = causal ? 1 : 0;
+  at.rescale_log2 = g.attn_rescale_log2 > 0.f ? g.attn_rescale_log2 : 8.0f;
   at.q_blocks = (rows_per_req + TB - 1) / TB;
   // key splits: enough work items for one per CU, each split at least two
   // 64-key blocks

@@ -26,6 +26,8 @@
 // With one key split the kernel normalises and writes O itself; otherwise
 // each split writes an unnormalised partial (O in the activation type, max
 // and sum in fp32) and a merge kernel combines them in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -50,7 +52,10 @@ struct AttnShape {
   static constexpr int FPW = NF / NW;                   // fragments each wave copies
   static constexpr int STAGE = NF * 1024;
   static constexpr int NBUF = (STAGE * 4 <= 128 * 1024) ? 4 : 2;
-  static constexpr int DIST = NBUF - 1;
+  // staggered halves (below) need a buffer between the one being copied and
+  // the one the late half still reads
+  static constexpr bool PP = NBUF >= 4;
+  static constexpr int DIST = PP ? NBUF - 2 : NBUF - 1;
   static_assert(NF % NW == 0 && NW * QTW * 16 == ATT_QR, "work split");
 };
 
@@ -142,36 +147,58 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
   }
 
   const float sl2 = 1.4426950408889634f / sqrtf((float)DH);
-  float m[QTW], l[QTW];
+  // Lazy rescaling.  Scores are taken relative to a per-row reference mref
+  // (raw score units; equal in the four lanes that hold a query's keys), which
+  // enters as the initial value of the score accumulators, so the MFMAs return
+  // s - mref.  The reference moves only when a score of the block exceeds it by
+  // more than tau / sl2 (every p = 2^(sl2 (s - mref)) stays below 2^tau), so a
+  // typical block needs no cross-lane maximum and no rescale of O.  O and the
+  // row sum l always share the reference, so the result is exact up to
+  // rounding for any reference.
+  const float tau_raw = a.rescale_log2 / sl2;
+  float mref[QTW];      // -inf until the row has seen a visible key
   f32x4 o[QTW][ND];
+  f32x4 lacc[QTW];      // bf16: row sums from an MFMA with a ones operand (all four equal);
+                        // f32: this lane's partial sum in [0]
 #pragma unroll
   for (int qt = 0; qt < QTW; ++qt) {
-    m[qt] = -INFINITY; l[qt] = 0.f;
+    mref[qt] = -INFINITY;
+    lacc[qt] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) o[qt][dt] = f32x4{0, 0, 0, 0};
   }
 
-  if (nblk > 0) {
-#pragma unroll
-    for (int j = 0; j < DIST; ++j) issue(j);
-  }
-  for (int b = 0; b < nblk; ++b) {
-    // block b has landed for this wave; after the barrier for all waves, and
-    // every wave is done with block b-1, whose buffer the next copy reuses
-    wait_vmcnt<(DIST - 1) * FPW>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue(b + DIST);
-    __builtin_amdgcn_sched_barrier(0);
+  // The work on one key block comes in three phases: scores (MFMA), softmax
+  // (VALU), and the O update (MFMA).
+  f32x4 sacc[4][QTW];   // S^T[st][qt] - mref: keys of subtile st x query tile qt; then P^T
+  u32x4 pf[QTW][2];     // P^T in bf16 (bf16 path)
+
+  // Masked keys (past the end of the range, or after the query under the
+  // causal mask) start at -inf, so they leave the MFMA as -inf and exp2 turns
+  // them into 0.  Blocks whose keys are all visible to every row of the wave
+  // take the unmasked variant.
+  auto scores = [&](int b, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const uint8_t* buf = lds + (b % NBUF) * STAGE + lane * 16;
     const int kb0 = kbeg + b * ATT_KB;
-
-    // S^T[st][qt]: keys of subtile st x query tile qt
-    f32x4 sacc[4][QTW];
+    float base[QTW];
+#pragma unroll
+    for (int qt = 0; qt < QTW; ++qt) base[qt] = mref[qt] == -INFINITY ? 0.f : -mref[qt];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
-      for (int qt = 0; qt < QTW; ++qt) sacc[st][qt] = f32x4{0, 0, 0, 0};
+      for (int qt = 0; qt < QTW; ++qt) {
+        if constexpr (MASKED) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int kidx = kb0 + 32 * (st >> 1) + 8 * (lane >> 4) + 4 * (st & 1) + q;
+            const bool ok = kidx < kend && (!a.causal || kidx <= qpos[qt]);
+            sacc[st][qt][q] = ok ? base[qt] : -INFINITY;
+          }
+        } else {
+          sacc[st][qt] = f32x4{base[qt], base[qt], base[qt], base[qt]};
+        }
+      }
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(buf + (st * NK + kk) * 1024);
@@ -189,58 +216,68 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
         }
       }
     }
-    // mask and online softmax (base 2); lane holds keys kb0 + 32c + 8*(lane/16) + 4*half + q.
-    // A block whose keys are all visible to every row of the wave skips the mask.
-    const bool full = kb0 + ATT_KB <= kend && (!a.causal || kb0 + ATT_KB - 1 <= pos0 + tok0);
+  };
+
+  // p = 2^(sl2 (s - mref)); lane holds keys kb0 + 32c + 8*(lane/16) + 4*half + q
+  auto softmax = [&]() {
 #pragma unroll
     for (int qt = 0; qt < QTW; ++qt) {
-      float mt = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) mt = fmaxf(mt, sacc[st][qt][q]);
-      } else {
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int kidx = kb0 + 32 * (st >> 1) + 8 * (lane >> 4) + 4 * (st & 1) + q;
-            const bool ok = kidx < kend && (!a.causal || kidx <= qpos[qt]);
-            const float v = ok ? sacc[st][qt][q] : -INFINITY;
-            sacc[st][qt][q] = v;
-            mt = fmaxf(mt, v);
-          }
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      // scores scale by sl2 > 0, so the scaled max is the max of the scaled scores
-      const float mn = fmaxf(m[qt], mt * sl2);
-      const float nmn = (mn == -INFINITY) ? 0.f : -mn;
-      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[qt] - mn);
-      float sum = 0.f;
+      float lm = sacc[0][qt][0];
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[st][qt][q], sl2, nmn));   // masked: exp2(-inf) = 0
-          sacc[st][qt][q] = e;
-          sum += e;
-        }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
-      l[qt] = l[qt] * alpha + sum;
-      m[qt] = mn;
-      // the running max of a row rarely moves once a few blocks are in: skip
-      // the (exact, times one) rescale when no row of the tile needs it
-      if (__ballot(alpha != 1.0f)) {
+        for (int q = 0; q < 4; ++q) lm = fmaxf(lm, sacc[st][qt][q]);
+      const bool first = mref[qt] == -INFINITY;
+      if (__ballot(first || lm > tau_raw)) {
+        // move the reference: to the row maximum on a row's first visible
+        // keys, else up by the excess of the row maximum over it (if any)
+        float rm = fmaxf(lm, __shfl_xor(lm, 16, 64));
+        rm = fmaxf(rm, __shfl_xor(rm, 32, 64));
+        const float sh = first ? (rm == -INFINITY ? 0.f : rm) : fmaxf(rm, 0.f);
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          o[qt][dt][0] *= alpha; o[qt][dt][1] *= alpha; o[qt][dt][2] *= alpha; o[qt][dt][3] *= alpha;
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sacc[st][qt][q] -= sh;
+        const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-sh * sl2);
+        mref[qt] = first ? (rm == -INFINITY ? -INFINITY : rm) : mref[qt] + sh;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            o[qt][dt][0] *= alpha; o[qt][dt][1] *= alpha; o[qt][dt][2] *= alpha; o[qt][dt][3] *= alpha;
+          }
+          lacc[qt][0] *= alpha; lacc[qt][1] *= alpha; lacc[qt][2] *= alpha; lacc[qt][3] *= alpha;
         }
       }
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sacc[st][qt][q] = __builtin_amdgcn_exp2f(sacc[st][qt][q] * sl2);   // -inf -> 0
+      if constexpr (AT == DT_F32) {
+        float sum = 0.f;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sum += sacc[st][qt][q];
+        lacc[qt][0] += sum;
+      }
     }
-    // O^T += V^T P^T
+    if constexpr (AT != DT_F32) {
+#pragma unroll
+      for (int qt = 0; qt < QTW; ++qt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          pf[qt][c][0] = pack_bf16(sacc[2 * c][qt][0], sacc[2 * c][qt][1]);
+          pf[qt][c][1] = pack_bf16(sacc[2 * c][qt][2], sacc[2 * c][qt][3]);
+          pf[qt][c][2] = pack_bf16(sacc[2 * c + 1][qt][0], sacc[2 * c + 1][qt][1]);
+          pf[qt][c][3] = pack_bf16(sacc[2 * c + 1][qt][2], sacc[2 * c + 1][qt][3]);
+        }
+    }
+  };
+
+  // O^T += V^T P^T; on the bf16 path also l += 1 P^T (the row sums of the
+  // bf16 weights that multiply V)
+  auto update = [&](int b) {
+    const uint8_t* buf = lds + (b % NBUF) * STAGE + lane * 16;
     if constexpr (AT == DT_F32) {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
@@ -254,16 +291,6 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
               o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vf[j]), sacc[st][qt][j], o[qt][dt], 0, 0, 0);
         }
     } else {
-      u32x4 pf[QTW][2];
-#pragma unroll
-      for (int qt = 0; qt < QTW; ++qt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          pf[qt][c][0] = pack_bf16(sacc[2 * c][qt][0], sacc[2 * c][qt][1]);
-          pf[qt][c][1] = pack_bf16(sacc[2 * c][qt][2], sacc[2 * c][qt][3]);
-          pf[qt][c][2] = pack_bf16(sacc[2 * c + 1][qt][0], sacc[2 * c + 1][qt][1]);
-          pf[qt][c][3] = pack_bf16(sacc[2 * c + 1][qt][2], sacc[2 * c + 1][qt][3]);
-        }
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -274,7 +301,72 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
             o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf),
                                                                 __builtin_bit_cast(bf16x8, pf[qt][c]), o[qt][dt], 0, 0, 0);
         }
+      const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+      for (int qt = 0; qt < QTW; ++qt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones),
+                                                             __builtin_bit_cast(bf16x8, pf[qt][c]), lacc[qt], 0, 0, 0);
     }
+  };
+
+  // scores and softmax of block b, masked only where needed
+  auto scores_softmax = [&](int b) {
+    const int kb0 = kbeg + b * ATT_KB;
+    const bool full = kb0 + ATT_KB <= kend && (!a.causal || kb0 + ATT_KB - 1 <= pos0 + tok0);
+    if (full) scores(b, std::integral_constant<bool, false>{});
+    else scores(b, std::integral_constant<bool, true>{});
+    softmax();
+  };
+
+  // Block b has landed for this wave; after the barrier it has for every
+  // wave, and no wave still reads the buffer that block b + DIST goes into.
+  auto sync_issue = [&](int b) {
+    wait_vmcnt<(DIST - 1) * FPW>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(b + DIST);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nblk > 0) {
+#pragma unroll
+    for (int j = 0; j < DIST; ++j) issue(j);
+    if (!S::PP || wave < S::NW / 2) {
+      for (int b = 0; b < nblk; ++b) {
+        sync_issue(b);
+        scores_softmax(b);
+        update(b);
+      }
+    } else {
+      // The second half of the waves runs half a block behind: it meets
+      // barrier b after the softmax of block b-1 and updates O with that
+      // block after the barrier.  Each SIMD holds one wave of each half, so
+      // one wave's softmax runs under the other's MFMAs.  The copy issued at
+      // barrier b overwrites block b-2's buffer, which the late waves left
+      // before barrier b.
+      sync_issue(0);
+      scores_softmax(0);
+      for (int b = 1; b < nblk; ++b) {
+        sync_issue(b);
+        update(b - 1);
+        scores_softmax(b);
+      }
+      update(nblk - 1);
+    }
+  }
+  // the row sum, and the reference in scaled (base-2) units for the merge
+  float l[QTW], m[QTW];
+#pragma unroll
+  for (int qt = 0; qt < QTW; ++qt) {
+    float sum = lacc[qt][0];
+    if constexpr (AT == DT_F32) {
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+    }
+    l[qt] = sum;
+    m[qt] = mref[qt] == -INFINITY ? -INFINITY : mref[qt] * sl2;
   }
   wait_vmcnt<0>();   // no copy into LDS may be in flight when the workgroup exits
 

@@ -96,6 +96,7 @@ struct AttnArgs {
   const int32_t* pos0;    // per-request position of row 0 (= committed length)
   int pos0_stride;
   int causal;             // 0: keys [0, pos0+rows) all visible; 1: key <= query pos
+  float rescale_log2;     // lazy softmax: the row reference moves when a score exceeds it by more (log2)
   int n_split, split_len; // key range split
   void* part_o;           // [n_split][rows_total][Hq][dh] unnormalised partial O: f32, or bf16
                           // when the activations are bf16

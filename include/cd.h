@@ -81,6 +81,9 @@ typedef struct cd_config {
   int32_t max_requests;   /* requests denoised together */
   int32_t max_ctx;        /* KV capacity per request, tokens */
   int32_t max_prefill;    /* largest single prefill call, tokens */
+  float attn_rescale_log2; /* attention softmax: the running row reference moves only when a
+                              score exceeds it by more than this many powers of two (the
+                              result is exact up to rounding for any value); 0 selects 8 */
 } cd_config;
 
 /* Per-request result of one denoise pass, written to device memory. */
