@@ -7,8 +7,9 @@
 // Work item = (request, KV head, block of 256 query rows, key split).  The
 // 256 query rows are the Hq/Hkv query heads that share one KV head times
 // 256/(Hq/Hkv) tokens, so every K/V byte feeds all heads of its group.  Each
-// of the 8 waves owns 32 query rows (two 16-row tiles); two waves share a
-// SIMD, so one's softmax (VALU, exp) overlaps the other's MFMAs.
+// of the 8 waves owns 32 query rows (two 16-row tiles); waves w and w+4 share
+// a SIMD, and the second half runs half a key block behind the first, so one
+// wave's softmax (VALU, exp) overlaps the other's MFMAs.
 //  * Keys go in blocks of 64.  The block's K tile and V^T tile are copied
 //    from global memory straight into LDS (global_load_lds, 16 bytes a lane),
 //    already cut into 1 KB MFMA operand fragments, shared by the 8 waves and
@@ -19,13 +20,16 @@
 //    The 16 key rows of a K fragment are taken in the order that leaves each
 //    lane holding 8 consecutive keys of a 32-key chunk, which is exactly the
 //    P^T operand of the next product, so P never leaves registers.
-//  * online softmax in base 2 with the 1/sqrt(dh) scale folded in; row max
-//    and sum reduce across the 4 lane groups with two xor shuffles;
+//  * softmax in base 2 against a per-row reference that starts the score
+//    accumulators and moves only when a score exceeds it by more than a
+//    threshold, so most blocks need neither a cross-lane maximum nor a
+//    rescale of O (lazy rescaling); masked keys start at -inf;
 //  * O^T += V^T P^T on MFMA; V is cached transposed ([dh][ctx]) so its
-//    fragments are contiguous in the key index.
+//    fragments are contiguous in the key index; on the bf16 path the row sums
+//    come from one more MFMA with an all-ones operand.
 // With one key split the kernel normalises and writes O itself; otherwise
-// each split writes an unnormalised partial (O in the activation type, max
-// and sum in fp32) and a merge kernel combines them in fp32.
+// each split writes an unnormalised partial (O in the activation type, its
+// reference and row sum in fp32) and a merge kernel combines them in fp32.
 #include <type_traits>
 
 #include "common.h"

@@ -9,13 +9,18 @@
 //    global memory straight into LDS with global_load_lds_dwordx4 -- each
 //    lane's 16 bytes land at the wave's LDS base + lane*16, which is exactly
 //    the fragment layout -- so staging costs no VGPRs;
+//  * bf16 and fp32 weights: the 16 weight fragments of the stage (256
+//    columns) are copied into LDS the same way, so the two row halves that
+//    use a weight tile share one global read of it; fp8 weights go straight
+//    into registers (a grouped fp8 launch shares a weight chunk between few
+//    row tiles, and there the extra LDS traffic cost more than it saved);
 //  * eight waves, two per SIMD: waves 0-3 take rows 0-127 and waves 4-7 rows
-//    128-255, each streaming four 16-column weight tiles into registers and
-//    reading its eight activation fragments of the stage from LDS (one
-//    contiguous, conflict-free 1 KB ds_read each);
-//  * activations and weights are both prefetched DIST stages ahead (LDS
-//    buffers and register slots), so the one in-order vmcnt counter covers
-//    both streams with a single wait per stage;
+//    128-255, each with four weight fragments and its eight activation
+//    fragments of the stage read from LDS (one contiguous, conflict-free 1 KB
+//    ds_read each);
+//  * activations and weights are both prefetched DIST stages ahead, so the
+//    one in-order vmcnt counter covers both streams with a single wait per
+//    stage;
 //  * fp8 weights are widened to bf16 once per stage for all row tiles;
 //  * the contraction can also be split into fp32 partials (EPI_F32 with
 //    ksplit > 1).
@@ -36,12 +41,16 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
   constexpr int XW = (WT == DT_FP8) ? 2 : 1;          // 1 KB activation fragments per k-tile and row tile
   constexpr int XSTEP = (WT == DT_FP8) ? 128 : 64;    // activation bytes per k-tile (per lane group)
-  constexpr int NBUF = (WT == DT_FP8) ? 2 : 4;
+  constexpr bool WLDS = WT != DT_FP8;                 // weights staged in LDS
+  constexpr int NBUF = WLDS ? 4 : 2;
   constexpr int DIST = NBUF - 1;
-  constexpr int BLK = XMT * XW;                       // fragments per stage
-  constexpr int BPW = BLK / XWAVES;                   // fragments each wave copies
-  constexpr int LPS = BPW + XNTW;                     // vector loads per wave per stage
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[NBUF][BLK * 1024];
+  constexpr int BLK = XMT * XW;                       // activation fragments per stage
+  constexpr int BPW = BLK / XWAVES;                   // activation fragments each wave copies
+  constexpr int WFR = WLDS ? 4 * XNTW : 0;            // weight fragments per stage in LDS (256 columns)
+  constexpr int WPW = WFR / XWAVES;                   // weight fragments each wave copies
+  constexpr int NWP = WLDS ? WPW : XNTW;              // weight streams of this wave
+  constexpr int LPS = BPW + NWP;                      // vector loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[NBUF][(BLK + WFR) * 1024];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -89,10 +98,14 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   // still copies activations and meets every barrier)
   const bool row_live = wm * XMTW * 16 < rows;
   const uint8_t* wbase = a.W + (int64_t)group * a.w_gstride;
-  const uint8_t* wp[XNTW];
+  // LDS-staged weights: this wave copies fragments wave*WPW.. of the
+  // chunk's 16 tiles; else it loads its own four tiles nt0.. into registers
+  const uint8_t* wp[NWP];
 #pragma unroll
-  for (int j = 0; j < XNTW; ++j)
-    wp[j] = wbase + ((int64_t)min(nt0 + j, a.Nt - 1) * KTall + kt0) * 1024 + lane * 16;
+  for (int j = 0; j < NWP; ++j) {
+    const int t = WLDS ? chunk * 4 * XNTW + wave * WPW + j : nt0 + j;
+    wp[j] = wbase + ((int64_t)min(t, a.Nt - 1) * KTall + kt0) * 1024 + lane * 16;
+  }
   // rows past the tile's end read its last row (finite); their results are dropped
   const uint8_t* xsrc[BPW];
 #pragma unroll
@@ -111,17 +124,24 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   for (int mt = 0; mt < XMTW; ++mt)
 #pragma unroll
     for (int j = 0; j < XNTW; ++j) acc[mt][j] = f32x4{0, 0, 0, 0};
-  u32x4 w[DIST][XNTW];
+  u32x4 w[WLDS ? 1 : DIST][XNTW];   // register weight stages (fp8)
 
   // stage indices past the end are clamped to the last stage: the copies
   // stay in bounds and land in buffers no later stage reads
-  auto issue_x = [&](int s) {
+  auto issue = [&](int s) {
     const int sc = min(s, nst - 1);
     uint8_t* dst = xs[s % NBUF] + wave * BPW * 1024;
 #pragma unroll
     for (int i = 0; i < BPW; ++i)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xsrc[i] + (int64_t)sc * XSTEP),
                                        (lds_void*)(dst + i * 1024), 16, 0, 0);
+    if constexpr (WLDS) {
+      uint8_t* wdst = xs[s % NBUF] + (BLK + wave * WPW) * 1024;
+#pragma unroll
+      for (int j = 0; j < WPW; ++j)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(wp[j] + (int64_t)sc * 1024),
+                                         (lds_void*)(wdst + j * 1024), 16, 0, 0);
+    }
   };
   auto issue_w = [&](u32x4 (&ww)[XNTW], int s) {
     const int sc = min(s, nst - 1);
@@ -131,7 +151,13 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   // all 16 row tiles are computed: rows past M hold copies of row M-1 (finite)
   // and their results are dropped, which keeps the loop free of branches
   // LDS fragment reads run one row tile ahead of the MFMAs that use them
-  auto compute = [&](const u32x4 (&ww)[XNTW], const uint8_t* buf) {
+  auto compute = [&](const u32x4 (&wr)[XNTW], const uint8_t* buf) {
+    u32x4 ww[XNTW];
+#pragma unroll
+    for (int j = 0; j < XNTW; ++j) {
+      if constexpr (WLDS) ww[j] = *reinterpret_cast<const u32x4*>(buf + ((BLK + wn * XNTW + j) * 64 + lane) * 16);
+      else ww[j] = wr[j];
+    }
     u32x4 xa[XW], xb[XW];
     auto rd = [&](u32x4 (&x)[XW], int mt) {
 #pragma unroll
@@ -170,10 +196,11 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
         for (int j = 0; j < XNTW; ++j) acc[mt + 1][j] = mma_tile<WT>(ww[j], xb, acc[mt + 1][j]);
       }
     }
-    // order: reads of tile 0, then (reads of tile mt+1, MFMAs of tile mt)
+    // order: weight reads and reads of tile 0, then (reads of tile mt+1,
+    // MFMAs of tile mt)
     constexpr int RD = XW;                                                     // DS reads per tile
     constexpr int MF = XNTW * (WT == DT_F32 ? 4 : (WT == DT_FP8 ? 2 : 1));     // MFMAs per tile
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, (WLDS ? XNTW : 0) + RD, 0);
 #pragma unroll
     for (int mt = 0; mt + 1 < XMTW; ++mt) {
       __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
@@ -184,8 +211,8 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
 
 #pragma unroll
   for (int j = 0; j < DIST; ++j) {
-    issue_x(j);
-    issue_w(w[j], j);
+    issue(j);
+    if constexpr (!WLDS) issue_w(w[j], j);
   }
   for (int s0 = 0; s0 < nst; s0 += DIST) {
 #pragma unroll
@@ -198,12 +225,14 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
       wait_vmcnt<(DIST - 1) * LPS>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      issue_x(s + DIST);
+      issue(s + DIST);
       __builtin_amdgcn_sched_barrier(0);
-      if (s < nst && row_live) compute(w[j], xs[s % NBUF]);
+      if (s < nst && row_live) compute(w[WLDS ? 0 : j], xs[s % NBUF]);
       __builtin_amdgcn_sched_barrier(0);
-      issue_w(w[j], s + DIST);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!WLDS) {
+        issue_w(w[j], s + DIST);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   wait_vmcnt<0>();   // no LDS copy may still be in flight when the workgroup exits
