@@ -418,6 +418,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       a.kc = kc; a.vc = vc; a.kv_req_stride = p.kv_req_stride;
       a.max_ctx = p.ctx; a.Hq = g.n_q_heads; a.Hkv = g.n_kv_heads; a.dh = dh;
       a.rows_per_req = rows_per_req; a.pos0 = pos0; a.pos0_stride = pos_stride; a.rope_cs = rope;
+      a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)dh));   // log2(e) / sqrt(dh)
       { PROF(CD_PROF_QKV); gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s); }
       at.kc = kc; at.vc = vc;
     }

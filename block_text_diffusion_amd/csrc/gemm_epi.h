@@ -113,9 +113,11 @@ __device__ __forceinline__ void epi_store(const GemmArgs& a, const float* sc, in
         x0 = rx0; y0 = ry0; x1 = rx1; y1 = ry1;
       }
       if (n < qdim) {
+        // queries leave scaled for a base-2 softmax (one rounding, as unscaled)
+        const float qs = a.q_scale;
         const int64_t base = (int64_t)row * a.ldy + head * dh;
-        store2<AT>(a.Y, base + i0, x0, x1);
-        store2<AT>(a.Y, base + i0 + half, y0, y1);
+        store2<AT>(a.Y, base + i0, x0 * qs, x1 * qs);
+        store2<AT>(a.Y, base + i0 + half, y0 * qs, y1 * qs);
       } else {
         const int64_t base = (int64_t)req * a.kv_req_stride + ((int64_t)head * a.max_ctx + pos) * dh;
         store2<AT>(a.kc, base + i0, x0, x1);

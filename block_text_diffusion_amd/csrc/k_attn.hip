@@ -150,16 +150,18 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
     for (int kk = 0; kk < NK; ++kk) qf[qt][kk] = ld16<AT>(a.Q, row * ld + h * DH + kk * KF + (lane >> 4) * KQ);
   }
 
-  const float sl2 = 1.4426950408889634f / sqrtf((float)DH);
+  // The queries arrive multiplied by log2(e) / sqrt(dh) (the QKV epilogue
+  // applies it before rounding), so a score s is already the base-2 exponent
+  // of its softmax weight.
   // Lazy rescaling.  Scores are taken relative to a per-row reference mref
-  // (raw score units; equal in the four lanes that hold a query's keys), which
-  // enters as the initial value of the score accumulators, so the MFMAs return
-  // s - mref.  The reference moves only when a score of the block exceeds it by
-  // more than tau / sl2 (every p = 2^(sl2 (s - mref)) stays below 2^tau), so a
-  // typical block needs no cross-lane maximum and no rescale of O.  O and the
-  // row sum l always share the reference, so the result is exact up to
-  // rounding for any reference.
-  const float tau_raw = a.rescale_log2 / sl2;
+  // (equal in the four lanes that hold a query's keys), which enters as the
+  // initial value of the score accumulators, so the MFMAs return s - mref.
+  // The reference moves only when a score of the block exceeds it by more
+  // than tau (every p = 2^(s - mref) stays below 2^tau), so a typical block
+  // needs no cross-lane maximum and no rescale of O.  O and the row sum l
+  // always share the reference, so the result is exact up to rounding for any
+  // reference.
+  const float tau = a.rescale_log2;
   float mref[QTW];      // -inf until the row has seen a visible key
   f32x4 o[QTW][ND];
   f32x4 lacc[QTW];      // bf16: row sums from an MFMA with a ones operand (all four equal);
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
     }
   };
 
-  // p = 2^(sl2 (s - mref)); lane holds keys kb0 + 32c + 8*(lane/16) + 4*half + q
+  // p = 2^(s - mref); lane holds keys kb0 + 32c + 8*(lane/16) + 4*half + q
   auto softmax = [&]() {
 #pragma unroll
     for (int qt = 0; qt < QTW; ++qt) {
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) lm = fmaxf(lm, sacc[st][qt][q]);
       const bool first = mref[qt] == -INFINITY;
-      if (__ballot(first || lm > tau_raw)) {
+      if (__ballot(first || lm > tau)) {
         // move the reference: to the row maximum on a row's first visible
         // keys, else up by the excess of the row maximum over it (if any)
         float rm = fmaxf(lm, __shfl_xor(lm, 16, 64));
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
         for (int st = 0; st < 4; ++st)
 #pragma unroll
           for (int q = 0; q < 4; ++q) sacc[st][qt][q] -= sh;
-        const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-sh * sl2);
+        const float alpha = first ? 1.0f : __builtin_amdgcn_exp2f(-sh);
         mref[qt] = first ? (rm == -INFINITY ? -INFINITY : rm) : mref[qt] + sh;
         if (__ballot(alpha != 1.0f)) {
 #pragma unroll
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sacc[st][qt][q] = __builtin_amdgcn_exp2f(sacc[st][qt][q] * sl2);   // -inf -> 0
+        for (int q = 0; q < 4; ++q) sacc[st][qt][q] = __builtin_amdgcn_exp2f(sacc[st][qt][q]);   // -inf -> 0
       if constexpr (AT == DT_F32) {
         float sum = 0.f;
 #pragma unroll
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
       update(nblk - 1);
     }
   }
-  // the row sum, and the reference in scaled (base-2) units for the merge
+  // the row sum and the reference (base 2) for the merge
   float l[QTW], m[QTW];
 #pragma unroll
   for (int qt = 0; qt < QTW; ++qt) {
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
       sum += __shfl_xor(sum, 32, 64);
     }
     l[qt] = sum;
-    m[qt] = mref[qt] == -INFINITY ? -INFINITY : mref[qt] * sl2;
+    m[qt] = mref[qt];
   }
   wait_vmcnt<0>();   // no copy into LDS may be in flight when the workgroup exits
 

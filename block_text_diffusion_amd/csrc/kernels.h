@@ -57,6 +57,7 @@ struct GemmArgs {
   const int32_t* pos0;     // per request: position of its row 0
   int pos0_stride;         // int32 stride between requests in pos0
   const float* rope_cs;    // [max_ctx][dh/2] (cos, sin) pairs, or null
+  float q_scale;           // EPI_QKV: factor on the query outputs before their rounding
 };
 
 void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
