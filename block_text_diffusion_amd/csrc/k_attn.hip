@@ -82,12 +82,19 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int TB = ATT_QR / G;                     // tokens per query block
 
-  int bid = blockIdx.x;
-  const int s = bid % a.n_split; bid /= a.n_split;
+  // Work items go to the 8 XCDs (the dispatcher deals workgroups to them
+  // round-robin) in contiguous runs, query block fastest, so the query blocks
+  // that read one key range run back to back on one XCD and the second finds
+  // the keys and values in that XCD's L2.  The grid is rounded up to a
+  // multiple of 8; surplus workgroups return at once.
+  const int work = a.n_req * a.Hkv * a.q_blocks * a.n_split;
+  const int w8 = (work + 7) & ~7;
+  int bid = (int)(blockIdx.x & 7) * (w8 >> 3) + (int)(blockIdx.x >> 3);
+  if (bid >= work) return;
   const int qb = bid % a.q_blocks; bid /= a.q_blocks;
+  const int s = bid % a.n_split; bid /= a.n_split;
   const int g = bid % a.Hkv; bid /= a.Hkv;
   const int r = bid;
-  if (r >= a.n_req) return;
 
   const int pos0 = a.pos0[r * a.pos0_stride];
   const int nrows = a.rows_per_req;
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const AttnArgs a, int dh) {
 }
 
 void launch_attention(int adt, const AttnArgs& a, hipStream_t s) {
-  const int blocks = a.n_req * a.Hkv * a.q_blocks * a.n_split;
+  const int blocks = (a.n_req * a.Hkv * a.q_blocks * a.n_split + 7) & ~7;
   if (adt == DT_F32) {
     if (a.dh == 64) hipLaunchKernelGGL((k_attn<DT_F32, 64>), dim3(blocks), dim3(512), 0, s, a);
     else hipLaunchKernelGGL((k_attn<DT_F32, 128>), dim3(blocks), dim3(512), 0, s, a);
