@@ -108,7 +108,7 @@ int32_t validate_config(const cd_config* c) {
 
 int sampler_chunks(int V) {
   int n = 1;
-  while (V / n > 16384 && (V % (2 * n * 4)) == 0) n *= 2;
+  while (V / n > 8192 && (V % (2 * n * 4)) == 0) n *= 2;   // chunks of at most 8192 logits
   return n;
 }
 

@@ -1,9 +1,9 @@
 // Fused vocabulary-wide sampler.
 //
 // Pass 1 (k_sample_part): the fp32 logits are read exactly once.  Each row
-// is cut into chunks, one 256-thread workgroup per (row, chunk), so a
-// 256-row canvas still launches thousands of workgroups; each thread streams
-// 16-byte loads and keeps an online (max m, S = sum e^(z-m),
+// is cut into chunks of at most 8192 logits, one 256-thread workgroup per
+// (row, chunk), so a 256-row canvas launches 8192 workgroups; each thread
+// streams 16-byte loads, four in flight, and keeps an online (max m, S = sum e^(z-m),
 // U = sum e^(z-m)(z-m), index of the first max).  Partials merge across the
 // wave with shuffles and across waves through LDS.
 // Pass 2 (k_sample_final): one workgroup per request, one thread per canvas
@@ -42,28 +42,41 @@ __global__ __launch_bounds__(256) void k_sample_part(SampleArgs a) {
   float m = -INFINITY, S = 0.f, U = 0.f;
   int idx = 0x7FFFFFFF;
   const int n4 = a.chunk / 4;
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    float4 v = z4[i];
-    float z[4] = {v.x, v.y, v.z, v.w};
-    float vm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    if (vm > m) {
-      int j = 0;
-      while (z[j] != vm) ++j;
-      if (m != -INFINITY) {
-        const float dd = m - vm;
-        const float f = exp2f(dd * L2E);
-        U = f * (U + dd * S);
-        S = f * S;
-      }
-      m = vm;
-      idx = chunk * a.chunk + 4 * i + j;
-    }
+  // Four 16-byte loads per thread are issued before any is used (indices
+  // clamped, so none is conditional; non-temporal: the logits are read once),
+  // then taken in the order i, i+256, ... as a one-load loop would.
+  constexpr int UNR = 4;
+  typedef float f32v4 __attribute__((ext_vector_type(4)));
+  const f32v4* zv = reinterpret_cast<const f32v4*>(z4);
+  for (int i0 = threadIdx.x; i0 < n4; i0 += 256 * UNR) {
+    f32v4 vv[UNR];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float dz = z[q] - m;
-      const float e = exp2f(dz * L2E);
-      S += e;
-      U += e * dz;
+    for (int u = 0; u < UNR; ++u) vv[u] = __builtin_nontemporal_load(zv + min(i0 + u * 256, n4 - 1));
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = i0 + u * 256;
+      if (i >= n4) break;
+      float z[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      float vm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      if (vm > m) {
+        int j = 0;
+        while (z[j] != vm) ++j;
+        if (m != -INFINITY) {
+          const float dd = m - vm;
+          const float f = exp2f(dd * L2E);
+          U = f * (U + dd * S);
+          S = f * S;
+        }
+        m = vm;
+        idx = chunk * a.chunk + 4 * i + j;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float dz = z[q] - m;
+        const float e = exp2f(dz * L2E);
+        S += e;
+        U += e * dz;
+      }
     }
   }
   // a NaN logit never passes the comparisons above; make it visible
@@ -100,18 +113,35 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
   int nlock = 0, stable = 1, xeq = 1, nonfin = 0;
   for (int i = threadIdx.x; i < a.C; i += 256) {
     const int64_t row = (int64_t)rr * a.C + i;
+    // the row's chunk partials in groups of 8, each group loaded before use
+    // (indices clamped: a repeated last chunk leaves the maximum unchanged and
+    // is skipped in the sums), chunks taken in ascending order
+    const float4* pr = a.part + row * a.n_chunks;
+    const int nc = a.n_chunks;
     double M = -INFINITY;
-    for (int c = 0; c < a.n_chunks; ++c) M = fmax(M, (double)a.part[row * a.n_chunks + c].x);
+    for (int c0 = 0; c0 < nc; c0 += 8) {
+      float mx[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mx[u] = pr[min(c0 + u, nc - 1)].x;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) M = fmax(M, (double)mx[u]);
+    }
     double S = 0.0, U = 0.0;
     int idx = 0x7FFFFFFF;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const float4 p = a.part[row * a.n_chunks + c];
-      if (p.x == -INFINITY) continue;
-      const double d = (double)p.x - M;
-      const double f = exp(d);
-      S += f * (double)p.y;
-      U += f * ((double)p.z + d * (double)p.y);
-      if ((double)p.x == M) idx = min(idx, __float_as_int(p.w));
+    for (int c0 = 0; c0 < nc; c0 += 8) {
+      float4 pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = pr[min(c0 + u, nc - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float4 p = pv[u];
+        if (c0 + u >= nc || p.x == -INFINITY) continue;
+        const double d = (double)p.x - M;
+        const double f = exp(d);
+        S += f * (double)p.y;
+        U += f * ((double)p.z + d * (double)p.y);
+        if ((double)p.x == M) idx = min(idx, __float_as_int(p.w));
+      }
     }
     const double H = log(S) - U / S;
     const double pm = 1.0 / S;
