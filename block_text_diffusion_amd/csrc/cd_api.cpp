@@ -405,10 +405,13 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
   at.part_ml = c->st<float>(p.part_ml);
 
   { PROF(CD_PROF_EMBED); launch_embed(p.wdt_other, c->W + p.embed, ids, T, g.vocab, d, h, s); }
+  // u holds RMSNorm(h) once a combine has written it for the next consumer
+  bool u_ready = false;
   for (int l = 0; l < g.n_layers; ++l) {
     const LayerOff& lw = p.layer[l];
     if (trace && c->trace_h) launch_copy_f32(h, c->trace_h + (int64_t)l * T * d, (int64_t)T * d, s);
-    { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
+    if (!u_ready) { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
+    u_ready = false;
     // QKV + rotary, K/V scattered into the cache at positions P_r + i
     {
       GemmArgs a = gemm_base(u, d, c->W + lw.qkv, c->wt<float>(lw.qkv_s), d, p.qkv_npad,
@@ -489,16 +492,20 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       PROF(CD_PROF_EXPERT_DOWN);
       gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, s);
     }
-    // h += sum_j gate_j * y_j (choice order) + shared FFN row
+    // h += sum_j gate_j * y_j (choice order) + shared FFN row; the same kernel
+    // writes u = RMSNorm(h) for the next layer or the LM head (every reader
+    // of this layer's u ran before it on this stream or joined above)
     if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
     {
+      u_ready = l + 1 < g.n_layers || head;
       PROF(CD_PROF_COMBINE);
       launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate),
-                     g.shared_hidden ? c->st<float>(p.sout) : nullptr, T, k, d, h, s);
+                     g.shared_hidden ? c->st<float>(p.sout) : nullptr, T, k, d, h, u_ready ? u : nullptr,
+                     g.rms_eps, s);
     }
   }
   if (head) {
-    { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
+    if (!u_ready) { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
     float* logits = c->st<float>(p.logits) + (int64_t)r0 * g.canvas_len * g.vocab;
     GemmArgs a = gemm_base(u, d, c->W + p.lm, nullptr, d, p.lm_npad, g.vocab, logits, g.vocab);
     PROF(CD_PROF_LM_HEAD);

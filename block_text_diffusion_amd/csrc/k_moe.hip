@@ -363,11 +363,15 @@ void launch_route(const RouteArgs& a, hipStream_t s) {
 // h[t] += sum_j gate[t][j] * Y[slot[t][j]] (j in order: deterministic), then
 // + add[t] (the shared FFN's fp32 row) when given.  A token's gates and slots
 // (k <= 16) are loaded once, and the k expert rows of a column group in
-// batches of 8 before any is added, so the loads overlap.
+// batches of 8 before any is added, so the loads overlap.  When u is given
+// the workgroup also writes the RMSNorm (unit gain) of the new row into it,
+// the input of the next layer or of the LM head.
 template <int AT>
 __global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* slot, const float* gate,
-                                                 const float* add, int k, int d, float* h) {
+                                                 const float* add, int k, int d, float* h, void* u, float eps) {
+  __shared__ float red[4];
   const int t = blockIdx.x;
+  float ss = 0.f;
   float g[16];
   int64_t yr[16];
 #pragma unroll
@@ -402,13 +406,32 @@ __global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* 
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = acc;
+    ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+  }
+  if (!u) return;
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  // each thread reads back the elements of h it wrote itself
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
+    if constexpr (AT == DT_F32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(u) + (int64_t)t * d + c) =
+          make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    } else {
+      uint2 p;
+      p.x = pack_bf16(v.x * inv, v.y * inv);
+      p.y = pack_bf16(v.z * inv, v.w * inv);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(u) + (int64_t)t * d + c) = p;
+    }
   }
 }
 
 void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k,
-                    int d, float* h, hipStream_t s) {
-  if (adt == DT_F32) hipLaunchKernelGGL(k_combine<DT_F32>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h);
-  else hipLaunchKernelGGL(k_combine<DT_BF16>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h);
+                    int d, float* h, void* u, float eps, hipStream_t s) {
+  if (adt == DT_F32) hipLaunchKernelGGL(k_combine<DT_F32>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h, u, eps);
+  else hipLaunchKernelGGL(k_combine<DT_BF16>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h, u, eps);
 }
 
 }  // namespace cd

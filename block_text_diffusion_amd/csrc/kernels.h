@@ -131,9 +131,10 @@ void launch_route(const RouteArgs& a, hipStream_t s);
 void launch_embed(int edt, const void* E, const int32_t* ids, int T, int V, int d, float* h, hipStream_t s);
 void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s);
 void launch_rope_table(float* cs, int max_ctx, int dh, float theta, hipStream_t s);
-// h[t] += sum_j gate[t][j] * Yp[slot[t][j]] (choice order) + add[t] (fp32 row, or null)
+// h[t] += sum_j gate[t][j] * Yp[slot[t][j]] (choice order) + add[t] (fp32 row, or null);
+// when u is not null also u[t] = RMSNorm(h[t]) (unit gain) in the activation type
 void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k,
-                    int d, float* h, hipStream_t s);
+                    int d, float* h, void* u, float eps, hipStream_t s);
 void launch_attn_merge(int adt, const AttnArgs& a, hipStream_t s);
 void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 
