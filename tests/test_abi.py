@@ -93,7 +93,8 @@ def test_capacity_checked_before_prefill():
 
 def test_sampler_argument_checks():
     cfg = _cfg("sampler", L=1, d=64, Hq=1, Hkv=1, dh=64, E=1, k=1, fe=64, fs=0, wdtype="f32", P0=0)
-    assert B.cd_sample_workspace_bytes(256, 262144) == 16 * 256 * 16
+    # one 16-byte partial per (row, chunk of at most 8192 logits)
+    assert B.cd_sample_workspace_bytes(256, 262144) == 16 * 256 * (262144 // 8192)
     L = B.lib()
     args = [1 << 12] * 8
     assert L.cd_sample_step(ctypes.byref(cfg), 1 << 12, 100, None, 1, 1, 0, 0, *args[:7], None) == B.CD_ERR_INVALID_ARG
