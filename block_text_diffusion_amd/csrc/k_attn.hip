@@ -325,12 +325,22 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
   };
 
   // scores and softmax of block b, masked only where needed
+  // The MFMA phases run at a raised wave priority: when the other wave on
+  // the SIMD is in its softmax, the MFMA pipe is fed first and the VALU work
+  // fills the gaps.
   auto scores_softmax = [&](int b) {
     const int kb0 = kbeg + b * ATT_KB;
     const bool full = kb0 + ATT_KB <= kend && (!a.causal || kb0 + ATT_KB - 1 <= pos0 + tok0);
+    __builtin_amdgcn_s_setprio(1);
     if (full) scores(b, std::integral_constant<bool, false>{});
     else scores(b, std::integral_constant<bool, true>{});
+    __builtin_amdgcn_s_setprio(0);
     softmax();
+  };
+  auto update_p = [&](int b) {
+    __builtin_amdgcn_s_setprio(1);
+    update(b);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Block b has landed for this wave; after the barrier it has for every
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
       for (int b = 0; b < nblk; ++b) {
         sync_issue(b);
         scores_softmax(b);
-        update(b);
+        update_p(b);
       }
     } else {
       // The second half of the waves runs half a block behind: it meets
@@ -363,10 +373,10 @@ __global__ __launch_bounds__(512) void k_attn(const AttnArgs a) {
       scores_softmax(0);
       for (int b = 1; b < nblk; ++b) {
         sync_issue(b);
-        update(b - 1);
+        update_p(b - 1);
         scores_softmax(b);
       }
-      update(nblk - 1);
+      update_p(nblk - 1);
     }
   }
   // the row sum and the reference (base 2) for the merge
