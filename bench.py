@@ -298,6 +298,66 @@ def cpu_baseline(w):
             "est_step_s": step_s}
 
 
+def prefill_flops(w, n):
+    """Multiply-add FLOPs of a causal prefill of n tokens (all layers, no LM
+    head): QKV, O, router, k experts and the shared FFN per token, and causal
+    attention (query i sees i + 1 keys)."""
+    d, dh, Hq, Hkv, k, fe, fs, E = w["d"], w["dh"], w["Hq"], w["Hkv"], w["k"], w["fe"], w["fs"], w["E"]
+    per_tok = 2 * d * (Hq + 2 * Hkv) * dh + 2 * Hq * dh * d + 2 * d * E + k * 6 * d * fe + 6 * d * fs
+    attn = 4 * Hq * dh * (n * (n + 1) // 2)
+    return w["L"] * (n * per_tok + attn)
+
+
+def prefill_line(w, ms_per_request):
+    """Causal prefill of one prompt: tokens/s and MFMA rate against the bf16 peak."""
+    n = w["P0"]
+    if not n or not ms_per_request:
+        return None
+    tf = prefill_flops(w, n) / (ms_per_request * 1e-3) / 1e12
+    return {"tokens": n, "ms": round(ms_per_request, 2), "tok_s": round(n / ms_per_request * 1e3, 1),
+            "tflop": round(prefill_flops(w, n) / 1e12, 2), "tflops": round(tf, 1),
+            "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+def concurrency_sweep(w, counts):
+    """Committed tok/s of one full block (canvas start, passes to the stop,
+    commit) at several request counts, on one model: before each point the
+    request state is cleared and every request gets its own prefix."""
+    import torch
+    from block_text_diffusion_amd import binding as B
+    from block_text_diffusion_amd.engine import Engine
+
+    dev = torch.device("cuda:0")
+    C = w["C"]
+    eng = Engine(w, device=dev, max_requests=max(counts), max_ctx=w["P0"] + C)
+    ctx = eng.ctx
+    B.cd_synth_weights(ctx, w["weight_seed"])
+    ids_out = torch.empty(C, dtype=torch.int32, device=dev)
+    out = []
+    for R in counts:
+        B.cd_reset(ctx)
+        for r in range(R):
+            B.cd_prefill(ctx, r, torch.from_numpy(synth_inputs.prefix_ids(w["V"], w["P0"], w["prefix_seed"], r)).to(dev))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for r in range(R):
+            B.cd_init_canvas(ctx, r, w["gen_seed"], 0)
+        passes, stopped = 0, np.zeros(R, dtype=bool)
+        while not stopped.all():
+            B.cd_denoise_step(ctx, R, eng.info)
+            passes += 1
+            stopped |= np.array([bool(i.stop) for i in B.cd_read_step_info(ctx, eng.info, R)])
+        for r in range(R):
+            B.cd_commit_block(ctx, r, ids_out)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        out.append({"requests": R, "passes": passes, "block_ms": round(ms, 1),
+                    "ms_per_pass": round(ms / passes, 2), "committed_tok_s": round(R * C / ms * 1e3, 1)})
+        log(f"sweep: {out[-1]}")
+    eng.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,6 +368,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block", action="store_true", help="skip the full-block measurement")
     ap.add_argument("--copy-calib", action="store_true", help="only run the byte-counter calibration copy")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time one full block at 1, 2, 4 and 32 requests (the 32-request fp8 model)")
     args = ap.parse_args()
     if args.copy_calib:
         copy_calibration()
@@ -359,6 +421,7 @@ def main():
         "committed_tok_s": round(committed, 2) if committed else None,
         "block_passes": g["block_passes"], "blocks": g["blocks"],
         "prefill_ms": round(g["prefill_ms"], 2),
+        "prefill": prefill_line(w, g["prefill_ms"] / R),
         "roofline": roof,
         "ms_per_step_median": round(float(np.median(g["step_ms"])), 4),
         "ms_per_step_p95": round(float(np.percentile(g["step_ms"], 95)), 4),
@@ -373,6 +436,10 @@ def main():
         cb.pop("est_step_s")
         cb["value"] = float(f"{cb['value']:.6g}")
         line["cpu_baseline"] = cb
+    if args.sweep:
+        line["concurrency_sweep"] = {"workload": "batch_fp8 model, one 256-token block per request after a "
+                                                 f"{w['P0']}-token prefix",
+                                     "points": concurrency_sweep(synth_inputs.workload("batch_fp8"), (1, 2, 4, 32))}
     print(json.dumps(line), flush=True)
 
 
