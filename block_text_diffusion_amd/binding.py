@@ -83,6 +83,9 @@ def lib():
             "cd_get_length": [c_void_p, c_int32, P(c_int32)],
             "cd_set_trace": [c_void_p, c_void_p, c_void_p, c_void_p],
             "cd_abort_canvas": [c_void_p, c_int32],
+            "cd_release": [c_void_p, c_int32, c_void_p],
+            "cd_serve": [c_void_p, c_int32, c_void_p, P(ctypes.c_int64), P(c_int32), P(c_int32),
+                         P(c_uint64), c_int32, c_void_p, P(ctypes.c_int64), P(c_int32), c_void_p],
             "cd_profile": [c_void_p, c_int32],
             "cd_profile_read": [c_void_p, c_void_p, c_void_p, c_int32],
         }
@@ -101,7 +104,8 @@ def exported_names():
             "cd_synth_weights", "cd_set_weight", "cd_get_weight", "cd_prefill", "cd_init_canvas",
             "cd_denoise_step", "cd_read_step_info", "cd_commit_block", "cd_generate",
             "cd_sample_workspace_bytes", "cd_sample_step", "cd_get_buffer", "cd_get_length",
-            "cd_set_trace", "cd_abort_canvas", "cd_profile", "cd_profile_read", "cd_last_error"]
+            "cd_set_trace", "cd_abort_canvas", "cd_release", "cd_serve", "cd_profile", "cd_profile_read",
+            "cd_last_error"]
 
 
 def _check(code):
@@ -204,6 +208,38 @@ def cd_generate(ctx, req, prefix, n_blocks, seed, out_ids, stream=None):
     _check(lib().cd_generate(ctx, req, _ptr(prefix), n_prefix, n_blocks, seed, _ptr(out_ids), steps,
                              _stream(stream)))
     return list(steps)
+
+
+def cd_release(ctx, req, stream=None):
+    _check(lib().cd_release(ctx, req, _stream(stream)))
+
+
+def cd_serve(ctx, prefixes, n_blocks, seeds, n_slots, out_ids, stream=None):
+    """Queue of requests: prefixes (list of 1-D int32 device tensors), blocks
+    and seeds per request.  Request q's blocks land in out_ids (1-D int32
+    device) at the offset of the blocks of requests before it.  Returns the
+    passes per block, one list per request."""
+    import torch
+    n_q = len(prefixes)
+    assert len(n_blocks) == n_q and len(seeds) == n_q
+    flat = torch.cat([p.reshape(-1) for p in prefixes]).to(torch.int32).contiguous()
+    lens = [int(p.numel()) for p in prefixes]
+    poff = [0] * n_q
+    for q in range(1, n_q):
+        poff[q] = poff[q - 1] + lens[q - 1]
+    C = out_ids.numel() // max(1, sum(n_blocks))
+    ooff = [0] * n_q
+    for q in range(1, n_q):
+        ooff[q] = ooff[q - 1] + n_blocks[q - 1] * C
+    steps = (c_int32 * sum(n_blocks))()
+    _check(lib().cd_serve(ctx, n_q, _ptr(flat), (ctypes.c_int64 * n_q)(*poff), (c_int32 * n_q)(*lens),
+                          (c_int32 * n_q)(*n_blocks), (c_uint64 * n_q)(*seeds), n_slots, _ptr(out_ids),
+                          (ctypes.c_int64 * n_q)(*ooff), steps, _stream(stream)))
+    out, i = [], 0
+    for nb in n_blocks:
+        out.append(list(steps[i:i + nb]))
+        i += nb
+    return out
 
 
 def cd_sample_workspace_bytes(rows, vocab):

@@ -98,6 +98,7 @@ int32_t validate_config(const cd_config* c) {
     return fail(CD_ERR_UNSUPPORTED, "n_experts <= 256 and top_k <= min(16, n_experts) required");
   if (c->vocab % 128) return fail(CD_ERR_UNSUPPORTED, "vocab must be a multiple of 128");
   if (c->max_ctx < c->canvas_len + 1) return fail(CD_ERR_INVALID_ARG, "max_ctx must exceed canvas_len");
+  if (c->max_requests > 256) return fail(CD_ERR_UNSUPPORTED, "max_requests <= 256");
   if (!(c->lock_threshold >= 0.f && c->lock_threshold <= 1.f) || !(c->stop_entropy >= 0.f) || !(c->rms_eps >= 0.f) ||
       !(c->rope_theta >= 0.f))
     return fail(CD_ERR_INVALID_ARG, "bad sampler/norm constants");
@@ -533,6 +534,8 @@ void sample(cd_ctx* c, int r0, int n_req, hipStream_t s) {
   a.canvas_in = c->st<int32_t>(p.canvas) + (int64_t)r0 * C;
   a.rq = c->st<ReqDev>(p.rq) + r0;
   a.req0 = r0;
+  for (int r = r0; r < r0 + n_req; ++r)
+    if (c->req[r].active) a.active[r >> 6] |= 1ull << (r & 63);
   a.max_steps = g.max_steps; a.lock_th = g.lock_threshold; a.stop_H = g.stop_entropy;
   { PROF(CD_PROF_SAMPLER_PART); launch_sampler_part(a, s); }
   { PROF(CD_PROF_SAMPLER_FINAL); launch_sampler_final(a, s); }
@@ -540,17 +543,29 @@ void sample(cd_ctx* c, int r0, int n_req, hipStream_t s) {
 
 int32_t check_ctx(cd_ctx* c) { return c ? CD_OK : fail(CD_ERR_INVALID_ARG, "null context"); }
 
+// One pass over requests r0..r0+n_req-1.  Requests without an active canvas
+// ride along: their rows go through the forward (whatever ids their canvas
+// holds, keys/values written past their committed length), but the sampler
+// leaves their state untouched.
 int32_t step_internal(cd_ctx* c, int r0, int n_req, hipStream_t s) {
   const cd_config& g = c->p.c;
+  int n_active = 0;
   for (int r = r0; r < r0 + n_req; ++r) {
     const HostReq& q = c->req[r];
-    if (!q.active) return fail(CD_ERR_BAD_STATE, "request %d has no active canvas", r);
+    if (!q.active) {
+      if ((int64_t)q.P + g.canvas_len > g.max_ctx)
+        return fail(CD_ERR_CAPACITY, "idle request %d has no room for a canvas (release it)", r);
+      continue;
+    }
     if (q.t >= g.max_steps) return fail(CD_ERR_BAD_STATE, "request %d reached the step cap", r);
+    ++n_active;
   }
+  if (!n_active) return fail(CD_ERR_BAD_STATE, "no request in 0..%d has an active canvas", r0 + n_req - 1);
   forward(c, r0, n_req, g.canvas_len, c->st<int32_t>(c->p.canvas) + (int64_t)r0 * g.canvas_len, false, true,
           true, s);
   sample(c, r0, n_req, s);
-  for (int r = r0; r < r0 + n_req; ++r) c->req[r].t++;
+  for (int r = r0; r < r0 + n_req; ++r)
+    if (c->req[r].active) c->req[r].t++;
   return hip_status("denoise step");
 }
 
@@ -755,9 +770,22 @@ int32_t cd_prefill(cd_ctx* c, int32_t req, const int32_t* d_ids, int32_t n, void
   if ((int64_t)q.P + n + g.canvas_len > g.max_ctx) return fail(CD_ERR_CAPACITY, "KV cache too small for prefill");
   hipStream_t s = strm(stream);
   forward(c, req, 1, n, d_ids, true, false, true, s);
-  launch_advance(c->st<ReqDev>(c->p.rq), req, n, 0, s);
+  launch_advance(c->st<ReqDev>(c->p.rq), req, n, s);
   q.P += n;
   return hip_status("prefill");
+}
+
+// canvas start of slot req; rid keys its Philox stream (the slot itself for
+// the public call, the queue index in the batched loop)
+int32_t init_canvas_internal(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, int32_t rid, hipStream_t s) {
+  const cd_config& g = c->p.c;
+  HostReq& q = c->req[req];
+  if (q.active) return fail(CD_ERR_BAD_STATE, "request %d already has an active canvas", req);
+  if ((int64_t)q.P + g.canvas_len > g.max_ctx) return fail(CD_ERR_CAPACITY, "KV cache full");
+  launch_init_canvas(c->st<int32_t>(c->p.canvas), c->st<ReqDev>(c->p.rq), req, g.canvas_len, g.vocab, seed, block,
+                     rid, s);
+  q.active = true; q.t = 0; q.block = block; q.seed = seed;
+  return hip_status("init canvas");
 }
 
 int32_t cd_init_canvas(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, void* stream) {
@@ -765,13 +793,16 @@ int32_t cd_init_canvas(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, voi
   const cd_config& g = c->p.c;
   if (req < 0 || req >= g.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
   if (block < 0) return fail(CD_ERR_INVALID_ARG, "negative block index");
+  return init_canvas_internal(c, req, seed, block, req, strm(stream));
+}
+
+int32_t cd_release(cd_ctx* c, int32_t req, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (req < 0 || req >= c->p.c.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
   HostReq& q = c->req[req];
-  if (q.active) return fail(CD_ERR_BAD_STATE, "request %d already has an active canvas", req);
-  if ((int64_t)q.P + g.canvas_len > g.max_ctx) return fail(CD_ERR_CAPACITY, "KV cache full");
-  launch_init_canvas(c->st<int32_t>(c->p.canvas), c->st<ReqDev>(c->p.rq), req, g.canvas_len, g.vocab, seed, block,
-                     strm(stream));
-  q.active = true; q.t = 0; q.block = block; q.seed = seed;
-  return hip_status("init canvas");
+  if (q.P) launch_advance(c->st<ReqDev>(c->p.rq), req, -q.P, strm(stream));
+  q = HostReq();
+  return hip_status("release");
 }
 
 int32_t cd_denoise_step(cd_ctx* c, int32_t n_req, cd_step_info* d_info, void* stream) {
@@ -843,7 +874,7 @@ int32_t cd_commit_block(cd_ctx* c, int32_t req, int32_t* d_out_ids, void* stream
   int32_t* a = c->st<int32_t>(c->p.argmax) + (int64_t)req * g.canvas_len;
   if (!info.canvas_is_argmax) forward(c, req, 1, g.canvas_len, a, false, false, true, s);
   launch_copy_i32(a, d_out_ids, g.canvas_len, s);
-  launch_advance(c->st<ReqDev>(c->p.rq), req, g.canvas_len, 1, s);
+  launch_advance(c->st<ReqDev>(c->p.rq), req, g.canvas_len, s);
   q.P += g.canvas_len;
   q.active = false;
   return hip_status("commit");
@@ -879,6 +910,75 @@ int32_t cd_generate(cd_ctx* c, int32_t req, const int32_t* d_prefix, int32_t n_p
     if (int32_t st = cd_commit_block(c, req, d_out_ids + (int64_t)b * g.canvas_len, stream)) return st;
   }
   return hip_status("generate");
+}
+
+int32_t cd_serve(cd_ctx* c, int32_t n_queue, const int32_t* d_prefix, const int64_t* h_prefix_off,
+                 const int32_t* h_prefix_len, const int32_t* h_n_blocks, const uint64_t* h_seeds, int32_t n_slots,
+                 int32_t* d_out, const int64_t* h_out_off, int32_t* h_steps, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  const cd_config& g = c->p.c;
+  const int C = g.canvas_len;
+  if (n_queue < 1 || n_slots < 1 || n_slots > g.max_requests || !d_prefix || !h_prefix_off || !h_prefix_len ||
+      !h_n_blocks || !h_seeds || !d_out || !h_out_off || !h_steps)
+    return fail(CD_ERR_INVALID_ARG, "bad serve arguments");
+  for (int q = 0; q < n_queue; ++q) {
+    if (h_prefix_len[q] < 1 || h_prefix_len[q] > g.max_prefill || h_n_blocks[q] < 1 || h_prefix_off[q] < 0 ||
+        h_out_off[q] < 0)
+      return fail(CD_ERR_INVALID_ARG, "bad prefix length, block count or offset for queued request %d", q);
+    if ((int64_t)h_prefix_len[q] + (int64_t)h_n_blocks[q] * C > g.max_ctx)
+      return fail(CD_ERR_CAPACITY, "queued request %d does not fit the KV cache", q);
+  }
+  for (int r = 0; r < n_slots; ++r)
+    if (c->req[r].active) return fail(CD_ERR_BAD_STATE, "slot %d has an active canvas", r);
+  hipStream_t s = strm(stream);
+  for (int r = 0; r < n_slots; ++r)
+    if (int32_t st = cd_release(c, r, stream)) return st;
+  std::vector<int64_t> steps_off(n_queue + 1, 0);
+  for (int q = 0; q < n_queue; ++q) steps_off[q + 1] = steps_off[q] + h_n_blocks[q];
+  std::vector<int> slot_q(n_slots, -1), slot_b(n_slots, 0);
+  int next = 0;
+  // a free slot takes the next queued request: cleared, prefilled, first canvas
+  auto admit = [&](int r) -> int32_t {
+    slot_q[r] = -1;
+    if (int32_t st = cd_release(c, r, stream)) return st;
+    if (next >= n_queue) return CD_OK;
+    const int q = next++;
+    if (int32_t st = cd_prefill(c, r, d_prefix + h_prefix_off[q], h_prefix_len[q], stream)) return st;
+    if (int32_t st = init_canvas_internal(c, r, h_seeds[q], 0, q, s)) return st;
+    slot_q[r] = q;
+    slot_b[r] = 0;
+    return CD_OK;
+  };
+  for (int r = 0; r < n_slots; ++r)
+    if (int32_t st = admit(r)) return st;
+  std::vector<cd_step_info> info(n_slots);
+  for (;;) {
+    int n_act = 0;   // busy slots past the last one are not computed
+    for (int r = 0; r < n_slots; ++r)
+      if (slot_q[r] >= 0) n_act = r + 1;
+    if (!n_act) break;
+    if (int32_t st = step_internal(c, 0, n_act, s)) return st;
+    if (hipMemcpyAsync(info.data(), c->st<cd_step_info>(c->p.info), sizeof(cd_step_info) * n_act,
+                       hipMemcpyDeviceToHost, s) != hipSuccess)
+      return hip_status("step info copy");
+    if (hipStreamSynchronize(s) != hipSuccess) return hip_status("stream sync");
+    for (int r = 0; r < n_act; ++r) {
+      const int q = slot_q[r];
+      if (q < 0) continue;
+      if (info[r].nonfinite) return fail(CD_ERR_NUMERIC, "non-finite logits for queued request %d", q);
+      if (!info[r].stop) continue;
+      const int b = slot_b[r];
+      h_steps[steps_off[q] + b] = info[r].step;
+      if (int32_t st = cd_commit_block(c, r, d_out + h_out_off[q] + (int64_t)b * C, stream)) return st;
+      if (b + 1 < h_n_blocks[q]) {
+        slot_b[r] = b + 1;
+        if (int32_t st = init_canvas_internal(c, r, h_seeds[q], b + 1, q, s)) return st;
+      } else if (int32_t st = admit(r)) {
+        return st;
+      }
+    }
+  }
+  return hip_status("serve");
 }
 
 int32_t cd_sample_workspace_bytes(int32_t rows, int32_t vocab, size_t* bytes) {

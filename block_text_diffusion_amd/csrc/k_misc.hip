@@ -86,27 +86,24 @@ void launch_rope_table(float* cs, int max_ctx, int dh, float theta, hipStream_t 
   hipLaunchKernelGGL(k_rope_table, dim3(1024), dim3(256), 0, s, cs, max_ctx, dh, (double)theta);
 }
 
-__global__ void k_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed, int block) {
+__global__ void k_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed, int block, int rid) {
   for (int i = threadIdx.x; i < C; i += blockDim.x)
-    canvas[(int64_t)req * C + i] = canvas_token(seed, i, 0, block, req, V);
+    canvas[(int64_t)req * C + i] = canvas_token(seed, i, 0, block, rid, V);
   if (threadIdx.x == 0) {
     rq[req].t = 0;
     rq[req].block = block;
-    rq[req].active = 1;
+    rq[req].rid = rid;
     rq[req].seed = seed;
   }
 }
-void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed, int block,
+void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed, int block, int rid,
                         hipStream_t s) {
-  hipLaunchKernelGGL(k_init_canvas, dim3(1), dim3(256), 0, s, canvas, rq, req, C, V, seed, block);
+  hipLaunchKernelGGL(k_init_canvas, dim3(1), dim3(256), 0, s, canvas, rq, req, C, V, seed, block, rid);
 }
 
-__global__ void k_advance(ReqDev* rq, int req, int dP, int clear_active) {
-  rq[req].P += dP;
-  if (clear_active) rq[req].active = 0;
-}
-void launch_advance(ReqDev* rq, int req, int dP, int clear_active, hipStream_t s) {
-  hipLaunchKernelGGL(k_advance, dim3(1), dim3(1), 0, s, rq, req, dP, clear_active);
+__global__ void k_advance(ReqDev* rq, int req, int dP) { rq[req].P += dP; }
+void launch_advance(ReqDev* rq, int req, int dP, hipStream_t s) {
+  hipLaunchKernelGGL(k_advance, dim3(1), dim3(1), 0, s, rq, req, dP);
 }
 
 __global__ void k_copy_i32(const int32_t* src, int32_t* dst, int n) {

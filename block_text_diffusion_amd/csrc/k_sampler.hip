@@ -105,7 +105,17 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
   int step, block, req;
   uint64_t seed;
   if (a.rq) {
-    step = a.rq[rr].t + 1; block = a.rq[rr].block; req = a.req0 + rr; seed = a.rq[rr].seed;
+    // a slot without an active canvas rides along in the pass: its rows were
+    // computed, but none of its state changes; its record reads step 0
+    const int ra = a.req0 + rr;
+    if (!((a.active[ra >> 6] >> (ra & 63)) & 1)) {
+      if (threadIdx.x == 0) {
+        cd_step_info z = {};
+        reinterpret_cast<cd_step_info*>(a.info)[rr] = z;
+      }
+      return;
+    }
+    step = a.rq[rr].t + 1; block = a.rq[rr].block; req = a.rq[rr].rid; seed = a.rq[rr].seed;
   } else {
     step = a.step; block = a.block; req = a.req0 + rr; seed = a.seed;
   }

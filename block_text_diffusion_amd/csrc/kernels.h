@@ -143,12 +143,14 @@ struct ReqDev {
   int32_t P;        // committed length
   int32_t t;        // passes done in the current block
   int32_t block;
-  int32_t active;   // canvas active
+  int32_t rid;      // request index that keys the Philox stream (the slot, unless a batched loop assigns one)
   uint64_t seed;
 };
+// canvas of slot req for block `block`, its Philox stream keyed by rid
 void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed,
-                        int block, hipStream_t s);
-void launch_advance(ReqDev* rq, int req, int dP, int clear_active, hipStream_t s);
+                        int block, int rid, hipStream_t s);
+// P += dP for slot req
+void launch_advance(ReqDev* rq, int req, int dP, hipStream_t s);
 void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s);
 
 // ---- sampler ------------------------------------------------------------------------
@@ -166,6 +168,7 @@ struct SampleArgs {
   void* info;            // cd_step_info per request
   const int32_t* canvas_in;  // canvas fed to this pass (for canvas_is_argmax), or null
   ReqDev* rq;            // per-request state of request req0 + i, or null
+  uint64_t active[4];    // with rq: bit r set when request r has an active canvas (others are left untouched)
   uint64_t seed;         // used when rq is null
   int step, block, req0; // used when rq is null
   int max_steps;

@@ -78,7 +78,7 @@ typedef struct cd_config {
   float rms_eps;          /* RMSNorm epsilon */
   float rope_theta;       /* rotary base; 0 disables rotary embedding */
   int32_t weight_dtype;   /* CD_F32, CD_BF16 or CD_FP8 */
-  int32_t max_requests;   /* requests denoised together */
+  int32_t max_requests;   /* requests denoised together (<= 256) */
   int32_t max_ctx;        /* KV capacity per request, tokens */
   int32_t max_prefill;    /* largest single prefill call, tokens */
   float attn_rescale_log2; /* attention softmax: the running row reference moves only when a
@@ -151,8 +151,12 @@ int32_t cd_prefill(cd_ctx* ctx, int32_t req, const int32_t* d_ids, int32_t n, vo
  * counter = (i, 0, block, req)).  Allowed when no canvas is active. */
 int32_t cd_init_canvas(cd_ctx* ctx, int32_t req, uint64_t seed, int32_t block, void* stream);
 
-/* ③ One denoise pass over requests 0..n_req-1 (all with an active canvas):
- * bidirectional forward over every canvas (keys = committed cache + canvas),
+/* ③ One denoise pass over request slots 0..n_req-1, at least one of them
+ * with an active canvas.  A slot without one rides along: its rows are
+ * computed (keys/values land past its committed length, which needs
+ * P + canvas_len <= max_ctx, else CD_ERR_CAPACITY) but none of its state
+ * changes and its record is all zero.  Each active canvas gets a
+ * bidirectional forward (keys = committed cache + canvas),
  * LM head to fp32 logits, then the sampler: per position entropy (nats),
  * argmax (ties to the lowest id) and max prob; lock when max prob >
  * lock_threshold (the position takes the argmax), else re-noise with
@@ -165,6 +169,10 @@ int32_t cd_denoise_step(cd_ctx* ctx, int32_t n_req, cd_step_info* d_info, void* 
 /* Drop the active canvas of request req without committing it (the
  * request returns to the state after its last commit).  Host-side only. */
 int32_t cd_abort_canvas(cd_ctx* ctx, int32_t req);
+
+/* Free slot req for a new prompt: P = 0 and no canvas (an active one is
+ * dropped).  The cache rows it held are simply overwritten later. */
+int32_t cd_release(cd_ctx* ctx, int32_t req, void* stream);
 
 /* Copy n_req step records from device to host and wait for the stream. */
 int32_t cd_read_step_info(cd_ctx* ctx, const cd_step_info* d_info, int32_t n_req,
@@ -186,6 +194,24 @@ int32_t cd_commit_block(cd_ctx* ctx, int32_t req, int32_t* d_out_ids, void* stre
 int32_t cd_generate(cd_ctx* ctx, int32_t req, const int32_t* d_prefix, int32_t n_prefix,
                     int32_t n_blocks, uint64_t seed, int32_t* d_out_ids,
                     int32_t* h_steps_per_block, void* stream);
+
+/* Batched loop over a queue of n_queue requests on n_slots slots (the
+ * retire/admit loop of a server).  Request q: prompt d_prefix +
+ * h_prefix_off[q] (device ids; host offsets), h_prefix_len[q] >= 1 ids,
+ * h_n_blocks[q] blocks, seed h_seeds[q]; its Philox streams are keyed by
+ * request index q (not by slot), so its output equals cd_generate of the
+ * same prompt and seed run as request q.  Slots 0..n_slots-1 are released
+ * first and take requests in queue order; each pass denoises every slot up
+ * to the highest busy one (idle ones ride along); a block that stops is
+ * committed to d_out + h_out_off[q] + b*canvas_len and its slot starts the
+ * next block, or, after the last, takes the next queued request.
+ * h_steps (host) receives the passes per block, request after request
+ * (sum of h_n_blocks entries).  Synchronises every pass; every slot is
+ * released on return.  CD_ERR_NUMERIC on non-finite logits. */
+int32_t cd_serve(cd_ctx* ctx, int32_t n_queue, const int32_t* d_prefix, const int64_t* h_prefix_off,
+                 const int32_t* h_prefix_len, const int32_t* h_n_blocks, const uint64_t* h_seeds,
+                 int32_t n_slots, int32_t* d_out, const int64_t* h_out_off, int32_t* h_steps,
+                 void* stream);
 
 /* Sampler alone on caller logits (rows x vocab fp32, device), rows a
  * multiple of canvas_len, treated as rows/canvas_len requests at pass `step`

@@ -83,6 +83,40 @@ def test_state_machine_rejects_out_of_order_calls_without_side_effects():
     B.cd_ctx_destroy(ctx)
 
 
+def test_serve_and_release_argument_checks():
+    cfg = _cfg()
+    cfg.max_requests = 2
+    ctx = _fake_ctx(cfg)
+    L = B.lib()
+    assert L.cd_release(ctx, -1, None) == B.CD_ERR_INVALID_ARG
+    assert L.cd_release(ctx, 2, None) == B.CD_ERR_INVALID_ARG
+    i64, i32, u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64
+    C = cfg.canvas_len
+
+    def serve(n_q=1, lens=(16,), blocks=(1,), slots=1, poff=(0,), ooff=(0,)):
+        n = len(lens)
+        steps = (i32 * 8)()
+        return L.cd_serve(ctx, n_q, 1 << 12, (i64 * n)(*poff), (i32 * n)(*lens), (i32 * n)(*blocks),
+                          (u64 * n)(*([1] * n)), slots, 1 << 12, (i64 * n)(*ooff), steps, None)
+    assert serve(n_q=0) == B.CD_ERR_INVALID_ARG
+    assert serve(slots=0) == B.CD_ERR_INVALID_ARG
+    assert serve(slots=3) == B.CD_ERR_INVALID_ARG                        # beyond max_requests
+    assert serve(lens=(0,)) == B.CD_ERR_INVALID_ARG
+    assert serve(lens=(cfg.max_prefill + 1,)) == B.CD_ERR_INVALID_ARG
+    assert serve(blocks=(0,)) == B.CD_ERR_INVALID_ARG
+    assert serve(poff=(-1,)) == B.CD_ERR_INVALID_ARG
+    assert serve(ooff=(-1,)) == B.CD_ERR_INVALID_ARG
+    n_fit = (cfg.max_ctx - 16) // C
+    assert serve(blocks=(n_fit + 1,)) == B.CD_ERR_CAPACITY
+    assert serve(n_q=2, lens=(16, 16), blocks=(1, n_fit + 1), poff=(0, 16), ooff=(0, C)) == B.CD_ERR_CAPACITY
+    B.cd_ctx_destroy(ctx)
+    bad = _cfg()
+    bad.max_requests = 257
+    with pytest.raises(B.CDError) as e:
+        B.cd_state_bytes(bad)
+    assert e.value.code == B.CD_ERR_UNSUPPORTED
+
+
 def test_capacity_checked_before_prefill():
     cfg = _cfg(P0=128)
     cfg.max_ctx = 300                                   # 128 + 256 does not fit
