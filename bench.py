@@ -358,6 +358,38 @@ def concurrency_sweep(w, counts):
     return out
 
 
+def serve_queue(w, n_queue, n_slots, seed=12):
+    """Committed tok/s of a queue served by cd_serve: prompts of 512..4096
+    tokens and 1 or 2 blocks each (seeded), n_slots slots; wall time from
+    the first prefill to the last commit."""
+    import torch
+    from block_text_diffusion_amd import binding as B
+    from block_text_diffusion_amd.engine import Engine
+
+    dev = torch.device("cuda:0")
+    C = w["C"]
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(512, 4097, n_queue)]
+    blocks = [int(x) for x in rng.integers(1, 3, n_queue)]
+    eng = Engine(w, device=dev, max_requests=n_slots, max_ctx=4096 + 2 * C)
+    B.cd_synth_weights(eng.ctx, w["weight_seed"])
+    prefs = [torch.from_numpy(synth_inputs.prefix_ids(w["V"], n, w["prefix_seed"], q)).to(dev)
+             for q, n in enumerate(lens)]
+    out = torch.empty(sum(blocks) * C, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    steps = B.cd_serve(eng.ctx, prefs, blocks, [w["gen_seed"]] * n_queue, n_slots, out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3
+    eng.close()
+    n_blk = sum(blocks)
+    res = {"requests": n_queue, "slots": n_slots, "blocks": n_blk, "prompt_tokens": sum(lens),
+           "passes_per_block": round(sum(sum(s) for s in steps) / n_blk, 2), "ms": round(ms, 1),
+           "committed_tok_s": round(n_blk * C / ms * 1e3, 1)}
+    log(f"serve: {res}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +402,8 @@ def main():
     ap.add_argument("--copy-calib", action="store_true", help="only run the byte-counter calibration copy")
     ap.add_argument("--sweep", action="store_true",
                     help="also time one full block at 1, 2, 4 and 32 requests (the 32-request fp8 model)")
+    ap.add_argument("--serve", action="store_true",
+                    help="also time a queue of 64 requests served on 32 slots (the fp8 model)")
     args = ap.parse_args()
     if args.copy_calib:
         copy_calibration()
@@ -440,6 +474,10 @@ def main():
         line["concurrency_sweep"] = {"workload": "batch_fp8 model, one 256-token block per request after a "
                                                  f"{w['P0']}-token prefix",
                                      "points": concurrency_sweep(synth_inputs.workload("batch_fp8"), (1, 2, 4, 32))}
+    if args.serve:
+        line["serve_queue"] = {"workload": "batch_fp8 model, 64 queued requests (prompts 512..4096 tokens, 1 or 2 "
+                                           "blocks each) on 32 slots, prefills included",
+                               **serve_queue(synth_inputs.workload("batch_fp8"), 64, 32)}
     print(json.dumps(line), flush=True)
 
 

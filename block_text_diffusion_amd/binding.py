@@ -84,6 +84,7 @@ def lib():
             "cd_set_trace": [c_void_p, c_void_p, c_void_p, c_void_p],
             "cd_abort_canvas": [c_void_p, c_int32],
             "cd_release": [c_void_p, c_int32, c_void_p],
+            "cd_move_request": [c_void_p, c_int32, c_int32, c_void_p],
             "cd_serve": [c_void_p, c_int32, c_void_p, P(ctypes.c_int64), P(c_int32), P(c_int32),
                          P(c_uint64), c_int32, c_void_p, P(ctypes.c_int64), P(c_int32), c_void_p],
             "cd_profile": [c_void_p, c_int32],
@@ -104,7 +105,7 @@ def exported_names():
             "cd_synth_weights", "cd_set_weight", "cd_get_weight", "cd_prefill", "cd_init_canvas",
             "cd_denoise_step", "cd_read_step_info", "cd_commit_block", "cd_generate",
             "cd_sample_workspace_bytes", "cd_sample_step", "cd_get_buffer", "cd_get_length",
-            "cd_set_trace", "cd_abort_canvas", "cd_release", "cd_serve", "cd_profile", "cd_profile_read",
+            "cd_set_trace", "cd_abort_canvas", "cd_release", "cd_move_request", "cd_serve", "cd_profile", "cd_profile_read",
             "cd_last_error"]
 
 
@@ -212,6 +213,10 @@ def cd_generate(ctx, req, prefix, n_blocks, seed, out_ids, stream=None):
 
 def cd_release(ctx, req, stream=None):
     _check(lib().cd_release(ctx, req, _stream(stream)))
+
+
+def cd_move_request(ctx, src, dst, stream=None):
+    _check(lib().cd_move_request(ctx, src, dst, _stream(stream)))
 
 
 def cd_serve(ctx, prefixes, n_blocks, seeds, n_slots, out_ids, stream=None):

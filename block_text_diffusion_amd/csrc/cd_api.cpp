@@ -206,6 +206,7 @@ Plan make_plan(const cd_config& c) {
 
 struct HostReq {
   int P = 0, t = 0, block = 0;
+  int rid = -1;   // Philox request index once set (a moved or served request keeps its own), else the slot
   bool active = false;
   uint64_t seed = 0;
 };
@@ -784,8 +785,26 @@ int32_t init_canvas_internal(cd_ctx* c, int32_t req, uint64_t seed, int32_t bloc
   if ((int64_t)q.P + g.canvas_len > g.max_ctx) return fail(CD_ERR_CAPACITY, "KV cache full");
   launch_init_canvas(c->st<int32_t>(c->p.canvas), c->st<ReqDev>(c->p.rq), req, g.canvas_len, g.vocab, seed, block,
                      rid, s);
-  q.active = true; q.t = 0; q.block = block; q.seed = seed;
+  q.active = true; q.t = 0; q.block = block; q.seed = seed; q.rid = rid;
   return hip_status("init canvas");
+}
+
+// every per-slot row of request `from` (K/V region, canvas, last pass
+// outputs, device state) copied to the free slot `to`; `from` is released
+int32_t move_internal(cd_ctx* c, int from, int to, hipStream_t s) {
+  const Plan& p = c->p;
+  const int64_t C = p.c.canvas_len, kvb = p.kv_req_stride * esize(p.adt);
+  const int64_t span[][2] = {{p.kcache, kvb}, {p.vcache, kvb}, {p.canvas, 4 * C}, {p.argmax, 4 * C},
+                             {p.lock, C},     {p.entropy, 8 * C}, {p.pmax, 8 * C}, {p.rq, (int64_t)sizeof(ReqDev)}};
+  for (const auto& x : span)
+    if (hipMemcpyAsync(c->S + x[0] + to * x[1], c->S + x[0] + from * x[1], x[1], hipMemcpyDeviceToDevice, s) !=
+        hipSuccess)
+      return hip_status("slot move");
+  if (c->req[from].P) launch_advance(c->st<ReqDev>(p.rq), from, -c->req[from].P, s);
+  if (c->req[from].rid < 0) c->req[from].rid = from;
+  c->req[to] = c->req[from];
+  c->req[from] = HostReq();
+  return hip_status("slot move");
 }
 
 int32_t cd_init_canvas(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, void* stream) {
@@ -793,7 +812,7 @@ int32_t cd_init_canvas(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, voi
   const cd_config& g = c->p.c;
   if (req < 0 || req >= g.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
   if (block < 0) return fail(CD_ERR_INVALID_ARG, "negative block index");
-  return init_canvas_internal(c, req, seed, block, req, strm(stream));
+  return init_canvas_internal(c, req, seed, block, c->req[req].rid >= 0 ? c->req[req].rid : req, strm(stream));
 }
 
 int32_t cd_release(cd_ctx* c, int32_t req, void* stream) {
@@ -803,6 +822,15 @@ int32_t cd_release(cd_ctx* c, int32_t req, void* stream) {
   if (q.P) launch_advance(c->st<ReqDev>(c->p.rq), req, -q.P, strm(stream));
   q = HostReq();
   return hip_status("release");
+}
+
+int32_t cd_move_request(cd_ctx* c, int32_t from, int32_t to, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  const int R = c->p.c.max_requests;
+  if (from < 0 || from >= R || to < 0 || to >= R || from == to)
+    return fail(CD_ERR_INVALID_ARG, "bad slots %d -> %d", from, to);
+  if (c->req[to].P || c->req[to].active) return fail(CD_ERR_BAD_STATE, "slot %d is not free", to);
+  return move_internal(c, from, to, strm(stream));
 }
 
 int32_t cd_denoise_step(cd_ctx* c, int32_t n_req, cd_step_info* d_info, void* stream) {
@@ -976,6 +1004,19 @@ int32_t cd_serve(cd_ctx* c, int32_t n_queue, const int32_t* d_prefix, const int6
       } else if (int32_t st = admit(r)) {
         return st;
       }
+    }
+    // with the queue drained, idle slots would ride along below busy ones:
+    // the highest busy request moves into the lowest idle slot
+    for (;;) {
+      int hi = -1, lo = -1;
+      for (int r = n_slots - 1; r >= 0 && hi < 0; --r)
+        if (slot_q[r] >= 0) hi = r;
+      for (int r = 0; r < hi && lo < 0; ++r)
+        if (slot_q[r] < 0) lo = r;
+      if (lo < 0) break;
+      if (int32_t st = move_internal(c, hi, lo, s)) return st;
+      slot_q[lo] = slot_q[hi]; slot_b[lo] = slot_b[hi];
+      slot_q[hi] = -1;
     }
   }
   return hip_status("serve");

@@ -148,7 +148,9 @@ int32_t cd_prefill(cd_ctx* ctx, int32_t req, const int32_t* d_ids, int32_t n, vo
 
 /* ② Canvas start for request req, block index `block`: token i is
  * floor(r0 * V / 2^32) with (r0..r3) = Philox4x32-10(key = seed;
- * counter = (i, 0, block, req)).  Allowed when no canvas is active. */
+ * counter = (i, 0, block, id)).  id is the request's index: its slot req,
+ * unless the request was moved here (cd_move_request), which keeps the
+ * index it had.  Allowed when no canvas is active. */
 int32_t cd_init_canvas(cd_ctx* ctx, int32_t req, uint64_t seed, int32_t block, void* stream);
 
 /* ③ One denoise pass over request slots 0..n_req-1, at least one of them
@@ -173,6 +175,14 @@ int32_t cd_abort_canvas(cd_ctx* ctx, int32_t req);
 /* Free slot req for a new prompt: P = 0 and no canvas (an active one is
  * dropped).  The cache rows it held are simply overwritten later. */
 int32_t cd_release(cd_ctx* ctx, int32_t req, void* stream);
+
+/* Move the request in slot `from` (any state, also mid-block) to the free
+ * slot `to` (P == 0, no canvas): its K/V region, canvas, last pass outputs
+ * and step state are copied on the stream, and `from` is released.  Its
+ * Philox streams keep their request index, so the move changes no result.
+ * A server uses it to keep busy slots at the front: a pass over slots
+ * 0..n-1 then computes no idle slot.  CD_ERR_BAD_STATE if `to` is not free. */
+int32_t cd_move_request(cd_ctx* ctx, int32_t from, int32_t to, void* stream);
 
 /* Copy n_req step records from device to host and wait for the stream. */
 int32_t cd_read_step_info(cd_ctx* ctx, const cd_step_info* d_info, int32_t n_req,
@@ -204,7 +214,9 @@ int32_t cd_generate(cd_ctx* ctx, int32_t req, const int32_t* d_prefix, int32_t n
  * first and take requests in queue order; each pass denoises every slot up
  * to the highest busy one (idle ones ride along); a block that stops is
  * committed to d_out + h_out_off[q] + b*canvas_len and its slot starts the
- * next block, or, after the last, takes the next queued request.
+ * next block, or, after the last, takes the next queued request.  Once the
+ * queue is empty, busy requests move down into idle slots (as
+ * cd_move_request) so that the passes shrink with the work left.
  * h_steps (host) receives the passes per block, request after request
  * (sum of h_n_blocks entries).  Synchronises every pass; every slot is
  * released on return.  CD_ERR_NUMERIC on non-finite logits. */

@@ -90,6 +90,8 @@ def test_serve_and_release_argument_checks():
     L = B.lib()
     assert L.cd_release(ctx, -1, None) == B.CD_ERR_INVALID_ARG
     assert L.cd_release(ctx, 2, None) == B.CD_ERR_INVALID_ARG
+    for a, b in [(0, 0), (-1, 0), (0, 2), (2, 1)]:
+        assert L.cd_move_request(ctx, a, b, None) == B.CD_ERR_INVALID_ARG
     i64, i32, u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64
     C = cfg.canvas_len
 

@@ -3,8 +3,8 @@ pass, through the C ABI, against the oracle.
 
 * a queue of three requests with 1, 3 and 1 blocks and prompts of different
   lengths on two slots: a finished request hands its slot to the next queued
-  one, and once the queue is empty slot 0 idles (rides along) while slot 1
-  finishes its last block.  The step cap of 2 makes every block stop at pass
+  one, and once the queue is empty the request in slot 1 moves down to the
+  idle slot 0 for its last block.  The step cap of 2 makes every block stop at pass
   2, so the pass counts are known and each committed block is pass 2's argmax
   of the oracle run of that request on its own, with its Philox streams keyed
   by its queue index (a wrong key changes the re-noised canvas that pass 2
@@ -12,7 +12,10 @@ pass, through the C ABI, against the oracle.
   two logits lie within 1e-4 are excluded (fp32 reduction order may swap
   them); the rest must match exactly.
 * cd_denoise_step with an idle slot: its canvas, committed length and
-  sampler outputs stay as they were and its record is all zero."""
+  sampler outputs stay as they were and its record is all zero.
+* cd_move_request in the middle of a block: the moved request continues,
+  commits and starts its next block in the new slot and still matches the
+  oracle run of its own request index."""
 import numpy as np
 import pytest
 import torch
@@ -95,3 +98,50 @@ def test_idle_slot_rides_along_unchanged():
     eng.close()
     err = ((z_batch - z_alone).norm(dim=1) / z_alone.norm(dim=1)).max().item()
     assert err <= 1e-5
+
+
+def test_move_mid_block_matches_oracle():
+    # request 1 runs pass 1 in slot 1 (slot 0 idle), moves to slot 0, runs
+    # pass 2 there, commits and starts its second block through the public
+    # calls: every draw stays keyed by request index 1
+    w = synth_inputs.workload("tiny")
+    C, seed = w["C"], 4
+    announce("serve_move_mid_block")
+    pre = synth_inputs.prefix_ids(w["V"], 70, 8, 1)
+    eng = Engine(w, max_requests=2, max_ctx=70 + 2 * C, max_prefill=w["P0"])
+    B.cd_synth_weights(eng.ctx, w["weight_seed"])
+    B.cd_prefill(eng.ctx, 1, torch.from_numpy(pre).cuda())
+    B.cd_init_canvas(eng.ctx, 1, seed, 0)
+    B.cd_denoise_step(eng.ctx, 2, eng.info)
+    with pytest.raises(B.CDError) as e:
+        B.cd_move_request(eng.ctx, 0, 1)                 # slot 1 is not free
+    assert e.value.code == B.CD_ERR_BAD_STATE
+    B.cd_move_request(eng.ctx, 1, 0)
+    assert [B.cd_get_length(eng.ctx, r) for r in range(2)] == [70, 0]
+    B.cd_denoise_step(eng.ctx, 1, eng.info)
+    assert eng.step_info(1)[0].step == 2
+    got = []
+    ids = torch.empty(C, dtype=torch.int32, device="cuda")
+    B.cd_commit_block(eng.ctx, 0, ids)
+    got.append(ids.cpu().numpy().astype(np.int64))
+    B.cd_init_canvas(eng.ctx, 0, seed, 1)
+    for _ in range(2):
+        B.cd_denoise_step(eng.ctx, 1, eng.info)
+    assert eng.step_info(1)[0].step == 2
+    B.cd_commit_block(eng.ctx, 0, ids)
+    got.append(ids.cpu().numpy().astype(np.int64))
+    assert B.cd_get_length(eng.ctx, 0) == 70 + 2 * C
+    eng.close()
+    W = Weights(w)
+    req = loop.Request(w, 1)
+    loop.prefill(w, W, req, pre)
+    for b in range(2):
+        x = loop.init_canvas(w, seed, b, 1)
+        for t in (1, 2):
+            ref = loop.denoise_pass(w, W, req, x, t, b, seed)
+            x = ref["x_next"]
+        srt = np.sort(ref["z"], axis=1)
+        clear = srt[:, -1] - srt[:, -2] > 1e-4
+        assert clear.mean() > 0.9
+        assert np.array_equal(got[b][clear], ref["a"][clear]), b
+        loop.commit(w, W, req, got[b])
