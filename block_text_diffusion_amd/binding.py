@@ -18,6 +18,7 @@ c_int32, c_uint64, c_size_t, c_void_p, c_float, c_double = (
 CD_OK, CD_ERR_INVALID_ARG, CD_ERR_BAD_STATE, CD_ERR_CAPACITY, CD_ERR_HIP, CD_ERR_UNSUPPORTED, CD_ERR_NUMERIC = (
     0, -1, -2, -3, -4, -5, -6)
 CD_F32, CD_BF16, CD_FP8 = 0, 1, 2
+CD_LOCK_MAXPROB, CD_LOCK_ENTROPY = 0, 1
 (CD_W_EMBED, CD_W_LM, CD_W_Q, CD_W_K, CD_W_V, CD_W_O, CD_W_ROUTER, CD_W_GATE, CD_W_UP, CD_W_DOWN,
  CD_W_SHARED_GATE, CD_W_SHARED_UP, CD_W_SHARED_DOWN) = range(13)
 (CD_BUF_LOGITS, CD_BUF_CANVAS, CD_BUF_ARGMAX, CD_BUF_ENTROPY, CD_BUF_PMAX, CD_BUF_LOCK, CD_BUF_KCACHE,
@@ -30,7 +31,7 @@ class cd_config(ctypes.Structure):
         "expert_hidden", "shared_hidden", "vocab", "canvas_len", "max_steps")] + [
         (n, c_float) for n in ("lock_threshold", "stop_entropy", "rms_eps", "rope_theta")] + [
         (n, c_int32) for n in ("weight_dtype", "max_requests", "max_ctx", "max_prefill")] + [
-        ("attn_rescale_log2", c_float)]
+        ("attn_rescale_log2", c_float), ("lock_rule", c_int32), ("entropy_bound", c_float)]
 
 
 class cd_step_info(ctypes.Structure):
@@ -140,7 +141,9 @@ def make_config(w: dict, max_requests=None, max_ctx=None, max_prefill=None) -> c
         canvas_len=w["C"], max_steps=w["max_steps"], lock_threshold=w["lock"], stop_entropy=w["stop_H"],
         rms_eps=w["eps"], rope_theta=w["theta"], weight_dtype=dt, max_requests=R,
         max_ctx=max_ctx or (P0 + w.get("blocks", 1) * w["C"]),
-        max_prefill=max_prefill or max(P0, 1), attn_rescale_log2=w.get("attn_rescale_log2", 0.0))
+        max_prefill=max_prefill or max(P0, 1), attn_rescale_log2=w.get("attn_rescale_log2", 0.0),
+        lock_rule={"maxprob": CD_LOCK_MAXPROB, "entropy": CD_LOCK_ENTROPY}[w.get("lock_rule", "maxprob")],
+        entropy_bound=w.get("entropy_bound", 0.1))
 
 
 def cd_weights_bytes(cfg):

@@ -104,6 +104,9 @@ int32_t validate_config(const cd_config* c) {
     return fail(CD_ERR_INVALID_ARG, "bad sampler/norm constants");
   if (!(c->attn_rescale_log2 >= 0.f && c->attn_rescale_log2 <= 64.f))
     return fail(CD_ERR_INVALID_ARG, "attn_rescale_log2 must lie in [0, 64]");
+  if ((c->lock_rule != CD_LOCK_MAXPROB && c->lock_rule != CD_LOCK_ENTROPY) ||
+      !(c->entropy_bound >= 0.f && c->entropy_bound < INFINITY))
+    return fail(CD_ERR_INVALID_ARG, "bad lock rule or entropy bound");
   return CD_OK;
 }
 
@@ -538,6 +541,7 @@ void sample(cd_ctx* c, int r0, int n_req, hipStream_t s) {
   for (int r = r0; r < r0 + n_req; ++r)
     if (c->req[r].active) a.active[r >> 6] |= 1ull << (r & 63);
   a.max_steps = g.max_steps; a.lock_th = g.lock_threshold; a.stop_H = g.stop_entropy;
+  a.lock_rule = g.lock_rule; a.ent_bound = g.entropy_bound;
   { PROF(CD_PROF_SAMPLER_PART); launch_sampler_part(a, s); }
   { PROF(CD_PROF_SAMPLER_FINAL); launch_sampler_final(a, s); }
 }
@@ -1048,6 +1052,7 @@ int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows
   a.entropy = d_entropy; a.pmax = d_pmax; a.info = d_info; a.canvas_in = nullptr; a.rq = nullptr;
   a.seed = seed; a.step = step; a.block = block; a.req0 = req0;
   a.max_steps = cfg->max_steps; a.lock_th = cfg->lock_threshold; a.stop_H = cfg->stop_entropy;
+  a.lock_rule = cfg->lock_rule; a.ent_bound = cfg->entropy_bound;
   launch_sampler_part(a, strm(stream));
   launch_sampler_final(a, strm(stream));
   return hip_status("sample step");

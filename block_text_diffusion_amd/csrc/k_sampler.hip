@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
     const double pm = 1.0 / S;
     const bool bad = !(S >= 1.0) || !isfinite(S) || !isfinite(U) || !isfinite(M);
     if (bad) { nonfin = 1; idx = 0; }
-    const bool lk = !bad && pm > (double)a.lock_th;
+    const bool lk = !bad && (a.lock_rule ? H <= (double)a.ent_bound : pm > (double)a.lock_th);
     const int tok = lk ? idx : canvas_token(seed, i, step, block, req, a.V);
     if (a.prev_a && a.prev_a[row] != idx) stable = 0;
     if (a.canvas_in && a.canvas_in[row] != idx) xeq = 0;

@@ -173,6 +173,8 @@ struct SampleArgs {
   int step, block, req0; // used when rq is null
   int max_steps;
   float lock_th, stop_H;
+  int lock_rule;         // 0: max prob > lock_th; 1: entropy <= ent_bound
+  float ent_bound;
 };
 void launch_sampler_part(const SampleArgs& a, hipStream_t s);
 void launch_sampler_final(const SampleArgs& a, hipStream_t s);

@@ -60,6 +60,16 @@ enum {
  * tensor as bf16; activations are then bf16. */
 enum { CD_F32 = 0, CD_BF16 = 1, CD_FP8 = 2 };
 
+/* Lock rule of the sampler.  CD_LOCK_MAXPROB: a position keeps its argmax
+ * when its max probability exceeds lock_threshold (the canvas explainer
+ * page, step ③: confident tokens stay, uncertain ones are re-noised).
+ * CD_LOCK_ENTROPY: it keeps its argmax when its entropy is at most
+ * entropy_bound nats (the explainer's A/B guide serves the model with an
+ * entropy-bound sampler and bound 0.1, giving only the name and the bound;
+ * read here as the same per-position keep/re-noise choice made on the
+ * entropy instead of the max probability). */
+enum { CD_LOCK_MAXPROB = 0, CD_LOCK_ENTROPY = 1 };
+
 typedef struct cd_config {
   int32_t n_layers;       /* decoder layers */
   int32_t d_model;        /* hidden width, multiple of 64 */
@@ -84,13 +94,15 @@ typedef struct cd_config {
   float attn_rescale_log2; /* attention softmax: the running row reference moves only when a
                               score exceeds it by more than this many powers of two (the
                               result is exact up to rounding for any value); 0 selects 8 */
+  int32_t lock_rule;      /* CD_LOCK_MAXPROB or CD_LOCK_ENTROPY */
+  float entropy_bound;    /* CD_LOCK_ENTROPY: lock when entropy <= this, nats (0.1) */
 } cd_config;
 
 /* Per-request result of one denoise pass, written to device memory. */
 typedef struct cd_step_info {
   int32_t step;             /* pass index t (1-based) within the block */
   int32_t stop;             /* 1 when the adaptive stop or the cap fired */
-  int32_t n_locked;         /* positions whose max prob exceeded the threshold */
+  int32_t n_locked;         /* positions locked by the lock rule this pass */
   int32_t stable;           /* argmax equal to the previous pass's everywhere */
   int32_t canvas_is_argmax; /* the canvas fed to this pass equals its argmax */
   int32_t nonfinite;        /* a logit was NaN or infinite */
@@ -161,7 +173,8 @@ int32_t cd_init_canvas(cd_ctx* ctx, int32_t req, uint64_t seed, int32_t block, v
  * bidirectional forward (keys = committed cache + canvas),
  * LM head to fp32 logits, then the sampler: per position entropy (nats),
  * argmax (ties to the lowest id) and max prob; lock when max prob >
- * lock_threshold (the position takes the argmax), else re-noise with
+ * lock_threshold (CD_LOCK_ENTROPY: when entropy <= entropy_bound; the
+ * position takes the argmax), else re-noise with
  * Philox(seed; i, t, block, req); stop when t >= 2, mean entropy <
  * stop_entropy and the argmax equals the previous pass's at every position,
  * or when t == max_steps.  d_info receives n_req cd_step_info records.

@@ -17,10 +17,15 @@ re-noise draws a fresh uniform id from Philox keyed by (seed; position, pass,
 block, request); stability compares this pass's argmax with the previous
 pass's at all positions, so the earliest stop is pass 2; both stop conditions
 are strict and tested at the same pass; pass 48 always stops.
+Entropy-bound variant ([P3] A/B guide: the serving example selects an
+entropy-bound sampler with bound 0.1 and says no more): the same keep or
+re-noise choice per position, made on the entropy: keep the argmax when
+H <= bound (nats, inclusive), else re-noise.
 
 Pins (tests/test_oracle_sampler.py): uniform logits give H = ln V exactly;
 two-level distributions against their closed form; H in [0, ln V];
-p_max = 1/sum(exp(z - max)); argmax ties; the stop truth table.
+p_max = 1/sum(exp(z - max)); argmax ties; the stop truth table; entropy-bound
+decisions on two-level rows whose closed-form entropy straddles the bound.
 """
 from __future__ import annotations
 
@@ -56,7 +61,10 @@ def sample(cfg, z, seed, step, block, req):
     Returns dict(H, a, pmax, margin, lock, x_next, Hbar).
     """
     H, a, pmax, margin = row_stats(z)
-    lock = pmax > cfg["lock"]
+    if cfg.get("lock_rule", "maxprob") == "entropy":
+        lock = H <= cfg["entropy_bound"]
+    else:
+        lock = pmax > cfg["lock"]
     pos = np.arange(z.shape[0])
     noise = philox.token_draw(seed, pos, step, block, req, z.shape[1])
     x_next = np.where(lock, a, noise)

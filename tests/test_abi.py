@@ -45,7 +45,9 @@ def test_config_validation_and_sizes():
                              ("n_kv_heads", 3, B.CD_ERR_INVALID_ARG), ("top_k", 9, B.CD_ERR_UNSUPPORTED),
                              ("d_model", 250, B.CD_ERR_UNSUPPORTED), ("max_ctx", 100, B.CD_ERR_INVALID_ARG),
                              ("weight_dtype", 7, B.CD_ERR_INVALID_ARG), ("attn_rescale_log2", -1.0, B.CD_ERR_INVALID_ARG),
-                             ("attn_rescale_log2", 65.0, B.CD_ERR_INVALID_ARG)]:
+                             ("attn_rescale_log2", 65.0, B.CD_ERR_INVALID_ARG), ("lock_rule", 2, B.CD_ERR_INVALID_ARG),
+                             ("entropy_bound", -0.5, B.CD_ERR_INVALID_ARG),
+                             ("entropy_bound", float("inf"), B.CD_ERR_INVALID_ARG)]:
         bad = _cfg()
         setattr(bad, field, val)
         with pytest.raises(B.CDError) as e:

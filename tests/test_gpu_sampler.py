@@ -17,14 +17,14 @@ from tests.gpu_util import announce
 pytestmark = pytest.mark.gpu
 
 
-def _cfg(V, C=256, max_steps=48):
-    w = synth_inputs.workload("tiny", V=V, C=C, max_steps=max_steps)
+def _cfg(V, C=256, max_steps=48, rule="maxprob"):
+    w = synth_inputs.workload("tiny", V=V, C=C, max_steps=max_steps, lock_rule=rule, entropy_bound=0.1)
     return B.make_config(w), w
 
 
-def run(z, seed=1, step=1, block=0, req0=0, prev=None, C=256, max_steps=48):
+def run(z, seed=1, step=1, block=0, req0=0, prev=None, C=256, max_steps=48, rule="maxprob"):
     rows, V = z.shape
-    cfg, w = _cfg(V, C, max_steps)
+    cfg, w = _cfg(V, C, max_steps, rule)
     dev = torch.device("cuda")
     zt = torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to(dev)
     tok = torch.empty(rows, dtype=torch.int32, device=dev)
@@ -63,6 +63,40 @@ def test_sampler_full_size_matches_oracle():
     assert g["info"][0].n_locked == int(ref["lock"].sum())
     assert g["info"][0].stop == 0 and g["info"][0].step == 1
     assert 0 < ref["lock"].sum() < 256
+
+
+def test_entropy_bound_rule_full_size_and_straddling_rows():
+    announce("sampler_entropy_bound", rows=256, V=262144)
+    z = synth_inputs.sampler_logits(256, 262144, 1)
+    g, w = run(z, seed=1, step=1, rule="entropy")
+    ref = osamp.sample(w, z, seed=1, step=1, block=0, req=0)
+    ok = np.abs(ref["H"] - 0.1) > 1e-3
+    assert np.array_equal(g["lock"][ok], ref["lock"][ok])
+    assert 0 < ref["lock"].sum() < 256 and g["info"][0].n_locked == int(g["lock"].sum())
+    decided = ref["margin"] > 1e-3
+    same = g["lock"] == ref["lock"]
+    assert np.array_equal(g["tokens"][same & (decided | ~g["lock"])], ref["x_next"][same & (decided | ~g["lock"])])
+    # two-level rows (one logit a, the rest 0) with closed-form entropy just
+    # above and just below the bound, the gap found by bisection
+    V = 4096
+
+    def H2(a):
+        p1 = math.exp(a) / (math.exp(a) + V - 1)
+        return -p1 * math.log(p1) - (1 - p1) * math.log((1 - p1) / (V - 1))
+    lo, hi = 0.0, 60.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        lo, hi = (mid, hi) if H2(mid) > 0.1 else (lo, mid)
+    gaps = hi + np.linspace(-0.2, 0.2, 256)
+    gaps = gaps[np.abs([H2(a) - 0.1 for a in gaps]) > 1e-4]
+    z = np.zeros((256, V), np.float32)
+    z[:, 99] = np.resize(gaps, 256)
+    g, _ = run(z, seed=5, step=3, rule="entropy")
+    want = np.array([H2(float(a)) <= 0.1 for a in z[:, 99]])
+    assert 50 < want.sum() < 206
+    assert np.array_equal(g["lock"], want)
+    noise = philox.token_draw(5, np.arange(256), 3, 0, 0, V)
+    assert np.array_equal(g["tokens"], np.where(want, 99, noise))
 
 
 def test_uniform_and_two_level_rows():

@@ -149,13 +149,16 @@ def test_tiny_copy_model_stops_at_pass_two_via_generate():
     eng.close()
 
 
-def test_tiny_mixed_lock_decisions_match_oracle():
-    w = synth_inputs.workload("tiny")
-    announce("tiny_mixed_lock", s=2.1)
+@pytest.mark.parametrize("rule,s", [("maxprob", 2.1), ("entropy", 2.65)])
+def test_tiny_mixed_lock_decisions_match_oracle(rule, s):
+    # copy-model scales chosen so that about half the positions lock at
+    # pass 1 under each rule (max prob > 0.9, or entropy <= 0.1 nats)
+    w = synth_inputs.workload("tiny", lock_rule=rule, entropy_bound=0.1)
+    announce("tiny_mixed_lock", rule=rule, s=s)
     eng = Engine(w)
     B.cd_synth_weights(eng.ctx, w["weight_seed"])
-    _copy_model_gpu(eng, w, 2.1)
-    W = _copy_model_oracle(w, 2.1)
+    _copy_model_gpu(eng, w, s)
+    W = _copy_model_oracle(w, s)
     prefix = synth_inputs.prefix_ids(w["V"], w["P0"], w["prefix_seed"])
     B.cd_prefill(eng.ctx, 0, torch.from_numpy(prefix).cuda())
     req = loop.Request(w)
@@ -169,7 +172,8 @@ def test_tiny_mixed_lock_decisions_match_oracle():
         info = eng.step_info()[0]
         assert rel_l2_rows(to_np(eng.logits()), ref["z"]).max() <= TOL
         lock = to_np(eng.view(B.CD_BUF_LOCK, torch.uint8, (1, w["C"]))[0]).astype(bool)
-        ok = np.abs(ref["pmax"] - w["lock"]) > 1e-3
+        ok = (np.abs(ref["pmax"] - w["lock"]) > 1e-3 if rule == "maxprob"
+              else np.abs(ref["H"] - w["entropy_bound"]) > 1e-3)
         assert np.array_equal(lock[ok], ref["lock"][ok])
         if t == 1:
             assert 20 < ref["lock"].sum() < 236

@@ -81,3 +81,31 @@ def test_lock_and_renoise():
     zz = np.zeros((1, 10)); zz[0, 0] = math.log(0.9 * 9 / 0.1)
     H, a, pmax, _ = sampler.row_stats(zz)
     assert abs(pmax[0] - 0.9) < 1e-15
+
+
+def test_entropy_bound_lock_rule():
+    # two-level rows whose closed-form entropy lies just above, at about, and
+    # just below the bound: kept exactly where H <= bound; the rest re-noised
+    V, bound = 4096, 0.1
+
+    def H2(a):
+        p1 = math.exp(a) / (math.exp(a) + V - 1)
+        return -p1 * math.log(p1) - (1 - p1) * math.log((1 - p1) / (V - 1))
+    lo, hi = 0.0, 60.0                             # H2 falls monotonically in a
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        lo, hi = (mid, hi) if H2(mid) > bound else (lo, mid)
+    gaps = [hi - 0.05, hi - 0.001, hi + 0.001, hi + 0.05, 1.0, 40.0]
+    z = np.zeros((len(gaps), V))
+    z[np.arange(len(gaps)), 777] = gaps
+    want = np.array([H2(a) <= bound for a in gaps])
+    assert list(want) == [False, False, True, True, False, True]
+    w = synth_inputs.workload("tiny", lock_rule="entropy", entropy_bound=bound)
+    out = sampler.sample(w, z, seed=3, step=2, block=1, req=5)
+    assert np.array_equal(out["lock"], want)
+    assert np.allclose(out["H"], [H2(a) for a in gaps], rtol=1e-10, atol=1e-14)
+    noise = sampler.philox.token_draw(3, np.arange(len(gaps)), 2, 1, 5, V)
+    assert np.array_equal(out["x_next"], np.where(want, 777, noise))
+    # the default rule on the same rows: max probability against 0.9
+    ref = sampler.sample(synth_inputs.workload("tiny"), z, seed=3, step=2, block=1, req=5)
+    assert np.array_equal(ref["lock"], ref["pmax"] > 0.9) and not np.array_equal(ref["lock"], want)
