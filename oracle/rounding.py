@@ -8,7 +8,9 @@ with saturation at +-448.
 
 Pins (tests/test_oracle_rounding.py): torch's CPU casts fp32 -> bfloat16 and
 fp32 -> float8_e4m3fn on every value where they apply, and exact rational
-arithmetic (``fractions``) for fp64 inputs that fp32 cannot hold.
+arithmetic (``fractions``) for fp64 inputs that fp32 cannot hold; for E2M1,
+brute force over the 15 representable values (nearest, ties to the even
+code) and the format's own examples of the MX block scale.
 """
 from __future__ import annotations
 
@@ -42,6 +44,39 @@ def round_e4m3(x):
     """fp64 -> nearest E4M3FN value (4 significant bits), saturating."""
     out = _round_sig(x, 4, -9)
     return np.clip(out, -E4M3_MAX, E4M3_MAX)
+
+
+E2M1_MAX = 6.0
+
+
+def round_e2m1(x):
+    """fp64 -> nearest E2M1 value (2 significant bits, smallest step 0.5:
+    0, 0.5, 1, 1.5, 2, 3, 4, 6), ties to even, saturating at +-6."""
+    out = _round_sig(x, 2, -1)
+    return np.clip(out, -E2M1_MAX, E2M1_MAX)
+
+
+def mx_scale_exp(amax):
+    """Shared exponent of an MXFP4 block with largest magnitude amax (OCP
+    Microscaling Formats v1.0): floor(log2 amax) minus 2, the exponent of the
+    largest E2M1 power of two, clamped to [-126, 127] (E8M0 reaches -127;
+    stopping at -126 keeps the scale a normal fp32 number); 0 for an all-zero
+    block."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))     # amax in [2^(e-1), 2^e)
+    return np.where(amax > 0, np.clip(e - 1 - 2, -126, 127), 0).astype(np.int64)
+
+
+def quantize_mxfp4(w):
+    """Rows w[n][K] (K a multiple of 32) -> (dequantised values, block
+    exponents [n][K/32]): each 32-element block shares the scale 2^e and its
+    elements are round_e2m1(w / 2^e)."""
+    w = np.asarray(w, dtype=np.float64)
+    n, K = w.shape
+    blk = w.reshape(n, K // 32, 32)
+    e = mx_scale_exp(np.max(np.abs(blk), axis=2))
+    q = round_e2m1(np.ldexp(blk, -e[:, :, None]))
+    return np.ldexp(q, e[:, :, None]).reshape(n, K), e
 
 
 def bf16_bits(v):

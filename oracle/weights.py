@@ -19,7 +19,10 @@ gate [fe][d], up [fe][d], down [d][fe], 5+3E+{0,1,2} shared gate/up/down.
 Storage: ``f32`` workloads keep fp32; ``bf16`` workloads keep bf16;
 ``fp8`` workloads keep Wq/Wk/Wv/Wo and routed experts as E4M3FN with a bf16
 scale per output row (s = bf16(max|w_row| / 448), q = e4m3(w / s)) and every
-other tensor in bf16.
+other tensor in bf16; ``mxfp4`` workloads keep the routed experts as MXFP4
+(one E8M0 scale 2^e per 32 input columns of a row, e = floor(log2 of the
+block's largest magnitude) - 2, elements rounded to E2M1), Wq/Wk/Wv/Wo as
+fp8 like the ``fp8`` workloads, and every other tensor in bf16.
 
 Pins (tests/test_oracle_weights.py): Kolmogorov-Smirnov against the normal CDF,
 the chi-square(2) law of z0^2 + z1^2 for each Box-Muller pair, independence of
@@ -30,7 +33,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import philox
-from .rounding import round_bf16, round_e4m3, round_fp32, E4M3_MAX
+from .rounding import round_bf16, round_e4m3, round_fp32, quantize_mxfp4, E4M3_MAX
 
 STD = 0.02
 
@@ -69,10 +72,14 @@ def tensor_shape(cfg, name):
 
 
 def storage(cfg, name) -> str:
-    """Storage format of a tensor: 'f32', 'bf16' or 'fp8'."""
+    """Storage format of a tensor: 'f32', 'bf16', 'fp8' or 'mxfp4'."""
     wd = cfg["wdtype"]
     if wd == "fp8":
         return "fp8" if name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd") else "bf16"
+    if wd == "mxfp4":
+        if name in ("wg", "wu", "wd"):
+            return "mxfp4"
+        return "fp8" if name in ("wq", "wk", "wv", "wo") else "bf16"
     return wd
 
 
@@ -108,7 +115,8 @@ def stored_rows(cfg, name, layer=None, expert=None, rows=None):
     """Stored values (as fp64) of selected rows, plus per-row fp8 scales.
 
     Returns (values, scales); scales is None unless the tensor is fp8, in which
-    case values are the dequantised q*s and scales the bf16 row scales.
+    case values are the dequantised q*s and scales the bf16 row scales, or
+    MXFP4, in which case scales are the block exponents [rows][K/32].
     """
     w = raw_rows(cfg, name, layer, expert, rows)
     fmt = storage(cfg, name)
@@ -116,6 +124,8 @@ def stored_rows(cfg, name, layer=None, expert=None, rows=None):
         return round_fp32(w), None
     if fmt == "bf16":
         return round_bf16(w), None
+    if fmt == "mxfp4":
+        return quantize_mxfp4(w)
     s = round_bf16(np.max(np.abs(w), axis=1) / E4M3_MAX)
     q = round_e4m3(w / s[:, None])
     return q * s[:, None], s

@@ -8,6 +8,7 @@ from fractions import Fraction
 import numpy as np
 import torch
 
+from oracle import rounding
 from oracle.rounding import (round_bf16, round_e4m3, round_fp32, bf16_bits,
                              bf16_from_bits, e4m3_bits, e4m3_from_bits, E4M3_MAX)
 
@@ -78,3 +79,46 @@ def test_e4m3_matches_torch_cast_within_range():
 
 def test_e4m3_saturates():
     assert round_e4m3(np.array([449.0, 470.0, 1e6, -1e6])).tolist() == [448.0, 448.0, 448.0, -448.0]
+
+
+def test_e2m1_nearest_by_brute_force():
+    # E2M1 (OCP Microscaling Formats v1.0): codes 0..7 are 0, 0.5, 1, 1.5, 2,
+    # 3, 4, 6; round to nearest, ties to the even code, saturate at +-6
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rng = np.random.default_rng(5)
+    mids = (grid[1:] + grid[:-1]) / 2
+    xs = np.concatenate([rng.uniform(-9, 9, 4000), mids, -mids, grid, -grid, [6.5, 7.0, 1e9, -7.99]])
+    for x in xs:
+        a = abs(x)
+        d = np.abs(grid - min(a, 6.0))
+        best = np.flatnonzero(d == d.min())
+        code = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+        want = np.copysign(grid[code], x)
+        got = float(rounding.round_e2m1(np.array([x]))[0])
+        assert got == want or (got == 0 and want == 0), (x, got, want)
+
+
+def test_mx_block_scale_and_quantize():
+    # the shared exponent puts the block's largest magnitude in [4, 8) before
+    # rounding; examples: max 6 -> 2^0, max 8 -> 2^1, max 0.08 -> 2^-6
+    assert list(rounding.mx_scale_exp(np.array([6.0, 7.9, 8.0, 0.08, 0.0]))) == [0, 0, 1, -6, 0]
+    rng = np.random.default_rng(6)
+    w = rng.normal(0, 0.02, (16, 128))
+    w[3, :32] = 0.0                                   # an all-zero block
+    v, e = rounding.quantize_mxfp4(w)
+    assert e.shape == (16, 4) and e[3, 0] == 0 and np.all(v[3, :32] == 0)
+    blk = w.reshape(16, 4, 32)
+    amax = np.abs(blk).max(axis=2)
+    nz = amax > 0
+    r = amax[nz] / np.ldexp(1.0, e[nz])
+    assert np.all((r >= 4) & (r < 8))
+    q = np.ldexp(v.reshape(16, 4, 32), -e[:, :, None])
+    grid = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}
+    assert set(np.abs(q).ravel().tolist()) <= grid
+    # error at most half the local step (the grid step is 0.5 below 2, 1
+    # below 4, 2 above), except saturated elements, which become +-6
+    x = np.ldexp(blk, -e[:, :, None])
+    step = np.where(np.abs(x) < 2, 0.5, np.where(np.abs(x) < 4, 1.0, 2.0))
+    sat = np.abs(x) > 6
+    assert np.all(np.abs(q - x)[~sat] <= step[~sat] / 2 + 1e-12)
+    assert np.all(np.abs(q[sat]) == 6)

@@ -9,7 +9,7 @@ from scipy import stats
 
 import synth_inputs
 from oracle import weights
-from oracle.rounding import bf16_bits, bf16_from_bits, e4m3_bits, e4m3_from_bits
+from oracle.rounding import bf16_bits, bf16_from_bits, e4m3_bits, e4m3_from_bits, quantize_mxfp4
 
 
 def test_normal_law_and_box_muller_pairs():
@@ -59,3 +59,12 @@ def test_storage_formats():
     assert np.array_equal(bf16_from_bits(bf16_bits(s8)), s8)
     # non-attention, non-expert tensors stay bf16 in fp8 models
     assert weights.storage(cfg8, "wr") == "bf16" and weights.storage(cfg8, "lm") == "bf16"
+
+    cfg4 = synth_inputs.workload("tiny", wdtype="mxfp4")
+    v4, e4 = weights.stored_rows(cfg4, "wd", 1, 2, rows=np.arange(8))
+    raw4 = weights.raw_rows(cfg4, "wd", 1, 2, rows=np.arange(8))
+    assert e4.shape == (8, cfg4["fe"] // 32)
+    v_ref, e_ref = quantize_mxfp4(raw4)
+    assert np.array_equal(v4, v_ref) and np.array_equal(e4, e_ref)
+    assert weights.storage(cfg4, "wg") == "mxfp4" and weights.storage(cfg4, "wq") == "fp8"
+    assert weights.storage(cfg4, "sg") == "bf16" and weights.storage(cfg4, "lm") == "bf16"
