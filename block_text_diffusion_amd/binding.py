@@ -17,7 +17,7 @@ c_int32, c_uint64, c_size_t, c_void_p, c_float, c_double = (
 
 CD_OK, CD_ERR_INVALID_ARG, CD_ERR_BAD_STATE, CD_ERR_CAPACITY, CD_ERR_HIP, CD_ERR_UNSUPPORTED, CD_ERR_NUMERIC = (
     0, -1, -2, -3, -4, -5, -6)
-CD_F32, CD_BF16, CD_FP8 = 0, 1, 2
+CD_F32, CD_BF16, CD_FP8, CD_MXFP4 = 0, 1, 2, 3
 CD_LOCK_MAXPROB, CD_LOCK_ENTROPY = 0, 1
 (CD_W_EMBED, CD_W_LM, CD_W_Q, CD_W_K, CD_W_V, CD_W_O, CD_W_ROUTER, CD_W_GATE, CD_W_UP, CD_W_DOWN,
  CD_W_SHARED_GATE, CD_W_SHARED_UP, CD_W_SHARED_DOWN) = range(13)
@@ -132,7 +132,7 @@ def _stream(stream):
 
 def make_config(w: dict, max_requests=None, max_ctx=None, max_prefill=None) -> cd_config:
     """cd_config from a workload dict (synth_inputs layout)."""
-    dt = {"f32": CD_F32, "bf16": CD_BF16, "fp8": CD_FP8}[w["wdtype"]]
+    dt = {"f32": CD_F32, "bf16": CD_BF16, "fp8": CD_FP8, "mxfp4": CD_MXFP4}[w["wdtype"]]
     R = max_requests or w.get("R", 1)
     P0 = w.get("P0", 0)
     return cd_config(

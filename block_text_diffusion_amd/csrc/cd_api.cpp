@@ -68,6 +68,7 @@ struct Plan {
   int Tmax;                // rows of the largest forward
   int qkv_npad, wo_npad, wr_npad, gu_npad, dn_npad, sgu_npad, sdn_npad, lm_npad;
   int64_t gu_stride, dn_stride;        // bytes per expert
+  int64_t gu_mx, dn_mx;                // MXFP4: offset of an expert's scales in its stride
   // weights
   int64_t embed, lm;
   std::vector<LayerOff> layer;
@@ -87,7 +88,7 @@ int32_t validate_config(const cd_config* c) {
       c->n_experts < 1 || c->top_k < 1 || c->expert_hidden < 1 || c->shared_hidden < 0 || c->vocab < 1 ||
       c->canvas_len < 1 || c->max_steps < 1 || c->max_requests < 1 || c->max_ctx < 1 || c->max_prefill < 1)
     return fail(CD_ERR_INVALID_ARG, "config fields must be positive");
-  if (c->weight_dtype < CD_F32 || c->weight_dtype > CD_FP8) return fail(CD_ERR_INVALID_ARG, "bad weight_dtype");
+  if (c->weight_dtype < CD_F32 || c->weight_dtype > CD_MXFP4) return fail(CD_ERR_INVALID_ARG, "bad weight_dtype");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(CD_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c->n_q_heads % c->n_kv_heads) return fail(CD_ERR_INVALID_ARG, "n_q_heads %% n_kv_heads != 0");
   if (c->n_q_heads / c->n_kv_heads > 4 || c->n_q_heads / c->n_kv_heads == 3)
@@ -119,9 +120,12 @@ int sampler_chunks(int V) {
 Plan make_plan(const cd_config& c) {
   Plan p;
   p.c = c;
-  p.wdt_attn = c.weight_dtype;
+  // CD_FP8: attention and experts fp8; CD_MXFP4: attention fp8, experts
+  // MXFP4; everything else bf16 in both
+  const bool narrow = c.weight_dtype == CD_FP8 || c.weight_dtype == CD_MXFP4;
+  p.wdt_attn = narrow ? CD_FP8 : c.weight_dtype;
   p.wdt_exp = c.weight_dtype;
-  p.wdt_other = c.weight_dtype == CD_FP8 ? CD_BF16 : c.weight_dtype;
+  p.wdt_other = narrow ? CD_BF16 : c.weight_dtype;
   p.adt = c.weight_dtype == CD_F32 ? CD_F32 : CD_BF16;
   p.ctx = (int)round_up(c.max_ctx, 64);
   const int C = c.canvas_len, d = c.d_model, dh = c.head_dim, L = c.n_layers, E = c.n_experts;
@@ -134,9 +138,12 @@ Plan make_plan(const cd_config& c) {
   p.sgu_npad = 2 * c.shared_hidden;
   p.sdn_npad = (int)round_up(d, 32);
   p.lm_npad = (int)round_up(c.vocab, 32);
-  const bool f8 = c.weight_dtype == CD_FP8;
-  p.gu_stride = round_up(packed_bytes(p.gu_npad, d, p.wdt_exp), ALIGN);
-  p.dn_stride = round_up(packed_bytes(p.dn_npad, c.expert_hidden, p.wdt_exp), ALIGN);
+  const bool f8 = p.wdt_attn == CD_FP8, f8e = p.wdt_exp == CD_FP8;
+  // an expert's stride holds its packed tiles and, for MXFP4, their scales
+  p.gu_stride = round_up(packed_total(p.gu_npad, d, p.wdt_exp), ALIGN);
+  p.dn_stride = round_up(packed_total(p.dn_npad, c.expert_hidden, p.wdt_exp), ALIGN);
+  p.gu_mx = packed_bytes(p.gu_npad, d, p.wdt_exp);
+  p.dn_mx = packed_bytes(p.dn_npad, c.expert_hidden, p.wdt_exp);
 
   Carve w;
   p.embed = w.take((int64_t)c.vocab * d * esize(p.wdt_other));
@@ -150,9 +157,9 @@ Plan make_plan(const cd_config& c) {
     o.wo_s = f8 ? w.take(p.wo_npad * 4) : -1;
     o.wr = w.take(packed_bytes(p.wr_npad, d, p.wdt_other));
     o.gu = w.take(p.gu_stride * E);
-    o.gu_s = f8 ? w.take((int64_t)p.gu_npad * 4 * E) : -1;
+    o.gu_s = f8e ? w.take((int64_t)p.gu_npad * 4 * E) : -1;
     o.dn = w.take(p.dn_stride * E);
-    o.dn_s = f8 ? w.take((int64_t)p.dn_npad * 4 * E) : -1;
+    o.dn_s = f8e ? w.take((int64_t)p.dn_npad * 4 * E) : -1;
     o.sgu = c.shared_hidden ? w.take(packed_bytes(p.sgu_npad, d, p.wdt_other)) : -1;
     o.sdn = c.shared_hidden ? w.take(packed_bytes(p.sdn_npad, c.shared_hidden, p.wdt_other)) : -1;
   }
@@ -486,14 +493,14 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       GemmArgs a = gemm_base(u, d, c->W + lw.gu, c->wt<float>(lw.gu_s), d, p.gu_npad, 2 * g.expert_hidden,
                              c->st<void>(p.aperm), g.expert_hidden);
       a.row_map = c->st<int32_t>(p.row_map);
-      a.w_gstride = p.gu_stride; a.s_gstride = p.gu_npad;
+      a.w_gstride = p.gu_stride; a.s_gstride = p.gu_npad; a.mx_off = p.gu_mx;
       PROF(CD_PROF_EXPERT_GU);
       gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, (int64_t)T * k, s);
     }
     {
       GemmArgs a = gemm_base(c->st<void>(p.aperm), g.expert_hidden, c->W + lw.dn, c->wt<float>(lw.dn_s),
                              g.expert_hidden, p.dn_npad, d, c->st<void>(p.yperm), d);
-      a.w_gstride = p.dn_stride; a.s_gstride = p.dn_npad;
+      a.w_gstride = p.dn_stride; a.s_gstride = p.dn_npad; a.mx_off = p.dn_mx;
       PROF(CD_PROF_EXPERT_DOWN);
       gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, s);
     }
@@ -617,12 +624,13 @@ PackDesc desc_for(const cd_ctx* c, int kind, int layer, int expert, int& status)
     case CD_W_GATE: case CD_W_UP:
       d.dst = W + lw->gu + p.gu_stride * expert;
       d.scale = lw->gu_s >= 0 ? c->wt<float>(lw->gu_s) + (int64_t)p.gu_npad * expert : nullptr;
-      d.dt = p.wdt_exp; d.perm = PERM_GU; d.Npad = p.gu_npad; d.K = dm;
+      d.dt = p.wdt_exp; d.perm = PERM_GU; d.Npad = p.gu_npad; d.K = dm; d.mx_off = p.gu_mx;
       d.n_rows_src[0] = d.n_rows_src[1] = g.expert_hidden; d.only_sel = kind - CD_W_GATE; break;
     case CD_W_DOWN:
       d.dst = W + lw->dn + p.dn_stride * expert;
       d.scale = lw->dn_s >= 0 ? c->wt<float>(lw->dn_s) + (int64_t)p.dn_npad * expert : nullptr;
-      d.dt = p.wdt_exp; d.perm = PERM_NONE; d.Npad = p.dn_npad; d.K = g.expert_hidden; d.n_rows_src[0] = dm; break;
+      d.dt = p.wdt_exp; d.perm = PERM_NONE; d.Npad = p.dn_npad; d.K = g.expert_hidden; d.n_rows_src[0] = dm;
+      d.mx_off = p.dn_mx; break;
     case CD_W_SHARED_GATE: case CD_W_SHARED_UP:
       d.dst = W + lw->sgu; d.dt = p.wdt_other; d.perm = PERM_GU; d.Npad = p.sgu_npad; d.K = dm;
       d.n_rows_src[0] = d.n_rows_src[1] = g.shared_hidden; d.only_sel = kind - CD_W_SHARED_GATE; break;

@@ -9,7 +9,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_FP4 = 3 };
 
 // ---- bf16 -------------------------------------------------------------
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }

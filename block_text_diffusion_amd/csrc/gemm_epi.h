@@ -52,6 +52,32 @@ __device__ __forceinline__ void widen_fp8(const u32x4& w, u32x4 (&wb)[2]) {
     wb[h][3] = fp8x2_hi(w[2 * h + 1]);
   }
 }
+// MXFP4 weight fragment -> two bf16 operand fragments.  w[0], w[1]: the
+// lane's 8 code bytes (16 E2M1 values, even column in the low nibble), w[2]:
+// its E8M0 scale byte.  The hardware conversion turns byte b of a word into
+// the bf16 pair (low nibble, high nibble) times the scale, exactly.
+__device__ __forceinline__ uint32_t fp4x2(uint32_t v, float s, int b) {
+  switch (b) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3));
+  }
+}
+__device__ __forceinline__ void widen_fp4(const u32x4& w, u32x4 (&wb)[2]) {
+  const float s = __uint_as_float(w[2] << 23);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) wb[h][b] = fp4x2(w[h], s, b);
+}
+// one MXFP4 tile fragment: 8 code bytes at p, the scale byte at ps
+__device__ __forceinline__ u32x4 load_fp4(const uint8_t* p, const uint8_t* ps) {
+  const uint2 c = *reinterpret_cast<const uint2*>(p);
+  u32x4 r;
+  r[0] = c.x; r[1] = c.y; r[2] = *ps; r[3] = 0;
+  return r;
+}
 __device__ __forceinline__ f32x4 mma_bf16(const u32x4& a, const u32x4& b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
@@ -68,7 +94,8 @@ __device__ __forceinline__ f32x4 mma_tile(const u32x4& w, const u32x4* x, f32x4 
                                                   __builtin_bit_cast(bf16x8, x[0]), acc, 0, 0, 0);
   } else {
     u32x4 wb[2];
-    widen_fp8(w, wb);
+    if constexpr (WT == DT_FP4) widen_fp4(w, wb);
+    else widen_fp8(w, wb);
     acc = mma_bf16(wb[0], x[0], acc);
     acc = mma_bf16(wb[1], x[1], acc);
   }

@@ -44,14 +44,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   static_assert(EPI != EPI_SWIGLU || NTW == 2, "SwiGLU needs gate and up tiles in one wave");
   constexpr int MROWS = 16 * MT;
   constexpr int U = 4;
-  constexpr int XW = (WT == DT_FP8) ? 2 : 1;        // 16-byte activation loads per k-tile
-  constexpr int XSTEP = (WT == DT_FP8) ? 128 : 64;  // activation bytes per k-tile
+  constexpr bool F4 = WT == DT_FP4;                 // MXFP4: 512-byte tiles + a scale byte per lane
+  constexpr int TB = F4 ? 512 : 1024;               // bytes per weight tile
+  constexpr int XW = (WT >= DT_FP8) ? 2 : 1;        // 16-byte activation loads per k-tile
+  constexpr int XSTEP = (WT >= DT_FP8) ? 128 : 64;  // activation bytes per k-tile
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
   constexpr int NFR = MT * U * XW;        // 1 KB activation fragments per stage
   constexpr int FPW = NFR / NW;           // fragments each wave copies
   constexpr int STG = NFR * 1024;
   constexpr int XBUF = 3;
-  constexpr int LPS = FPW + NTW * U;      // vector loads per wave per stage
+  constexpr int LPS = FPW + NTW * U * (F4 ? 2 : 1);   // vector loads per wave per stage
   static_assert(NFR % NW == 0, "stage fragments");
   __shared__ __attribute__((aligned(1024))) uint8_t xs[XBUF * STG];
 
@@ -112,7 +114,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   const int kt_beg = (int)((int64_t)KTall * ks / ksplit);
   const int KT = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt_beg;   // k-tiles of this split
   const int nst = (KT + U - 1) / U;                                      // stages of U k-tiles
-  const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)ntc * KTall + kt_beg) * 1024 + lane * 16;
+  const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)ntc * KTall + kt_beg) * TB + lane * (TB / 64);
+  const uint8_t* mxp0 = a.W + (int64_t)group * a.w_gstride + a.mx_off + ((int64_t)ntc * KTall + kt_beg) * 32 +
+                        (lane & 15) * 2 + (lane >> 5);
   const int esa = (AT == DT_F32) ? 4 : 2;
   // this wave's share of the activation fragments of a stage: fragment
   // f = (mt*U + u)*XW + h holds rows mt*16.. at k-tile u (half h for fp8)
@@ -153,8 +157,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
     for (int u = 0; u < U; ++u) {
       const int kk = min(kt + u, KT - 1);
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        ww[j][u] = *reinterpret_cast<const u32x4*>(wp0 + ((int64_t)j * KTall + kk) * 1024);
+      for (int j = 0; j < NTW; ++j) {
+        if constexpr (F4)
+          ww[j][u] = load_fp4(wp0 + ((int64_t)j * KTall + kk) * TB, mxp0 + ((int64_t)j * KTall + kk) * 32);
+        else
+          ww[j][u] = *reinterpret_cast<const u32x4*>(wp0 + ((int64_t)j * KTall + kk) * 1024);
+      }
     }
   };
   auto compute = [&](const u32x4 (&ww)[NTW][U], int st) {
@@ -163,11 +171,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u < nu) {
-        if constexpr (WT == DT_FP8) {
-          // widen the fp8 weight fragments once for all row tiles
+        if constexpr (WT >= DT_FP8) {
+          // widen the fp8 / MXFP4 weight fragments once for all row tiles
           u32x4 wb[NTW][2];
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) widen_fp8(ww[j][u], wb[j]);
+          for (int j = 0; j < NTW; ++j) {
+            if constexpr (F4) widen_fp4(ww[j][u], wb[j]);
+            else widen_fp8(ww[j][u], wb[j]);
+          }
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -276,12 +287,17 @@ static void run_nw(const GemmArgs& a, hipStream_t s) {
 
 template <int WT, int AT, int MT>
 static void run_epi(int epi, const GemmArgs& a, hipStream_t s) {
-  switch (epi) {
-    case EPI_F32: run_nw<WT, AT, MT, EPI_F32>(a, s); break;
-    case EPI_ROWS: run_nw<WT, AT, MT, EPI_ROWS>(a, s); break;
-    case EPI_RESID: run_nw<WT, AT, MT, EPI_RESID>(a, s); break;
-    case EPI_SWIGLU: run_nw<WT, AT, MT, EPI_SWIGLU>(a, s); break;
-    case EPI_QKV: run_nw<WT, AT, MT, EPI_QKV>(a, s); break;
+  if constexpr (WT == DT_FP4) {   // routed experts only
+    if (epi == EPI_SWIGLU) run_nw<WT, AT, MT, EPI_SWIGLU>(a, s);
+    else run_nw<WT, AT, MT, EPI_ROWS>(a, s);
+  } else {
+    switch (epi) {
+      case EPI_F32: run_nw<WT, AT, MT, EPI_F32>(a, s); break;
+      case EPI_ROWS: run_nw<WT, AT, MT, EPI_ROWS>(a, s); break;
+      case EPI_RESID: run_nw<WT, AT, MT, EPI_RESID>(a, s); break;
+      case EPI_SWIGLU: run_nw<WT, AT, MT, EPI_SWIGLU>(a, s); break;
+      case EPI_QKV: run_nw<WT, AT, MT, EPI_QKV>(a, s); break;
+    }
   }
 }
 
@@ -297,7 +313,8 @@ static void run_mt(int mt, int epi, const GemmArgs& a, hipStream_t s) {
 void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s) {
   if (wdt == DT_F32) run_mt<DT_F32, DT_F32>(mt, epi, a, s);
   else if (wdt == DT_BF16) run_mt<DT_BF16, DT_BF16>(mt, epi, a, s);
-  else run_mt<DT_FP8, DT_BF16>(mt, epi, a, s);
+  else if (wdt == DT_FP8) run_mt<DT_FP8, DT_BF16>(mt, epi, a, s);
+  else run_mt<DT_FP4, DT_BF16>(mt, epi, a, s);
 }
 
 }  // namespace cd

@@ -39,9 +39,11 @@ constexpr int XNTW = 4;   // weight tiles per wave: a workgroup covers 256 colum
 template <int WT, int AT, int EPI>
 __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
-  constexpr int XW = (WT == DT_FP8) ? 2 : 1;          // 1 KB activation fragments per k-tile and row tile
-  constexpr int XSTEP = (WT == DT_FP8) ? 128 : 64;    // activation bytes per k-tile (per lane group)
-  constexpr bool WLDS = WT != DT_FP8;                 // weights staged in LDS
+  constexpr bool F4 = WT == DT_FP4;                   // MXFP4: 512-byte tiles + a scale byte per lane
+  constexpr int TB = F4 ? 512 : 1024;                 // bytes per weight tile
+  constexpr int XW = (WT >= DT_FP8) ? 2 : 1;          // 1 KB activation fragments per k-tile and row tile
+  constexpr int XSTEP = (WT >= DT_FP8) ? 128 : 64;    // activation bytes per k-tile (per lane group)
+  constexpr bool WLDS = WT < DT_FP8;                  // weights staged in LDS
   constexpr int NBUF = WLDS ? 4 : 2;
   constexpr int DIST = NBUF - 1;
   constexpr int BLK = XMT * XW;                       // activation fragments per stage
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   constexpr int WFR = WLDS ? 4 * XNTW : 0;            // weight fragments per stage in LDS (256 columns)
   constexpr int WPW = WFR / XWAVES;                   // weight fragments each wave copies
   constexpr int NWP = WLDS ? WPW : XNTW;              // weight streams of this wave
-  constexpr int LPS = BPW + NWP;                      // vector loads per wave per stage
+  constexpr int LPS = BPW + NWP * (F4 ? 2 : 1);       // vector loads per wave per stage
   __shared__ __attribute__((aligned(1024))) uint8_t xs[NBUF][(BLK + WFR) * 1024];
 
   const int lane = threadIdx.x & 63;
@@ -101,10 +103,12 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   // LDS-staged weights: this wave copies fragments wave*WPW.. of the
   // chunk's 16 tiles; else it loads its own four tiles nt0.. into registers
   const uint8_t* wp[NWP];
+  const uint8_t* mxp[NWP];
 #pragma unroll
   for (int j = 0; j < NWP; ++j) {
     const int t = WLDS ? chunk * 4 * XNTW + wave * WPW + j : nt0 + j;
-    wp[j] = wbase + ((int64_t)min(t, a.Nt - 1) * KTall + kt0) * 1024 + lane * 16;
+    wp[j] = wbase + ((int64_t)min(t, a.Nt - 1) * KTall + kt0) * TB + lane * (TB / 64);
+    mxp[j] = wbase + a.mx_off + ((int64_t)min(t, a.Nt - 1) * KTall + kt0) * 32 + (lane & 15) * 2 + (lane >> 5);
   }
   // rows past the tile's end read its last row (finite); their results are dropped
   const uint8_t* xsrc[BPW];
@@ -146,7 +150,10 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   auto issue_w = [&](u32x4 (&ww)[XNTW], int s) {
     const int sc = min(s, nst - 1);
 #pragma unroll
-    for (int j = 0; j < XNTW; ++j) ww[j] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)sc * 1024);
+    for (int j = 0; j < XNTW; ++j) {
+      if constexpr (F4) ww[j] = load_fp4(wp[j] + (int64_t)sc * TB, mxp[j] + (int64_t)sc * 32);
+      else ww[j] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)sc * 1024);
+    }
   };
   // all 16 row tiles are computed: rows past M hold copies of row M-1 (finite)
   // and their results are dropped, which keeps the loop free of branches
@@ -165,11 +172,14 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
         x[h] = *reinterpret_cast<const u32x4*>(buf + (((wm * XMTW + mt) * XW + h) * 64 + lane) * 16);
     };
     rd(xa, 0);
-    if constexpr (WT == DT_FP8) {
-      // widen the fp8 weight fragments once for all row tiles
+    if constexpr (WT >= DT_FP8) {
+      // widen the fp8 / MXFP4 weight fragments once for all row tiles
       u32x4 wb[XNTW][2];
 #pragma unroll
-      for (int j = 0; j < XNTW; ++j) widen_fp8(ww[j], wb[j]);
+      for (int j = 0; j < XNTW; ++j) {
+        if constexpr (F4) widen_fp4(ww[j], wb[j]);
+        else widen_fp8(ww[j], wb[j]);
+      }
 #pragma unroll
       for (int mt = 0; mt < XMTW; mt += 2) {
         rd(xb, mt + 1);
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
     // order: weight reads and reads of tile 0, then (reads of tile mt+1,
     // MFMAs of tile mt)
     constexpr int RD = XW;                                                     // DS reads per tile
-    constexpr int MF = XNTW * (WT == DT_F32 ? 4 : (WT == DT_FP8 ? 2 : 1));     // MFMAs per tile
+    constexpr int MF = XNTW * (WT == DT_F32 ? 4 : (WT >= DT_FP8 ? 2 : 1));     // MFMAs per tile
     __builtin_amdgcn_sched_group_barrier(0x100, (WLDS ? XNTW : 0) + RD, 0);
 #pragma unroll
     for (int mt = 0; mt + 1 < XMTW; ++mt) {
@@ -272,19 +282,25 @@ static void run_x(const GemmArgs& a, hipStream_t s) {
 
 template <int WT, int AT>
 static void run_x_epi(int epi, const GemmArgs& a, hipStream_t s) {
-  switch (epi) {
-    case EPI_F32: run_x<WT, AT, EPI_F32>(a, s); break;
-    case EPI_RESID: run_x<WT, AT, EPI_RESID>(a, s); break;
-    case EPI_SWIGLU: run_x<WT, AT, EPI_SWIGLU>(a, s); break;
-    case EPI_QKV: run_x<WT, AT, EPI_QKV>(a, s); break;
-    case EPI_ROWS: run_x<WT, AT, EPI_ROWS>(a, s); break;
+  if constexpr (WT == DT_FP4) {   // routed experts only
+    if (epi == EPI_SWIGLU) run_x<WT, AT, EPI_SWIGLU>(a, s);
+    else run_x<WT, AT, EPI_ROWS>(a, s);
+  } else {
+    switch (epi) {
+      case EPI_F32: run_x<WT, AT, EPI_F32>(a, s); break;
+      case EPI_RESID: run_x<WT, AT, EPI_RESID>(a, s); break;
+      case EPI_SWIGLU: run_x<WT, AT, EPI_SWIGLU>(a, s); break;
+      case EPI_QKV: run_x<WT, AT, EPI_QKV>(a, s); break;
+      case EPI_ROWS: run_x<WT, AT, EPI_ROWS>(a, s); break;
+    }
   }
 }
 
 void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s) {
   if (wdt == DT_F32) run_x_epi<DT_F32, DT_F32>(epi, a, s);
   else if (wdt == DT_BF16) run_x_epi<DT_BF16, DT_BF16>(epi, a, s);
-  else run_x_epi<DT_FP8, DT_BF16>(epi, a, s);
+  else if (wdt == DT_FP8) run_x_epi<DT_FP8, DT_BF16>(epi, a, s);
+  else run_x_epi<DT_FP4, DT_BF16>(epi, a, s);
 }
 
 }  // namespace cd

@@ -5,7 +5,10 @@
 // seed) through Box-Muller in fp64 -- words (r0, r1) feed elements 4q and
 // 4q+1 (cosine, sine), (r2, r3) feed 4q+2 and 4q+3 -- rounded once from fp64
 // to the storage format (fp32, bf16, or E4M3FN with a bf16 scale per output
-// row equal to bf16(max|w_row| / 448)).  The kernel writes the packed MFMA
+// row equal to bf16(max|w_row| / 448), or MXFP4: E2M1 codes with one E8M0
+// scale 2^e per 32 columns of a row, e = floor(log2(max|w_block|)) - 2 (the
+// largest E2M1 power of two is 2^2; OCP Microscaling Formats v1.0), codes
+// round(w / 2^e) to nearest even, saturating at +-6).  The kernel writes the packed MFMA
 // layout directly; packed rows are permuted so that the rotary pairs (i,
 // i+dh/2) of Q and K heads, and the gate/up rows of SwiGLU FFNs, land in the
 // same lane (see the row maps below).
@@ -71,6 +74,30 @@ __device__ __forceinline__ uint32_t e4m3_encode(double v) {  // v exactly E4M3
   return s | (ex << 3) | mant;
 }
 
+// fp64 value already on the E2M1 grid -> 4-bit code (sign in bit 3; -0 -> 0)
+__device__ __forceinline__ uint32_t e2m1_encode(double v) {
+  const uint32_t s = v < 0 ? 8u : 0u;
+  const double a = fabs(v);
+  if (a == 0.0) return 0u;
+  if (a == 0.5) return s | 1u;
+  int e;
+  const double m = frexp(a, &e);      // a = m * 2^e: biased exponent e, mantissa bit (2m - 1) * 2
+  return s | ((uint32_t)e << 1) | (uint32_t)((m * 2.0 - 1.0) * 2.0);
+}
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+  const float mag = (c & 6u) ? __uint_as_float(((((c >> 1) & 3u) + 126u) << 23) | ((c & 1u) << 22))
+                             : 0.5f * (float)(c & 1u);
+  return (c & 8u) ? -mag : mag;
+}
+// byte offsets of the 8-byte lane chunk holding columns k..k+15 (k % 16 == 0)
+// of packed row p, and of the scale of the 32-column block holding column k
+__device__ __forceinline__ int64_t fp4_chunk(int p, int k, int KT) {
+  return ((((int64_t)(p >> 4) * KT + k / 64) * 64) + (p & 15) + 16 * ((k % 64) / 16)) * 8;
+}
+__device__ __forceinline__ int64_t fp4_scale(int p, int k, int KT) {
+  return ((int64_t)(p >> 4) * KT + k / 64) * 32 + (p & 15) * 2 + (k % 64) / 32;
+}
+
 __device__ __forceinline__ void synth4(uint64_t seed, uint32_t tau, uint64_t q, double w[4]) {
   u4 c = {(uint32_t)q, (uint32_t)(q >> 32), tau, 1u << 24};
   u4 r = philox(c, (uint32_t)seed, (uint32_t)(seed >> 32));
@@ -125,6 +152,65 @@ __global__ __launch_bounds__(256) void k_pack(PackDesc d, int64_t dst_gstride, i
   if (d.only_sel >= 0 && sel != d.only_sel) return;
   const int K = d.K;
   const int nq = K / 4;
+
+  if (d.dt == DT_FP4) {
+    // one thread per 32-column block: scale, codes, two 8-byte lane chunks
+    const int KT = K / 64;
+    uint8_t* mx = dst + d.mx_off;
+    const float* src = sel == 0 ? s0 : sel == 1 ? s1 : s2;
+    float* out = sel == 0 ? o0 : sel == 1 ? o1 : o2;
+    const uint32_t tau = sel >= 0 ? d.tau[sel] + (uint32_t)(g * tau_gstride) : 0;
+    for (int b = threadIdx.x; b < K / 32; b += 256) {
+      const int k0 = 32 * b;
+      if (MODE == MODE_UNPACK) {
+        if (sel < 0) return;
+        const float sc = __uint_as_float((uint32_t)mx[fp4_scale(p, k0, KT)] << 23);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint2 c = *reinterpret_cast<const uint2*>(dst + fp4_chunk(p, k0 + 16 * h, KT));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t word = i < 8 ? c.x : c.y;
+            out[(int64_t)n * K + k0 + 16 * h + i] = e2m1_decode((word >> (4 * (i & 7))) & 15u) * sc;
+          }
+        }
+        continue;
+      }
+      double w[32];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (sel < 0) {
+          w[4 * j] = w[4 * j + 1] = w[4 * j + 2] = w[4 * j + 3] = 0.0;
+        } else if (MODE == MODE_SYNTH) {
+          synth4(seed, tau, ((uint64_t)n * K) / 4 + 8 * b + j, w + 4 * j);
+        } else {
+          const float4 f = *reinterpret_cast<const float4*>(src + (int64_t)n * K + k0 + 4 * j);
+          w[4 * j] = f.x; w[4 * j + 1] = f.y; w[4 * j + 2] = f.z; w[4 * j + 3] = f.w;
+        }
+      }
+      double amax = 0.0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(w[i]));
+      int e = 0;
+      if (amax > 0.0) {
+        frexp(amax, &e);                  // amax in [2^(e-1), 2^e): floor(log2 amax) = e - 1
+        e = min(max(e - 3, -126), 127);   // -126: the scale stays a normal fp32 number
+      }
+      mx[fp4_scale(p, k0, KT)] = (uint8_t)(e + 127);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint2 c = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const double q = fmin(fmax(round_sig(ldexp(w[16 * h + i], -e), 2, -1), -6.0), 6.0);
+          const uint32_t code = e2m1_encode(q) << (4 * (i & 7));
+          if (i < 8) c.x |= code; else c.y |= code;
+        }
+        *reinterpret_cast<uint2*>(dst + fp4_chunk(p, k0 + 16 * h, KT)) = c;
+      }
+    }
+    return;
+  }
 
   if (MODE == MODE_UNPACK) {
     if (sel < 0) return;

@@ -13,11 +13,24 @@ namespace cd {
 // of the element (fp32 16, bf16 32, fp8 64).  One 16-byte load per lane then
 // fetches a whole tile as one contiguous 1 KB wave access, already in MFMA
 // operand order.  N is padded to a multiple of 32 (zero rows).
+//
+// MXFP4 (dtype 3, routed experts only): E2M1 codes, two per byte (the even
+// column in the low nibble), in 16-row x 64-column tiles of 512 bytes; lane l
+// holds the 8 bytes of row nt*16 + l%16, columns kt*64 + (l/16)*16 + [0, 16).
+// Each row has one E8M0 scale (2^(byte - 127)) per 32 columns; the scales
+// follow the tiles, 32 bytes per tile (nt, kt) at mx_offset + (nt * KT + kt)
+// * 32 + (row % 16) * 2 + (column % 64) / 32, so lane l's scale is byte
+// (l % 16) * 2 + l / 32 of its tile's 32.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int esize(int dt) { return dt == 0 ? 4 : dt == 1 ? 2 : 1; }
 __host__ __device__ inline int kfrag(int dt) { return 64 / esize(dt); }
+// bytes of the packed tiles (MXFP4: codes only; the scales follow at this offset)
 __host__ __device__ inline int64_t packed_bytes(int64_t Npad, int64_t K, int dt) {
-  return Npad * K * esize(dt);
+  return dt == 3 ? Npad * K / 2 : Npad * K * esize(dt);
+}
+// packed bytes including MXFP4 scales
+__host__ __device__ inline int64_t packed_total(int64_t Npad, int64_t K, int dt) {
+  return packed_bytes(Npad, K, dt) + (dt == 3 ? Npad * K / 32 : 0);
 }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -36,6 +49,7 @@ struct GemmArgs {
   int64_t w_gstride;       // bytes between groups
   const float* wscale;     // fp8 per-row scales [group][Npad], or null
   int64_t s_gstride;
+  int64_t mx_off;          // MXFP4: bytes from a group's tiles to its E8M0 scales
   int K, Nt, N, n_chunks;  // Nt = packed 16-row tiles; N = logical outputs
   // work tiles: grouped (device table) or dense (M rows)
   const int32_t* tiles;    // [max_tiles][4]: group, row0, rows, 0
@@ -67,6 +81,7 @@ void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s);
 struct PackDesc {
   uint8_t* dst;        // packed tiles (or row-major for embedding)
   float* scale;        // fp8 per-row scales or null
+  int64_t mx_off;      // MXFP4: bytes from dst to the E8M0 scales
   int dt;              // storage dtype
   int perm;            // PERM_*
   int Npad, K;

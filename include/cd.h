@@ -57,8 +57,14 @@ enum {
 
 /* Weight storage formats.  CD_FP8 stores attention projections and routed
  * experts as OCP E4M3FN with one bf16 scale per output row and every other
- * tensor as bf16; activations are then bf16. */
-enum { CD_F32 = 0, CD_BF16 = 1, CD_FP8 = 2 };
+ * tensor as bf16; activations are then bf16.  CD_MXFP4 stores the routed
+ * experts as MXFP4 (OCP Microscaling Formats v1.0: E2M1 elements, one E8M0
+ * scale 2^e per 32 contraction elements of a row, e = floor(log2(max|w|))
+ * - 2, elements round(w / 2^e) to nearest even saturating at +-6), the
+ * attention projections as E4M3FN like CD_FP8, and everything else bf16;
+ * the pages list a 4-bit checkpoint (NVFP4, an NVIDIA format) beside BF16
+ * and FP8, and MXFP4 is the 4-bit format gfx950 converts natively. */
+enum { CD_F32 = 0, CD_BF16 = 1, CD_FP8 = 2, CD_MXFP4 = 3 };
 
 /* Lock rule of the sampler.  CD_LOCK_MAXPROB: a position keeps its argmax
  * when its max probability exceeds lock_threshold (the canvas explainer
@@ -87,7 +93,7 @@ typedef struct cd_config {
   float stop_entropy;     /* stop when mean canvas entropy < this (0.005) */
   float rms_eps;          /* RMSNorm epsilon */
   float rope_theta;       /* rotary base; 0 disables rotary embedding */
-  int32_t weight_dtype;   /* CD_F32, CD_BF16 or CD_FP8 */
+  int32_t weight_dtype;   /* CD_F32, CD_BF16, CD_FP8 or CD_MXFP4 */
   int32_t max_requests;   /* requests denoised together (<= 256) */
   int32_t max_ctx;        /* KV capacity per request, tokens */
   int32_t max_prefill;    /* largest single prefill call, tokens */

@@ -27,7 +27,7 @@ def to_np(t):
     return t.detach().cpu().numpy()
 
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "mxfp4": 6e-2}
 
 
 def check_routing(gpu_ids, oracle_trace, k, band):

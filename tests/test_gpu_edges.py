@@ -126,7 +126,7 @@ def test_capacity_boundary_prefill_and_blocks_fill_cache_exactly():
         assert rel_l2_rows(Kg.reshape(-1, w["dh"]), Ko.reshape(-1, w["dh"])).max() <= TOL["f32"], l
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16"])
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "mxfp4"])
 def test_prefill_with_large_expert_tiles(wdtype):
     # 1024 prompt tokens x top-2 over 8 experts: 256 or more rows per expert,
     # so the expert GEMMs take 256-row tiles on the LDS-staged kernel and the

@@ -1,8 +1,8 @@
-"""End-to-end parity on small bf16 / fp8 models that use every kernel path of
+"""End-to-end parity on small bf16 / fp8 / MXFP4-expert models that use every kernel path of
 the realistic-width step (head_dim 128, grouped-query pairs, top-k routing
 over 16 experts, a shared FFN, bf16 activations) with ragged sizes: a
 100-token prefix, a second request with a 37-token prefix denoised in the
-same pass, a 200-token canvas.  Tolerances: bf16 2e-2, fp8 6e-2 (per-row
+same pass, a 200-token canvas.  Tolerances: bf16 2e-2, fp8 and MXFP4 6e-2 (per-row
 relative L2 of hidden states, K/V and logits)."""
 import numpy as np
 import pytest
@@ -33,7 +33,7 @@ def _cmp_kv(eng, req_o, w, r, P0, P1, tol):
         assert rel_l2_rows(V.reshape(-1, w["dh"]), Vo.reshape(-1, w["dh"])).max() <= tol, ("V", l)
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "mxfp4"])
 def test_small_two_requests_step_and_commit(wdtype):
     w = small(wdtype, C=200)
     tol = TOL[wdtype]
