@@ -196,10 +196,11 @@ def measured_traffic(kernel_part):
 
 def expert_bytes(w, active, part):
     """Algorithmic HBM bytes of one grouped expert GEMM launch: the weights of
-    every expert that received tokens (bf16, or fp8 plus fp32 row scales), the
-    gathered bf16 activation rows read and the output rows written."""
+    every expert that received tokens (bf16; fp8 plus fp32 row scales; MXFP4
+    at half a byte per weight plus one scale byte per 32), the gathered bf16
+    activation rows read and the output rows written."""
     T, k, d, fe = w["R"] * w["C"], w["k"], w["d"], w["fe"]
-    wes = 1 if w["wdtype"] == "fp8" else 2
+    wes = {"fp8": 1, "mxfp4": 0.5 + 1 / 32}.get(w["wdtype"], 2)
     scale = 4 if w["wdtype"] == "fp8" else 0
     if part == "gate_up":
         return active * (2 * fe * d * wes + 2 * fe * scale) + T * k * d * 2 + T * k * fe * 2

@@ -19,6 +19,8 @@ Workloads (shapes follow the DiffusionGemma pages: 256-token canvas, step cap
 * ``gen_bf16``  the ``step_bf16`` model generating 4 blocks of 256 tokens.
 * ``batch_fp8`` the ``step_bf16`` model with fp8 e4m3 attention and expert
                 weights, 32 requests of 4096-token prefixes.
+* ``step_mxfp4`` the ``step_bf16`` step with MXFP4 experts and fp8 attention.
+* ``batch_mxfp4`` the ``batch_fp8`` batch with MXFP4 experts.
 """
 from __future__ import annotations
 
@@ -48,6 +50,12 @@ WORKLOADS = {
     "batch_fp8": dict(_COMMON, L=30, d=2816, Hq=16, Hkv=8, dh=128, E=128, k=8,
                       fe=704, fs=2112, V=262144, wdtype="fp8", P0=4096, R=32,
                       blocks=1),
+    "step_mxfp4": dict(_COMMON, L=30, d=2816, Hq=16, Hkv=8, dh=128, E=128, k=8,
+                       fe=704, fs=2112, V=262144, wdtype="mxfp4", P0=4096, R=1,
+                       blocks=1),
+    "batch_mxfp4": dict(_COMMON, L=30, d=2816, Hq=16, Hkv=8, dh=128, E=128, k=8,
+                        fe=704, fs=2112, V=262144, wdtype="mxfp4", P0=4096, R=32,
+                        blocks=1),
 }
 
 
