@@ -13,7 +13,9 @@ so it checks what it can compute one item at a time:
   routing under the near-tie rule;
 * the LM head on sampled vocabulary rows from the GPU's final residual;
 * the sampler on the GPU's own logits (all 256 x 262144).
-Tolerance: bf16 2e-2 (per-row relative L2)."""
+The same step with MXFP4 experts and fp8 attention (``step_mxfp4``) is
+checked the same way.  Tolerance: bf16 2e-2, MXFP4 6e-2 (per-row relative
+L2)."""
 import numpy as np
 import pytest
 import torch
@@ -29,10 +31,11 @@ from tests.oracle_rows import layer_rows
 pytestmark = pytest.mark.gpu
 
 
-def test_step_bf16_full_width_sampled_parity():
-    w = synth_inputs.workload("step_bf16")
-    tol = TOL["bf16"]
-    announce("full_width_step", L=w["L"], d=w["d"], E=w["E"], V=w["V"], P0=w["P0"])
+@pytest.mark.parametrize("name", ["step_bf16", "step_mxfp4"])
+def test_step_full_width_sampled_parity(name):
+    w = synth_inputs.workload(name)
+    tol = TOL[w["wdtype"]]
+    announce("full_width_step", workload=name, L=w["L"], d=w["d"], E=w["E"], V=w["V"], P0=w["P0"])
     L, C, d, k, P0, V = w["L"], w["C"], w["d"], w["k"], w["P0"], w["V"]
     eng = Engine(w, max_ctx=P0 + C)
     B.cd_synth_weights(eng.ctx, w["weight_seed"])
