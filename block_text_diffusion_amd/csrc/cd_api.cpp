@@ -117,6 +117,11 @@ int sampler_chunks(int V) {
   return n;
 }
 
+// expert row tile of the register-path grouped GEMM, in 16-row tiles: 32
+// rows; 16 for MXFP4, whose 4-bit weight bytes are no more than the
+// activation bytes a tile stages, so padding rows cost as much as weights
+int grouped_mt(const Plan& p) { return p.wdt_exp == CD_MXFP4 ? 1 : GROUPED_MT; }
+
 Plan make_plan(const cd_config& c) {
   Plan p;
   p.c = c;
@@ -166,7 +171,7 @@ Plan make_plan(const cd_config& c) {
   p.weights_bytes = w.off;
 
   const int R = c.max_requests, T = p.Tmax, k = c.top_k, ae = esize(p.adt);
-  const int mrows = 16 * GROUPED_MT;
+  const int mrows = 16 * grouped_mt(p);
   // expert segments are padded to the row tile: size for the larger tile
   // when the largest forward can take it
   const int pad_rows = big_expert_tiles((int64_t)T * k, E) ? BIG_TILE_ROWS : mrows;
@@ -366,10 +371,10 @@ void gemm_grouped(const cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, h
     launch_gemm_x(wdt, c->p.adt, epi, a, s);
     return;
   }
-  const int mrows = 16 * GROUPED_MT;
+  const int mt = grouped_mt(c->p), mrows = 16 * mt;
   a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + mrows - 1) / mrows + std::min<int64_t>(rows, c->p.c.n_experts));
   a.chunk_major = 0;
-  launch_gemm(wdt, c->p.adt, GROUPED_MT, epi, a, s);
+  launch_gemm(wdt, c->p.adt, mt, epi, a, s);
 }
 
 // ---- forward over rows of requests r0..r0+n_req-1 --------------------------------------
@@ -482,7 +487,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
     ra.blk_cnt = c->st<int32_t>(p.blk_cnt); ra.seg_off = c->st<int32_t>(p.seg_off);
     ra.row_map = c->st<int32_t>(p.row_map); ra.slot = c->st<int32_t>(p.slot);
     ra.tiles = c->st<int32_t>(p.tiles); ra.n_tiles = c->st<int32_t>(p.n_tiles);
-    ra.mrows = big_expert_tiles((int64_t)T * k, E) ? BIG_TILE_ROWS : 16 * GROUPED_MT;
+    ra.mrows = big_expert_tiles((int64_t)T * k, E) ? BIG_TILE_ROWS : 16 * grouped_mt(p);
     ra.max_rows = (int)p.max_rows; ra.max_tiles = (int)p.max_tiles;
     if (trace && c->trace_ids) {
       ra.trace_ids = c->trace_ids + (int64_t)l * T * k;
