@@ -240,9 +240,13 @@ def cd_serve(ctx, prefixes, n_blocks, seeds, n_slots, out_ids, stream=None):
     for q in range(1, n_q):
         ooff[q] = ooff[q - 1] + n_blocks[q - 1] * C
     steps = (c_int32 * sum(n_blocks))()
-    _check(lib().cd_serve(ctx, n_q, _ptr(flat), (ctypes.c_int64 * n_q)(*poff), (c_int32 * n_q)(*lens),
+    code = lib().cd_serve(ctx, n_q, _ptr(flat), (ctypes.c_int64 * n_q)(*poff), (c_int32 * n_q)(*lens),
                           (c_int32 * n_q)(*n_blocks), (c_uint64 * n_q)(*seeds), n_slots, _ptr(out_ids),
-                          (ctypes.c_int64 * n_q)(*ooff), steps, _stream(stream)))
+                          (ctypes.c_int64 * n_q)(*ooff), steps, _stream(stream))
+    if code != CD_OK:
+        # a failing call may leave prefills of the concatenated prompts queued
+        torch.cuda.synchronize()
+    _check(code)
     out, i = [], 0
     for nb in n_blocks:
         out.append(list(steps[i:i + nb]))
