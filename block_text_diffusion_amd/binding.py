@@ -224,9 +224,10 @@ def cd_move_request(ctx, src, dst, stream=None):
 
 def cd_serve(ctx, prefixes, n_blocks, seeds, n_slots, out_ids, stream=None):
     """Queue of requests: prefixes (list of 1-D int32 device tensors), blocks
-    and seeds per request.  Request q's blocks land in out_ids (1-D int32
-    device) at the offset of the blocks of requests before it.  Returns the
-    passes per block, one list per request."""
+    and seeds per request.  out_ids (1-D int32 device) holds exactly
+    sum(n_blocks) * canvas_len ids; request q's blocks land at the offset of
+    the blocks of requests before it.  Returns the passes per block, one list
+    per request."""
     import torch
     n_q = len(prefixes)
     assert len(n_blocks) == n_q and len(seeds) == n_q
@@ -235,7 +236,9 @@ def cd_serve(ctx, prefixes, n_blocks, seeds, n_slots, out_ids, stream=None):
     poff = [0] * n_q
     for q in range(1, n_q):
         poff[q] = poff[q - 1] + lens[q - 1]
-    C = out_ids.numel() // max(1, sum(n_blocks))
+    # out_ids holds exactly sum(n_blocks) blocks of canvas_len ids
+    assert sum(n_blocks) > 0 and out_ids.numel() % sum(n_blocks) == 0, "out_ids must hold sum(n_blocks) blocks"
+    C = out_ids.numel() // sum(n_blocks)
     ooff = [0] * n_q
     for q in range(1, n_q):
         ooff[q] = ooff[q - 1] + n_blocks[q - 1] * C
