@@ -795,7 +795,8 @@ int32_t cd_prefill(cd_ctx* c, int32_t req, const int32_t* d_ids, int32_t n, void
 
 // canvas start of slot req; rid keys its Philox stream (the slot itself for
 // the public call, the queue index in the batched loop)
-int32_t init_canvas_internal(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, int32_t rid, hipStream_t s) {
+static int32_t init_canvas_internal(cd_ctx* c, int32_t req, uint64_t seed, int32_t block, int32_t rid,
+                                    hipStream_t s) {
   const cd_config& g = c->p.c;
   HostReq& q = c->req[req];
   if (q.active) return fail(CD_ERR_BAD_STATE, "request %d already has an active canvas", req);
@@ -808,7 +809,7 @@ int32_t init_canvas_internal(cd_ctx* c, int32_t req, uint64_t seed, int32_t bloc
 
 // every per-slot row of request `from` (K/V region, canvas, last pass
 // outputs, device state) copied to the free slot `to`; `from` is released
-int32_t move_internal(cd_ctx* c, int from, int to, hipStream_t s) {
+static int32_t move_internal(cd_ctx* c, int from, int to, hipStream_t s) {
   const Plan& p = c->p;
   const int64_t C = p.c.canvas_len, kvb = p.kv_req_stride * esize(p.adt);
   const int64_t span[][2] = {{p.kcache, kvb}, {p.vcache, kvb}, {p.canvas, 4 * C}, {p.argmax, 4 * C},
@@ -957,24 +958,11 @@ int32_t cd_generate(cd_ctx* c, int32_t req, const int32_t* d_prefix, int32_t n_p
   return hip_status("generate");
 }
 
-int32_t cd_serve(cd_ctx* c, int32_t n_queue, const int32_t* d_prefix, const int64_t* h_prefix_off,
-                 const int32_t* h_prefix_len, const int32_t* h_n_blocks, const uint64_t* h_seeds, int32_t n_slots,
-                 int32_t* d_out, const int64_t* h_out_off, int32_t* h_steps, void* stream) {
-  if (int32_t st = check_ctx(c)) return st;
-  const cd_config& g = c->p.c;
-  const int C = g.canvas_len;
-  if (n_queue < 1 || n_slots < 1 || n_slots > g.max_requests || !d_prefix || !h_prefix_off || !h_prefix_len ||
-      !h_n_blocks || !h_seeds || !d_out || !h_out_off || !h_steps)
-    return fail(CD_ERR_INVALID_ARG, "bad serve arguments");
-  for (int q = 0; q < n_queue; ++q) {
-    if (h_prefix_len[q] < 1 || h_prefix_len[q] > g.max_prefill || h_n_blocks[q] < 1 || h_prefix_off[q] < 0 ||
-        h_out_off[q] < 0)
-      return fail(CD_ERR_INVALID_ARG, "bad prefix length, block count or offset for queued request %d", q);
-    if ((int64_t)h_prefix_len[q] + (int64_t)h_n_blocks[q] * C > g.max_ctx)
-      return fail(CD_ERR_CAPACITY, "queued request %d does not fit the KV cache", q);
-  }
-  for (int r = 0; r < n_slots; ++r)
-    if (c->req[r].active) return fail(CD_ERR_BAD_STATE, "slot %d has an active canvas", r);
+// the loop of cd_serve, on arguments it has validated
+static int32_t serve_loop(cd_ctx* c, int32_t n_queue, const int32_t* d_prefix, const int64_t* h_prefix_off,
+                          const int32_t* h_prefix_len, const int32_t* h_n_blocks, const uint64_t* h_seeds,
+                          int32_t n_slots, int32_t* d_out, const int64_t* h_out_off, int32_t* h_steps, void* stream) {
+  const int C = c->p.c.canvas_len;
   hipStream_t s = strm(stream);
   for (int r = 0; r < n_slots; ++r)
     if (int32_t st = cd_release(c, r, stream)) return st;
@@ -1037,6 +1025,35 @@ int32_t cd_serve(cd_ctx* c, int32_t n_queue, const int32_t* d_prefix, const int6
     }
   }
   return hip_status("serve");
+}
+
+int32_t cd_serve(cd_ctx* c, int32_t n_queue, const int32_t* d_prefix, const int64_t* h_prefix_off,
+                 const int32_t* h_prefix_len, const int32_t* h_n_blocks, const uint64_t* h_seeds, int32_t n_slots,
+                 int32_t* d_out, const int64_t* h_out_off, int32_t* h_steps, void* stream) {
+  if (int32_t st = check_ctx(c)) return st;
+  const cd_config& g = c->p.c;
+  if (n_queue < 1 || n_slots < 1 || n_slots > g.max_requests || !d_prefix || !h_prefix_off || !h_prefix_len ||
+      !h_n_blocks || !h_seeds || !d_out || !h_out_off || !h_steps)
+    return fail(CD_ERR_INVALID_ARG, "bad serve arguments");
+  for (int q = 0; q < n_queue; ++q) {
+    if (h_prefix_len[q] < 1 || h_prefix_len[q] > g.max_prefill || h_n_blocks[q] < 1 || h_prefix_off[q] < 0 ||
+        h_out_off[q] < 0)
+      return fail(CD_ERR_INVALID_ARG, "bad prefix length, block count or offset for queued request %d", q);
+    if ((int64_t)h_prefix_len[q] + (int64_t)h_n_blocks[q] * g.canvas_len > g.max_ctx)
+      return fail(CD_ERR_CAPACITY, "queued request %d does not fit the KV cache", q);
+  }
+  for (int r = 0; r < n_slots; ++r)
+    if (c->req[r].active) return fail(CD_ERR_BAD_STATE, "slot %d has an active canvas", r);
+  const int32_t st = serve_loop(c, n_queue, d_prefix, h_prefix_off, h_prefix_len, h_n_blocks, h_seeds, n_slots,
+                                d_out, h_out_off, h_steps, stream);
+  if (st) {
+    // a failed loop still releases its slots (the error message is kept)
+    for (int r = 0; r < n_slots; ++r) {
+      if (c->req[r].P) launch_advance(c->st<ReqDev>(c->p.rq), r, -c->req[r].P, strm(stream));
+      c->req[r] = HostReq();
+    }
+  }
+  return st;
 }
 
 int32_t cd_sample_workspace_bytes(int32_t rows, int32_t vocab, size_t* bytes) {

@@ -238,7 +238,8 @@ int32_t cd_generate(cd_ctx* ctx, int32_t req, const int32_t* d_prefix, int32_t n
  * cd_move_request) so that the passes shrink with the work left.
  * h_steps (host) receives the passes per block, request after request
  * (sum of h_n_blocks entries).  Synchronises every pass; every slot is
- * released on return.  CD_ERR_NUMERIC on non-finite logits. */
+ * released on return, also when the call fails (argument errors excepted:
+ * they change nothing).  CD_ERR_NUMERIC on non-finite logits. */
 int32_t cd_serve(cd_ctx* ctx, int32_t n_queue, const int32_t* d_prefix, const int64_t* h_prefix_off,
                  const int32_t* h_prefix_len, const int32_t* h_n_blocks, const uint64_t* h_seeds,
                  int32_t n_slots, int32_t* d_out, const int64_t* h_out_off, int32_t* h_steps,

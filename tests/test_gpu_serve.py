@@ -15,7 +15,8 @@ pass, through the C ABI, against the oracle.
   sampler outputs stay as they were and its record is all zero.
 * cd_move_request in the middle of a block: the moved request continues,
   commits and starts its next block in the new slot and still matches the
-  oracle run of its own request index."""
+  oracle run of its own request index.
+* a loop that fails (non-finite logits) releases every slot."""
 import numpy as np
 import pytest
 import torch
@@ -145,3 +146,22 @@ def test_move_mid_block_matches_oracle():
         assert clear.mean() > 0.9
         assert np.array_equal(got[b][clear], ref["a"][clear]), b
         loop.commit(w, W, req, got[b])
+
+
+def test_serve_failure_releases_slots():
+    # NaN LM-head weights make every logit NaN: the sampler flags it, the
+    # loop stops with CD_ERR_NUMERIC, and every slot is released
+    w = synth_inputs.workload("tiny")
+    C = w["C"]
+    announce("serve_failure_path")
+    eng = Engine(w, max_requests=2, max_ctx=64 + C, max_prefill=64)
+    B.cd_synth_weights(eng.ctx, w["weight_seed"])
+    B.cd_set_weight(eng.ctx, B.CD_W_LM, 0, 0, torch.full((w["V"], w["d"]), float("nan"), device="cuda"))
+    prefs = [torch.from_numpy(synth_inputs.prefix_ids(w["V"], 30 + q, 2, q)).cuda() for q in range(3)]
+    out = torch.empty(3 * C, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.CDError) as e:
+        B.cd_serve(eng.ctx, prefs, [1, 1, 1], [1, 2, 3], 2, out)
+    assert e.value.code == B.CD_ERR_NUMERIC
+    assert [B.cd_get_length(eng.ctx, r) for r in range(2)] == [0, 0]
+    B.cd_init_canvas(eng.ctx, 0, 1, 0)                 # no canvas was left active
+    eng.close()
