@@ -181,10 +181,11 @@ int32_t cd_init_canvas(cd_ctx* ctx, int32_t req, uint64_t seed, int32_t block, v
  * argmax (ties to the lowest id) and max prob; lock when max prob >
  * lock_threshold (CD_LOCK_ENTROPY: when entropy <= entropy_bound; the
  * position takes the argmax), else re-noise with
- * Philox(seed; i, t, block, req); stop when t >= 2, mean entropy <
- * stop_entropy and the argmax equals the previous pass's at every position,
- * or when t == max_steps.  d_info receives n_req cd_step_info records.
- * CD_ERR_BAD_STATE if a request has no canvas or has reached max_steps. */
+ * Philox(seed; i, t, block, id), id the request index of the canvas start;
+ * stop when t >= 2, mean entropy < stop_entropy and the argmax equals the
+ * previous pass's at every position, or when t == max_steps.  d_info
+ * receives n_req cd_step_info records.  CD_ERR_BAD_STATE if no slot has a
+ * canvas or an active one has reached max_steps. */
 int32_t cd_denoise_step(cd_ctx* ctx, int32_t n_req, cd_step_info* d_info, void* stream);
 
 /* Drop the active canvas of request req without committing it (the
@@ -228,8 +229,9 @@ int32_t cd_generate(cd_ctx* ctx, int32_t req, const int32_t* d_prefix, int32_t n
  * retire/admit loop of a server).  Request q: prompt d_prefix +
  * h_prefix_off[q] (device ids; host offsets), h_prefix_len[q] >= 1 ids,
  * h_n_blocks[q] blocks, seed h_seeds[q]; its Philox streams are keyed by
- * request index q (not by slot), so its output equals cd_generate of the
- * same prompt and seed run as request q.  Slots 0..n_slots-1 are released
+ * request index q (not by slot), so its output is that of cd_generate of
+ * the same prompt and seed run as request q (up to the rounding order of a
+ * batched pass: split counts depend on the batch).  Slots 0..n_slots-1 are released
  * first and take requests in queue order; each pass denoises every slot up
  * to the highest busy one (idle ones ride along); a block that stops is
  * committed to d_out + h_out_off[q] + b*canvas_len and its slot starts the
