@@ -11,7 +11,10 @@ bench.py times.  The oracle checks what it can compute item by item:
   under the near-tie rule;
 * the LM head on sampled vocabulary rows of the last request;
 * the sampler on the last request's GPU logits (its own Philox stream).
-Tolerance: fp8 6e-2 (per-row relative L2)."""
+The same batch with MXFP4 experts (``batch_mxfp4``: 512 rows per expert, so
+the expert GEMMs run the LDS-staged kernel's MXFP4 path at K = 2816 and 704)
+is checked the same way.  Tolerance: fp8 and MXFP4 6e-2 (per-row relative
+L2)."""
 import numpy as np
 import pytest
 import torch
@@ -27,11 +30,12 @@ from tests.oracle_rows import layer_rows
 pytestmark = pytest.mark.gpu
 
 
-def test_batch_fp8_full_width_sampled_parity():
-    w = synth_inputs.workload("batch_fp8")
-    tol = TOL["fp8"]
+@pytest.mark.parametrize("name", ["batch_fp8", "batch_mxfp4"])
+def test_batch_full_width_sampled_parity(name):
+    w = synth_inputs.workload(name)
+    tol = TOL[w["wdtype"]]
     L, C, d, k, P0, V, R = w["L"], w["C"], w["d"], w["k"], w["P0"], w["V"], w["R"]
-    announce("batch_fp8", R=R, L=L, d=d, E=w["E"], V=V, P0=P0)
+    announce("batch", workload=name, R=R, L=L, d=d, E=w["E"], V=V, P0=P0)
     eng = Engine(w, max_ctx=P0 + C)
     B.cd_synth_weights(eng.ctx, w["weight_seed"])
     for r in range(R):
