@@ -78,6 +78,13 @@ __device__ __forceinline__ u32x4 load_fp4(const uint8_t* p, const uint8_t* ps) {
   r[0] = c.x; r[1] = c.y; r[2] = *ps; r[3] = 0;
   return r;
 }
+// the 8 code bytes only (the scales come as one dword per four k-tiles)
+__device__ __forceinline__ u32x4 load_fp4_codes(const uint8_t* p) {
+  const uint2 c = *reinterpret_cast<const uint2*>(p);
+  u32x4 r;
+  r[0] = c.x; r[1] = c.y; r[2] = 0; r[3] = 0;
+  return r;
+}
 __device__ __forceinline__ f32x4 mma_bf16(const u32x4& a, const u32x4& b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }

@@ -53,7 +53,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   constexpr int FPW = NFR / NW;           // fragments each wave copies
   constexpr int STG = NFR * 1024;
   constexpr int XBUF = 3;
-  constexpr int LPS = FPW + NTW * U * (F4 ? 2 : 1);   // vector loads per wave per stage
+  static_assert(!F4 || U == 4, "MXFP4 scales come as one dword per four k-tiles");
+  constexpr int LPS = FPW + NTW * U + (F4 ? NTW : 0);   // vector loads per wave per stage
   static_assert(NFR % NW == 0, "stage fragments");
   __shared__ __attribute__((aligned(1024))) uint8_t xs[XBUF * STG];
 
@@ -115,8 +116,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   const int KT = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt_beg;   // k-tiles of this split
   const int nst = (KT + U - 1) / U;                                      // stages of U k-tiles
   const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)ntc * KTall + kt_beg) * TB + lane * (TB / 64);
-  const uint8_t* mxp0 = a.W + (int64_t)group * a.w_gstride + a.mx_off + ((int64_t)ntc * KTall + kt_beg) * 32 +
-                        (lane & 15) * 2 + (lane >> 5);
+  // MXFP4 scales: one dword per lane per four k-tiles (the grouped expert
+  // launches never split the contraction, so stages start at k-tile 4 * st)
+  const int KT4 = (KTall + 3) / 4;
+  const uint8_t* mxp0 = a.W + (int64_t)group * a.w_gstride + a.mx_off + (int64_t)ntc * KT4 * 128 +
+                        ((lane & 15) * 2 + (lane >> 5)) * 4;
   const int esa = (AT == DT_F32) ? 4 : 2;
   // this wave's share of the activation fragments of a stage: fragment
   // f = (mt*U + u)*XW + h holds rows mt*16.. at k-tile u (half h for fp8)
@@ -159,10 +163,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
         if constexpr (F4)
-          ww[j][u] = load_fp4(wp0 + ((int64_t)j * KTall + kk) * TB, mxp0 + ((int64_t)j * KTall + kk) * 32);
+          ww[j][u] = load_fp4_codes(wp0 + ((int64_t)j * KTall + kk) * TB);
         else
           ww[j][u] = *reinterpret_cast<const u32x4*>(wp0 + ((int64_t)j * KTall + kk) * 1024);
       }
+    }
+    if constexpr (F4) {
+      const int s4 = min(st, KT4 - 1);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        ww[j][0][3] = *reinterpret_cast<const uint32_t*>(mxp0 + ((int64_t)j * KT4 + s4) * 128);
     }
   };
   auto compute = [&](const u32x4 (&ww)[NTW][U], int st) {
@@ -176,8 +186,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
           u32x4 wb[NTW][2];
 #pragma unroll
           for (int j = 0; j < NTW; ++j) {
-            if constexpr (F4) widen_fp4(ww[j][u], wb[j]);
-            else widen_fp8(ww[j][u], wb[j]);
+            if constexpr (F4) {
+              u32x4 t = ww[j][u];
+              t[2] = (ww[j][0][3] >> (8 * u)) & 0xFFu;   // this k-tile's scale byte
+              widen_fp4(t, wb[j]);
+            } else {
+              widen_fp8(ww[j][u], wb[j]);
+            }
           }
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)

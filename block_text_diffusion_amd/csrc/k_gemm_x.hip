@@ -108,7 +108,8 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   for (int j = 0; j < NWP; ++j) {
     const int t = WLDS ? chunk * 4 * XNTW + wave * WPW + j : nt0 + j;
     wp[j] = wbase + ((int64_t)min(t, a.Nt - 1) * KTall + kt0) * TB + lane * (TB / 64);
-    mxp[j] = wbase + a.mx_off + ((int64_t)min(t, a.Nt - 1) * KTall + kt0) * 32 + (lane & 15) * 2 + (lane >> 5);
+    mxp[j] = wbase + a.mx_off + (int64_t)min(t, a.Nt - 1) * ((KTall + 3) / 4) * 128 +
+             ((lane & 15) * 2 + (lane >> 5)) * 4;
   }
   // rows past the tile's end read its last row (finite); their results are dropped
   const uint8_t* xsrc[BPW];
@@ -151,7 +152,10 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
     const int sc = min(s, nst - 1);
 #pragma unroll
     for (int j = 0; j < XNTW; ++j) {
-      if constexpr (F4) ww[j] = load_fp4(wp[j] + (int64_t)sc * TB, mxp[j] + (int64_t)sc * 32);
+      if constexpr (F4) {
+        const int kt = kt0 + sc;   // scale byte of k-tile kt in its group of four
+        ww[j] = load_fp4(wp[j] + (int64_t)sc * TB, mxp[j] + (int64_t)(kt >> 2) * 128 + (kt & 3));
+      }
       else ww[j] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)sc * 1024);
     }
   };

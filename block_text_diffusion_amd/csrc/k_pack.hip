@@ -95,7 +95,8 @@ __device__ __forceinline__ int64_t fp4_chunk(int p, int k, int KT) {
   return ((((int64_t)(p >> 4) * KT + k / 64) * 64) + (p & 15) + 16 * ((k % 64) / 16)) * 8;
 }
 __device__ __forceinline__ int64_t fp4_scale(int p, int k, int KT) {
-  return ((int64_t)(p >> 4) * KT + k / 64) * 32 + (p & 15) * 2 + (k % 64) / 32;
+  const int kt = k / 64, KT4 = (KT + 3) / 4;
+  return (((int64_t)(p >> 4) * KT4 + kt / 4) * 32 + (p & 15) * 2 + (k % 64) / 32) * 4 + kt % 4;
 }
 
 __device__ __forceinline__ void synth4(uint64_t seed, uint32_t tau, uint64_t q, double w[4]) {

@@ -18,9 +18,11 @@ namespace cd {
 // column in the low nibble), in 16-row x 64-column tiles of 512 bytes; lane l
 // holds the 8 bytes of row nt*16 + l%16, columns kt*64 + (l/16)*16 + [0, 16).
 // Each row has one E8M0 scale (2^(byte - 127)) per 32 columns; the scales
-// follow the tiles, 32 bytes per tile (nt, kt) at mx_offset + (nt * KT + kt)
-// * 32 + (row % 16) * 2 + (column % 64) / 32, so lane l's scale is byte
-// (l % 16) * 2 + l / 32 of its tile's 32.
+// follow the tiles in groups of four k-tiles: the scale of row r, column c
+// (k-tile kt = c / 64) is byte ((nt * KT4 + kt / 4) * 32 + (r % 16) * 2 +
+// (c % 64) / 32) * 4 + kt % 4 after them, KT4 = ceil(KT / 4), so one dword
+// per lane (lane l: index (l % 16) * 2 + l / 32) holds its scales of four
+// consecutive k-tiles.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int esize(int dt) { return dt == 0 ? 4 : dt == 1 ? 2 : 1; }
 __host__ __device__ inline int kfrag(int dt) { return 64 / esize(dt); }
@@ -30,7 +32,7 @@ __host__ __device__ inline int64_t packed_bytes(int64_t Npad, int64_t K, int dt)
 }
 // packed bytes including MXFP4 scales
 __host__ __device__ inline int64_t packed_total(int64_t Npad, int64_t K, int dt) {
-  return packed_bytes(Npad, K, dt) + (dt == 3 ? Npad * K / 32 : 0);
+  return packed_bytes(Npad, K, dt) + (dt == 3 ? (Npad / 16) * ((K / 64 + 3) / 4) * 128 : 0);
 }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
