@@ -104,6 +104,8 @@ def gpu_part(w, steps, warmup, prof_steps, do_block=True):
         B.cd_denoise_step(ctx, R, eng.info)
         info = B.cd_read_step_info(ctx, eng.info, R)          # the loop's stop-flag read-back
         state["t"] += 1
+        if any(i.stop for i in info):
+            state["t"] = w["max_steps"]                       # a stopped request takes no further pass
         return info
 
     fresh()

@@ -36,7 +36,7 @@ class cd_config(ctypes.Structure):
 
 class cd_step_info(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("step", "stop", "n_locked", "stable", "canvas_is_argmax",
-                                       "nonfinite")] + [("mean_entropy", c_double)]
+                                       "nonfinite", "after_stop")] + [("mean_entropy", c_double)]
 
 
 STEP_INFO_BYTES = ctypes.sizeof(cd_step_info)
@@ -82,6 +82,7 @@ def lib():
                                c_void_p, c_void_p],
             "cd_get_buffer": [c_void_p, c_int32, P(c_void_p), P(c_size_t)],
             "cd_get_length": [c_void_p, c_int32, P(c_int32)],
+            "cd_get_config": [c_void_p, P(cd_config)],
             "cd_set_trace": [c_void_p, c_void_p, c_void_p, c_void_p],
             "cd_abort_canvas": [c_void_p, c_int32],
             "cd_release": [c_void_p, c_int32, c_void_p],
@@ -105,7 +106,7 @@ def exported_names():
     return ["cd_weights_bytes", "cd_state_bytes", "cd_ctx_create", "cd_ctx_destroy", "cd_reset",
             "cd_synth_weights", "cd_set_weight", "cd_get_weight", "cd_prefill", "cd_init_canvas",
             "cd_denoise_step", "cd_read_step_info", "cd_commit_block", "cd_generate",
-            "cd_sample_workspace_bytes", "cd_sample_step", "cd_get_buffer", "cd_get_length",
+            "cd_sample_workspace_bytes", "cd_sample_step", "cd_get_buffer", "cd_get_config", "cd_get_length",
             "cd_set_trace", "cd_abort_canvas", "cd_release", "cd_move_request", "cd_serve", "cd_profile", "cd_profile_read",
             "cd_last_error"]
 
@@ -202,11 +203,20 @@ def cd_read_step_info(ctx, info, n_req, stream=None):
     return list(out)
 
 
+def _check_ids(t, n, what):
+    """Output ids: a contiguous int32 tensor of exactly n elements."""
+    import torch
+    if not (isinstance(t, torch.Tensor) and t.dtype == torch.int32 and t.is_contiguous() and t.numel() == n):
+        raise ValueError(f"{what}: needs a contiguous int32 tensor of exactly {n} ids")
+
+
 def cd_commit_block(ctx, req, out_ids, stream=None):
+    _check_ids(out_ids, cd_get_config(ctx).canvas_len, "cd_commit_block out_ids")
     _check(lib().cd_commit_block(ctx, req, _ptr(out_ids), _stream(stream)))
 
 
 def cd_generate(ctx, req, prefix, n_blocks, seed, out_ids, stream=None):
+    _check_ids(out_ids, n_blocks * cd_get_config(ctx).canvas_len, "cd_generate out_ids")
     steps = (c_int32 * n_blocks)()
     n_prefix = 0 if prefix is None else prefix.numel()
     _check(lib().cd_generate(ctx, req, _ptr(prefix), n_prefix, n_blocks, seed, _ptr(out_ids), steps,
@@ -236,9 +246,9 @@ def cd_serve(ctx, prefixes, n_blocks, seeds, n_slots, out_ids, stream=None):
     poff = [0] * n_q
     for q in range(1, n_q):
         poff[q] = poff[q - 1] + lens[q - 1]
-    # out_ids holds exactly sum(n_blocks) blocks of canvas_len ids
-    assert sum(n_blocks) > 0 and out_ids.numel() % sum(n_blocks) == 0, "out_ids must hold sum(n_blocks) blocks"
-    C = out_ids.numel() // sum(n_blocks)
+    # out_ids holds exactly sum(n_blocks) blocks of the context's canvas_len ids
+    C = cd_get_config(ctx).canvas_len
+    _check_ids(out_ids, sum(n_blocks) * C, "cd_serve out_ids")
     ooff = [0] * n_q
     for q in range(1, n_q):
         ooff[q] = ooff[q - 1] + n_blocks[q - 1] * C
@@ -274,6 +284,12 @@ def cd_get_buffer(ctx, which):
     p, n = c_void_p(), c_size_t()
     _check(lib().cd_get_buffer(ctx, which, ctypes.byref(p), ctypes.byref(n)))
     return p.value, n.value
+
+
+def cd_get_config(ctx):
+    cfg = cd_config()
+    _check(lib().cd_get_config(ctx, ctypes.byref(cfg)))
+    return cfg
 
 
 def cd_get_length(ctx, req):

@@ -253,6 +253,8 @@ struct cd_ctx {
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool side_tried = false;
+  // first refusal of a kernel launcher during the current call (0 = none)
+  int32_t launch_err = 0;
   template <class T> T* st(int64_t off) const { return reinterpret_cast<T*>(S + off); }
   template <class T> T* wt(int64_t off) const { return off < 0 ? nullptr : reinterpret_cast<T*>(W + off); }
 };
@@ -340,7 +342,11 @@ int router_split(const cd_config& g, int T) {
 // row-tiled kernel: at the canvas batch, 32-row tiles give each weight chunk
 // 8 workgroups on one XCD (one HBM read, the rest from its L2) and fill the
 // chip without splitting the contraction.
-void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
+void note_launch(cd_ctx* c, int st) {
+  if (st && !c->launch_err) c->launch_err = st;
+}
+
+void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
   // the LDS-staged kernel needs enough (256-row slab, 256-column chunk)
   // items to fill the chip; the expert-combining epilogue gathers 8 rows per
   // output and prefers the many workgroups of the row-tiled kernel
@@ -349,7 +355,7 @@ void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_
   if (lds_staged) {
     a.M = M;
     a.tiles = nullptr;
-    launch_gemm_x(wdt, c->p.adt, epi, a, s);
+    note_launch(c, launch_gemm_x(wdt, c->p.adt, epi, a, s));
     return;
   }
   const int mt = M > 256 ? 4 : (M > 16 ? 2 : 1);
@@ -357,24 +363,24 @@ void gemm_dense(const cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_
   a.max_tiles = (M + 16 * mt - 1) / (16 * mt);
   a.chunk_major = 1;
   a.tiles = nullptr;
-  launch_gemm(wdt, c->p.adt, mt, epi, a, s);
+  note_launch(c, launch_gemm(wdt, c->p.adt, mt, epi, a, s));
 }
 
 // rows: assignments of this forward (T * top_k); the grid is sized for the
 // most tiles they can form, so idle workgroups stay few
-void gemm_grouped(const cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, hipStream_t s) {
+void gemm_grouped(cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, hipStream_t s) {
   a.tiles = c->st<int32_t>(c->p.tiles);
   a.n_tiles = c->st<int32_t>(c->p.n_tiles);
   if (big_expert_tiles(rows, c->p.c.n_experts)) {
     a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + BIG_TILE_ROWS - 1) / BIG_TILE_ROWS +
                                                             std::min<int64_t>(rows, c->p.c.n_experts));
-    launch_gemm_x(wdt, c->p.adt, epi, a, s);
+    note_launch(c, launch_gemm_x(wdt, c->p.adt, epi, a, s));
     return;
   }
   const int mt = grouped_mt(c->p), mrows = 16 * mt;
   a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + mrows - 1) / mrows + std::min<int64_t>(rows, c->p.c.n_experts));
   a.chunk_major = 0;
-  launch_gemm(wdt, c->p.adt, mt, epi, a, s);
+  note_launch(c, launch_gemm(wdt, c->p.adt, mt, epi, a, s));
 }
 
 // ---- forward over rows of requests r0..r0+n_req-1 --------------------------------------
@@ -560,6 +566,16 @@ void sample(cd_ctx* c, int r0, int n_req, hipStream_t s) {
 
 int32_t check_ctx(cd_ctx* c) { return c ? CD_OK : fail(CD_ERR_INVALID_ARG, "null context"); }
 
+// end of a call that launched a forward: a launcher refusal, else the HIP status
+int32_t finish(cd_ctx* c, const char* where) {
+  if (c->launch_err) {
+    const int32_t st = c->launch_err;
+    c->launch_err = 0;
+    return fail(st, "%s: a GEMM launch was refused (MXFP4 weights with a split contraction)", where);
+  }
+  return hip_status(where);
+}
+
 // One pass over requests r0..r0+n_req-1.  Requests without an active canvas
 // ride along: their rows go through the forward (whatever ids their canvas
 // holds, keys/values written past their committed length), but the sampler
@@ -583,7 +599,7 @@ int32_t step_internal(cd_ctx* c, int r0, int n_req, hipStream_t s) {
   sample(c, r0, n_req, s);
   for (int r = r0; r < r0 + n_req; ++r)
     if (c->req[r].active) c->req[r].t++;
-  return hip_status("denoise step");
+  return finish(c, "denoise step");
 }
 
 int32_t read_info(cd_ctx* c, int r, cd_step_info* out, hipStream_t s) {
@@ -790,7 +806,7 @@ int32_t cd_prefill(cd_ctx* c, int32_t req, const int32_t* d_ids, int32_t n, void
   forward(c, req, 1, n, d_ids, true, false, true, s);
   launch_advance(c->st<ReqDev>(c->p.rq), req, n, s);
   q.P += n;
-  return hip_status("prefill");
+  return finish(c, "prefill");
 }
 
 // canvas start of slot req; rid keys its Philox stream (the slot itself for
@@ -813,12 +829,14 @@ static int32_t move_internal(cd_ctx* c, int from, int to, hipStream_t s) {
   const Plan& p = c->p;
   const int64_t C = p.c.canvas_len, kvb = p.kv_req_stride * esize(p.adt);
   const int64_t span[][2] = {{p.kcache, kvb}, {p.vcache, kvb}, {p.canvas, 4 * C}, {p.argmax, 4 * C},
-                             {p.lock, C},     {p.entropy, 8 * C}, {p.pmax, 8 * C}, {p.rq, (int64_t)sizeof(ReqDev)}};
+                             {p.lock, C},     {p.entropy, 8 * C}, {p.pmax, 8 * C}, {p.rq, (int64_t)sizeof(ReqDev)},
+                             {p.info, (int64_t)sizeof(cd_step_info)}};
   for (const auto& x : span)
     if (hipMemcpyAsync(c->S + x[0] + to * x[1], c->S + x[0] + from * x[1], x[1], hipMemcpyDeviceToDevice, s) !=
         hipSuccess)
       return hip_status("slot move");
   if (c->req[from].P) launch_advance(c->st<ReqDev>(p.rq), from, -c->req[from].P, s);
+  launch_zero_u32(c->st<cd_step_info>(p.info) + from, sizeof(cd_step_info) / 4, s);
   if (c->req[from].rid < 0) c->req[from].rid = from;
   c->req[to] = c->req[from];
   c->req[from] = HostReq();
@@ -837,7 +855,10 @@ int32_t cd_release(cd_ctx* c, int32_t req, void* stream) {
   if (int32_t st = check_ctx(c)) return st;
   if (req < 0 || req >= c->p.c.max_requests) return fail(CD_ERR_INVALID_ARG, "request %d out of range", req);
   HostReq& q = c->req[req];
-  if (q.P) launch_advance(c->st<ReqDev>(c->p.rq), req, -q.P, strm(stream));
+  hipStream_t s = strm(stream);
+  if (q.P) launch_advance(c->st<ReqDev>(c->p.rq), req, -q.P, s);
+  // the slot's last step record goes with the request
+  launch_zero_u32(c->st<cd_step_info>(c->p.info) + req, sizeof(cd_step_info) / 4, s);
   q = HostReq();
   return hip_status("release");
 }
@@ -904,6 +925,9 @@ int32_t cd_read_step_info(cd_ctx* c, const cd_step_info* d_info, int32_t n_req, 
   if (hipMemcpyAsync(h_info, d_info, sizeof(cd_step_info) * n_req, hipMemcpyDeviceToHost, s) != hipSuccess)
     return hip_status("step info copy");
   if (hipStreamSynchronize(s) != hipSuccess) return hip_status("stream sync");
+  for (int r = 0; r < n_req; ++r)
+    if (h_info[r].after_stop)
+      return fail(CD_ERR_BAD_STATE, "request %d was given a denoise pass after its stop (records copied)", r);
   return CD_OK;
 }
 
@@ -917,13 +941,15 @@ int32_t cd_commit_block(cd_ctx* c, int32_t req, int32_t* d_out_ids, void* stream
   hipStream_t s = strm(stream);
   cd_step_info info;
   if (int32_t st = read_info(c, req, &info, s)) return st;
+  if (info.after_stop)
+    return fail(CD_ERR_BAD_STATE, "request %d was given a denoise pass after its stop; abort its canvas", req);
   int32_t* a = c->st<int32_t>(c->p.argmax) + (int64_t)req * g.canvas_len;
   if (!info.canvas_is_argmax) forward(c, req, 1, g.canvas_len, a, false, false, true, s);
   launch_copy_i32(a, d_out_ids, g.canvas_len, s);
   launch_advance(c->st<ReqDev>(c->p.rq), req, g.canvas_len, s);
   q.P += g.canvas_len;
   q.active = false;
-  return hip_status("commit");
+  return finish(c, "commit");
 }
 
 int32_t cd_generate(cd_ctx* c, int32_t req, const int32_t* d_prefix, int32_t n_prefix, int32_t n_blocks,
@@ -1110,6 +1136,13 @@ int32_t cd_get_buffer(cd_ctx* c, int32_t which, void** d_ptr, size_t* bytes) {
   }
   *d_ptr = c->S + off;
   if (bytes) *bytes = (size_t)n;
+  return CD_OK;
+}
+
+int32_t cd_get_config(cd_ctx* c, cd_config* out) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (!out) return fail(CD_ERR_INVALID_ARG, "null output");
+  *out = c->p.c;
   return CD_OK;
 }
 

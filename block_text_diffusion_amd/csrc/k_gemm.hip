@@ -116,8 +116,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs a) {
   const int KT = (int)((int64_t)KTall * (ks + 1) / ksplit) - kt_beg;   // k-tiles of this split
   const int nst = (KT + U - 1) / U;                                      // stages of U k-tiles
   const uint8_t* wp0 = a.W + (int64_t)group * a.w_gstride + ((int64_t)ntc * KTall + kt_beg) * TB + lane * (TB / 64);
-  // MXFP4 scales: one dword per lane per four k-tiles (the grouped expert
-  // launches never split the contraction, so stages start at k-tile 4 * st)
+  // MXFP4 scales: one dword per lane per four k-tiles (the launcher refuses
+  // an MXFP4 launch with a split contraction, so stages start at k-tile 4 * st)
   const int KT4 = (KTall + 3) / 4;
   const uint8_t* mxp0 = a.W + (int64_t)group * a.w_gstride + a.mx_off + (int64_t)ntc * KT4 * 128 +
                         ((lane & 15) * 2 + (lane >> 5)) * 4;
@@ -325,11 +325,13 @@ static void run_mt(int mt, int epi, const GemmArgs& a, hipStream_t s) {
   }
 }
 
-void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s) {
+int launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s) {
+  if (wdt == DT_FP4 && a.ksplit > 1) return -5;   // MXFP4 scales are indexed from k-tile 0
   if (wdt == DT_F32) run_mt<DT_F32, DT_F32>(mt, epi, a, s);
   else if (wdt == DT_BF16) run_mt<DT_BF16, DT_BF16>(mt, epi, a, s);
   else if (wdt == DT_FP8) run_mt<DT_FP8, DT_BF16>(mt, epi, a, s);
   else run_mt<DT_FP4, DT_BF16>(mt, epi, a, s);
+  return 0;
 }
 
 }  // namespace cd

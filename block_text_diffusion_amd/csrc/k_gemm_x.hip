@@ -300,11 +300,13 @@ static void run_x_epi(int epi, const GemmArgs& a, hipStream_t s) {
   }
 }
 
-void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s) {
+int launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s) {
+  if (wdt == DT_FP4 && a.ksplit > 1) return -5;   // MXFP4 scales are indexed from k-tile 0
   if (wdt == DT_F32) run_x_epi<DT_F32, DT_F32>(epi, a, s);
   else if (wdt == DT_BF16) run_x_epi<DT_BF16, DT_BF16>(epi, a, s);
   else if (wdt == DT_FP8) run_x_epi<DT_FP8, DT_BF16>(epi, a, s);
   else run_x_epi<DT_FP4, DT_BF16>(epi, a, s);
+  return 0;
 }
 
 }  // namespace cd

@@ -94,6 +94,7 @@ __global__ void k_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V
     rq[req].block = block;
     rq[req].rid = rid;
     rq[req].seed = seed;
+    rq[req].stopped = 0;
   }
 }
 void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed, int block, int rid,
@@ -111,6 +112,15 @@ __global__ void k_copy_i32(const int32_t* src, int32_t* dst, int n) {
 }
 void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s) {
   hipLaunchKernelGGL(k_copy_i32, dim3((n + 255) / 256), dim3(256), 0, s, src, dst, n);
+}
+__global__ void k_zero_u32(uint32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+void launch_zero_u32(void* p, int64_t n, hipStream_t s) {
+  int64_t b = (n + 255) / 256;
+  if (b > 65536) b = 65536;
+  if (b > 0) hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)b), dim3(256), 0, s, reinterpret_cast<uint32_t*>(p), n);
 }
 __global__ void k_copy_f32(const float* src, float* dst, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)

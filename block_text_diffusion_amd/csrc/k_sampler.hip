@@ -11,7 +11,9 @@
 // entropy H = ln S - U/S (nats), max prob 1/S and the argmax; locks when max
 // prob > threshold (position takes the argmax), else re-noises with
 // Philox(seed; position, pass, block, request); then the canvas mean entropy,
-// argmax stability against the previous pass and the stop flag.
+// argmax stability against the previous pass and the stop flag.  A request
+// whose stop has fired takes no further pass: a later pass leaves its state
+// as it was and flags its record (after_stop).
 #include "common.h"
 #include "kernels.h"
 #include "../../include/cd.h"
@@ -115,6 +117,14 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
       }
       return;
     }
+    if (a.rq[rr].stopped) {
+      // a pass after the stop of this block is refused for this request: its
+      // canvas, argmax and last record stay as they were (the pass did write
+      // keys/values of its canvas rows past P, which a commit would have to
+      // redo); the record is marked so the next synchronising call reports it
+      if (threadIdx.x == 0) reinterpret_cast<cd_step_info*>(a.info)[rr].after_stop = 1;
+      return;
+    }
     step = a.rq[rr].t + 1; block = a.rq[rr].block; req = a.rq[rr].rid; seed = a.rq[rr].seed;
   } else {
     step = a.step; block = a.block; req = a.req0 + rr; seed = a.seed;
@@ -192,8 +202,12 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
     inf.nonfinite = shN[0] | shN[1] | shN[2] | shN[3];
     inf.mean_entropy = Hbar;
     inf.stop = (step >= a.max_steps) || (step >= 2 && inf.stable && Hbar < (double)a.stop_H);
+    inf.after_stop = 0;
     reinterpret_cast<cd_step_info*>(a.info)[rr] = inf;
-    if (a.rq) a.rq[rr].t = step;
+    if (a.rq) {
+      a.rq[rr].t = step;
+      a.rq[rr].stopped = inf.stop;
+    }
   }
 }
 

@@ -76,9 +76,11 @@ struct GemmArgs {
   float q_scale;           // EPI_QKV: factor on the query outputs before their rounding
 };
 
-void launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
+// Both launchers return 0, or CD_ERR_UNSUPPORTED (-5) for an MXFP4 launch with
+// a split contraction (its scale dwords are indexed from k-tile 0).
+int launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
 // 256-row work items, activations staged in LDS (a.ksplit > 1: EPI_F32 partials)
-void launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s);
+int launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s);
 // ---- weight synthesis / packing --------------------------------------------
 struct PackDesc {
   uint8_t* dst;        // packed tiles (or row-major for embedding)
@@ -162,6 +164,8 @@ struct ReqDev {
   int32_t block;
   int32_t rid;      // request index that keys the Philox stream (the slot, unless a batched loop assigns one)
   uint64_t seed;
+  int32_t stopped;  // the adaptive stop (or the cap) fired in the current block; cleared by the canvas start
+  int32_t pad_;
 };
 // canvas of slot req for block `block`, its Philox stream keyed by rid
 void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint64_t seed,
@@ -169,6 +173,8 @@ void launch_init_canvas(int32_t* canvas, ReqDev* rq, int req, int C, int V, uint
 // P += dP for slot req
 void launch_advance(ReqDev* rq, int req, int dP, hipStream_t s);
 void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s);
+// n 32-bit words at p set to zero (a fill kernel, not a memset node)
+void launch_zero_u32(void* p, int64_t n, hipStream_t s);
 
 // ---- sampler ------------------------------------------------------------------------
 struct SampleArgs {

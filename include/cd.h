@@ -112,6 +112,9 @@ typedef struct cd_step_info {
   int32_t stable;           /* argmax equal to the previous pass's everywhere */
   int32_t canvas_is_argmax; /* the canvas fed to this pass equals its argmax */
   int32_t nonfinite;        /* a logit was NaN or infinite */
+  int32_t after_stop;       /* 1: a pass ran after this block's stop had fired; it was
+                               refused for this request (the rest of the record is that
+                               of the stopping pass) */
   double mean_entropy;      /* canvas mean entropy, nats */
 } cd_step_info;
 
@@ -185,26 +188,37 @@ int32_t cd_init_canvas(cd_ctx* ctx, int32_t req, uint64_t seed, int32_t block, v
  * stop when t >= 2, mean entropy < stop_entropy and the argmax equals the
  * previous pass's at every position, or when t == max_steps.  d_info
  * receives n_req cd_step_info records.  CD_ERR_BAD_STATE if no slot has a
- * canvas or an active one has reached max_steps. */
+ * canvas or an active one has reached max_steps.  The explainer's step ④
+ * commits the block once its stop has fired: a pass over a request whose
+ * stop already fired in this block is refused for that request on the
+ * device (its canvas, argmax and last record stay as they were; keys/values
+ * of its canvas rows past P are rewritten, as for a ride-along slot), its
+ * record is flagged after_stop, and the next cd_read_step_info or
+ * cd_commit_block for it returns CD_ERR_BAD_STATE (cd_abort_canvas then
+ * drops the canvas). */
 int32_t cd_denoise_step(cd_ctx* ctx, int32_t n_req, cd_step_info* d_info, void* stream);
 
 /* Drop the active canvas of request req without committing it (the
  * request returns to the state after its last commit).  Host-side only. */
 int32_t cd_abort_canvas(cd_ctx* ctx, int32_t req);
 
-/* Free slot req for a new prompt: P = 0 and no canvas (an active one is
- * dropped).  The cache rows it held are simply overwritten later. */
+/* Free slot req for a new prompt: P = 0, no canvas (an active one is
+ * dropped) and an all-zero step record.  The cache rows it held are simply
+ * overwritten later. */
 int32_t cd_release(cd_ctx* ctx, int32_t req, void* stream);
 
 /* Move the request in slot `from` (any state, also mid-block) to the free
- * slot `to` (P == 0, no canvas): its K/V region, canvas, last pass outputs
- * and step state are copied on the stream, and `from` is released.  Its
+ * slot `to` (P == 0, no canvas): its K/V region, canvas, last pass outputs,
+ * step record and step state are copied on the stream, and `from` is
+ * released.  Its
  * Philox streams keep their request index, so the move changes no result.
  * A server uses it to keep busy slots at the front: a pass over slots
  * 0..n-1 then computes no idle slot.  CD_ERR_BAD_STATE if `to` is not free. */
 int32_t cd_move_request(cd_ctx* ctx, int32_t from, int32_t to, void* stream);
 
-/* Copy n_req step records from device to host and wait for the stream. */
+/* Copy n_req step records from device to host and wait for the stream.
+ * Returns CD_ERR_BAD_STATE (the records are still copied) when a record is
+ * flagged after_stop. */
 int32_t cd_read_step_info(cd_ctx* ctx, const cd_step_info* d_info, int32_t n_req,
                           cd_step_info* h_info, void* stream);
 
@@ -213,10 +227,15 @@ int32_t cd_read_step_info(cd_ctx* ctx, const cd_step_info* d_info, int32_t n_req
  * come from a canvas-mode pass over the committed ids at positions
  * P..P+C-1, unless the last pass's canvas already equalled its argmax (then
  * that pass's keys/values are the same and are kept).  The cache below P is
- * never written.  P grows by canvas_len.  Synchronises the stream once. */
+ * never written.  P grows by canvas_len.  Synchronises the stream once.
+ * CD_ERR_BAD_STATE (nothing committed) if no pass ran since the canvas
+ * start, or a pass ran after the stop (record flagged after_stop). */
 int32_t cd_commit_block(cd_ctx* ctx, int32_t req, int32_t* d_out_ids, void* stream);
 
-/* Whole loop for one request: optional prefill of n_prefix ids, then
+/* Whole loop for one request (the canvas explainer, steps ① to ④, with the
+ * next canvas conditioned on the committed blocks as in the MarkTechPost
+ * article's "architecture" section, block-autoregressive diffusion):
+ * optional prefill of n_prefix ids, then
  * n_blocks blocks of init -> passes to the adaptive stop -> commit.
  * d_out_ids receives n_blocks*canvas_len ids; h_steps_per_block (host,
  * n_blocks entries) the passes each block took.  Synchronises every pass.
@@ -226,7 +245,9 @@ int32_t cd_generate(cd_ctx* ctx, int32_t req, const int32_t* d_prefix, int32_t n
                     int32_t* h_steps_per_block, void* stream);
 
 /* Batched loop over a queue of n_queue requests on n_slots slots (the
- * retire/admit loop of a server).  Request q: prompt d_prefix +
+ * retire/admit loop of a server; the explainer's A/B guide and official
+ * benchmark serve the model at several request concurrencies, and its
+ * steps ① to ④ are run per request, each with its own adaptive stop).  Request q: prompt d_prefix +
  * h_prefix_off[q] (device ids; host offsets), h_prefix_len[q] >= 1 ids,
  * h_n_blocks[q] blocks, seed h_seeds[q]; its Philox streams are keyed by
  * request index q (not by slot), so its output is that of cd_generate of
@@ -247,7 +268,11 @@ int32_t cd_serve(cd_ctx* ctx, int32_t n_queue, const int32_t* d_prefix, const in
                  int32_t n_slots, int32_t* d_out, const int64_t* h_out_off, int32_t* h_steps,
                  void* stream);
 
-/* Sampler alone on caller logits (rows x vocab fp32, device), rows a
+/* Sampler alone on caller logits (the canvas explainer, step ③: per
+ * position entropy, argmax and lock / re-noise, then the adaptive stop on
+ * the canvas mean entropy and argmax stability; the MarkTechPost article,
+ * "how text diffusion works": low-confidence tokens are re-noised and
+ * predicted again).  Logits rows x vocab fp32, device, rows a
  * multiple of canvas_len, treated as rows/canvas_len requests at pass `step`
  * of block `block`, request indices req0, req0+1, ...  d_prev_argmax (rows
  * int32, may be NULL: then no stability) is the previous pass's argmax.
@@ -272,6 +297,9 @@ enum { CD_BUF_LOGITS = 0,   /* f32 [max_requests*C][vocab] last pass logits */
        CD_BUF_VCACHE = 7,   /* [max_requests][L][Hkv][dh][max_ctx] values (act type) */
        CD_BUF_HIDDEN = 8 }; /* f32 [tokens][d] residual stream after the last layer */
 int32_t cd_get_buffer(cd_ctx* ctx, int32_t which, void** d_ptr, size_t* bytes);
+
+/* The configuration a context was created with (host copy). */
+int32_t cd_get_config(cd_ctx* ctx, cd_config* out);
 
 /* Committed length P of a request (host mirror; no synchronisation). */
 int32_t cd_get_length(cd_ctx* ctx, int32_t req, int32_t* P);

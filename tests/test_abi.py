@@ -138,3 +138,28 @@ def test_sampler_argument_checks():
     args = [1 << 12] * 8
     assert L.cd_sample_step(ctypes.byref(cfg), 1 << 12, 100, None, 1, 1, 0, 0, *args[:7], None) == B.CD_ERR_INVALID_ARG
     assert L.cd_sample_step(ctypes.byref(cfg), 1 << 12, 256, None, 1, 0, 0, 0, *args[:7], None) == B.CD_ERR_INVALID_ARG
+
+
+def test_get_config_and_binding_output_size_checks():
+    import torch
+    cfg = _cfg()
+    ctx = _fake_ctx(cfg)
+    got = B.cd_get_config(ctx)
+    assert (got.canvas_len, got.vocab, got.n_layers, got.max_requests) == (
+        cfg.canvas_len, cfg.vocab, cfg.n_layers, cfg.max_requests)
+    C = cfg.canvas_len
+    for bad in (torch.empty(C - 1, dtype=torch.int32), torch.empty(C, dtype=torch.int64),
+                torch.empty(2 * C, dtype=torch.int32)[::2]):
+        with pytest.raises(ValueError):
+            B.cd_commit_block(ctx, 0, bad)
+    with pytest.raises(B.CDError) as e:            # right size: the library's own state check
+        B.cd_commit_block(ctx, 0, torch.empty(C, dtype=torch.int32), stream=0)
+    assert e.value.code == B.CD_ERR_BAD_STATE
+    with pytest.raises(ValueError):
+        B.cd_generate(ctx, 0, None, 2, 1, torch.empty(C, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        # a buffer of half-size blocks must not pass as two blocks of the context's canvas
+        B.cd_serve(ctx, [torch.zeros(8, dtype=torch.int32)] * 2, [1, 1], [1, 2], 1,
+                   torch.empty(C, dtype=torch.int32))
+    assert B.cd_get_length(ctx, 0) == 0
+    B.cd_ctx_destroy(ctx)
