@@ -55,9 +55,12 @@ def row_stats(z):
     return H, a, pmax, margin
 
 
-def sample(cfg, z, seed, step, block, req):
+def sample(cfg, z, seed, step, block, req, pos=None):
     """One sampler pass over canvas logits z[C][V] after pass ``step``.
 
+    ``pos`` (optional) gives the canvas positions of the rows of z when z
+    holds only some of them (default: rows 0..C-1); every quantity except
+    Hbar is per position, and Hbar is then the mean over the given rows.
     Returns dict(H, a, pmax, margin, lock, x_next, Hbar).
     """
     H, a, pmax, margin = row_stats(z)
@@ -65,7 +68,7 @@ def sample(cfg, z, seed, step, block, req):
         lock = H <= cfg["entropy_bound"]
     else:
         lock = pmax > cfg["lock"]
-    pos = np.arange(z.shape[0])
+    pos = np.arange(z.shape[0]) if pos is None else np.asarray(pos)
     noise = philox.token_draw(seed, pos, step, block, req, z.shape[1])
     x_next = np.where(lock, a, noise)
     return dict(H=H, a=a, pmax=pmax, margin=margin, lock=lock,

@@ -111,15 +111,67 @@ def raw_rows(cfg, name, layer=None, expert=None, rows=None):
     return STD * normal_draws(cfg["weight_seed"], tau, idx)
 
 
+_FMT_CODE = {"f32": 0, "bf16": 1, "fp8": 2, "mxfp4": 3}
+_wgen = None
+
+
+def _c_generator():
+    """The C version of stored_rows (oracle/csrc/wgen.c, built into
+    oracle/libwgen.so), or None when it has not been built."""
+    global _wgen
+    if _wgen is None:
+        import ctypes
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwgen.so")
+        if not os.path.exists(path):
+            _wgen = False
+        else:
+            lib = ctypes.CDLL(path)
+            lib.wgen_rows.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+            lib.wgen_rows.restype = ctypes.c_int
+            _wgen = lib
+    return _wgen or None
+
+
+def stored_rows_c(cfg, name, layer=None, expert=None, rows=None, fmt=None):
+    """stored_rows computed by the C generator (same definition, pinned
+    bit-exactly against the numpy code in tests/test_oracle_wgen.py);
+    fmt="raw" returns the unrounded values.  Requires libwgen.so."""
+    lib = _c_generator()
+    if lib is None:
+        raise RuntimeError("oracle/libwgen.so is not built")
+    n_out, n_in = tensor_shape(cfg, name)
+    rows = np.arange(n_out, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    fmt = storage(cfg, name) if fmt is None else fmt
+    code = 4 if fmt == "raw" else _FMT_CODE[fmt]
+    out = np.empty((rows.size, n_in))
+    aux = np.empty(rows.size * (n_in // 32 if code == 3 else 1))
+    st = lib.wgen_rows(int(cfg["weight_seed"]) & 0xFFFFFFFFFFFFFFFF, tensor_id(cfg, name, layer, expert), n_in,
+                       rows.ctypes.data, rows.size, code, out.ctypes.data, aux.ctypes.data)
+    if st:
+        raise ValueError(f"wgen_rows refused format {fmt} for {name}")
+    if code == 2:
+        return out, aux
+    if code == 3:
+        return out, aux.reshape(rows.size, n_in // 32).astype(np.int64)
+    return out, None
+
+
 def stored_rows(cfg, name, layer=None, expert=None, rows=None):
     """Stored values (as fp64) of selected rows, plus per-row fp8 scales.
 
     Returns (values, scales); scales is None unless the tensor is fp8, in which
     case values are the dequantised q*s and scales the bf16 row scales, or
     MXFP4, in which case scales are the block exponents [rows][K/32].
+    Tensors stored in bf16, fp8 or MXFP4 are generated by the C version when
+    it is built (bit-identical, much faster); fp32 tensors always take the
+    numpy code below.
     """
-    w = raw_rows(cfg, name, layer, expert, rows)
     fmt = storage(cfg, name)
+    if fmt != "f32" and _c_generator() is not None:
+        return stored_rows_c(cfg, name, layer, expert, rows)
+    w = raw_rows(cfg, name, layer, expert, rows)
     if fmt == "f32":
         return round_fp32(w), None
     if fmt == "bf16":

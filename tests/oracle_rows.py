@@ -1,9 +1,104 @@
 """Oracle recomputation of single rows of a full-width forward, for the
 sampled parity tests (test code composing oracle functions; the full-size
-forward is too large for the oracle to run whole)."""
+forward is too large for the oracle to run whole).
+
+A layer is checked from the GPU's own traced input rows of that layer and
+the GPU's K/V cache of that layer: the oracle computes the rows' keys and
+values, their attention over the cache (no mask for canvas rows; keys at or
+before the row's position for prefill rows), the output projection and the
+MoE block, following the GPU's routing where a top-k decision is a near-tie
+(rule R23), and the result is compared with the GPU's input of the next
+layer.  Each layer's weights are generated once for all rows checked in it.
+"""
+from concurrent.futures import ThreadPoolExecutor
+import os
+
 import numpy as np
 
 from oracle import model
+from oracle import sampler as osamp
+from oracle.weights import Weights
+from tests.gpu_util import rel_l2_rows
+
+
+def _n_threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return 4
+
+
+def sample_threaded(w, z, seed, step, block, req):
+    """The oracle sampler over all rows of z[C][V], rows split over threads
+    (each chunk with its canvas positions); Hbar over all rows."""
+    n = z.shape[0]
+    nt = _n_threads()
+    bounds = np.linspace(0, n, nt + 1).astype(int)
+    chunks = [(bounds[i], bounds[i + 1]) for i in range(nt) if bounds[i + 1] > bounds[i]]
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        parts = list(ex.map(lambda c: osamp.sample(w, z[c[0]:c[1]], seed, step, block, req,
+                                                   pos=np.arange(c[0], c[1])), chunks))
+    out = {k: np.concatenate([p[k] for p in parts]) for k in ("H", "a", "pmax", "margin", "lock", "x_next")}
+    out["Hbar"] = float(out["H"].mean())
+    return out
+
+
+def routing_adoptions(w, r, gpu_ids, tol, what):
+    """Rows whose GPU top-k set differs from the oracle's own: every chosen
+    expert must lie within tol * rms(logits) of the oracle's k-th logit."""
+    k = w["k"]
+    own = np.argsort(-r, axis=1, kind="stable")[:, :k]
+    kth = np.sort(r, axis=1)[:, ::-1][:, k - 1]
+    rms = np.sqrt(np.mean(r ** 2, axis=1))
+    adopted = 0
+    for t in range(r.shape[0]):
+        if set(gpu_ids[t]) != set(own[t]):
+            assert np.all(r[t, gpu_ids[t]] >= kth[t] - tol * rms[t]), (what, t)
+            adopted += 1
+    return adopted
+
+
+def check_layer(w, l, items, tol, W=None):
+    """Check layer l for several groups of rows (items), each a dict:
+    h_in [n][d] GPU input rows of layer l; h_out [n][d] the GPU's input rows
+    of layer l+1 (or final residual); pos [n] their positions; K, V
+    [Hkv][m][dh] the GPU's cache of layer l (keys 0..m-1); causal (prefill
+    rows see keys <= their position, canvas rows every key); ids [n][k] the
+    GPU's routing; k_got, v_got [n][Hkv][dh] the GPU's new keys/values.
+    Returns, per item, the max per-row relative L2 errors of k, v and h_out
+    and the routing adoptions; asserts each against tol."""
+    W = Weights(w, cache=False) if W is None else W
+    Hq, Hkv, dh = w["Hq"], w["Hkv"], w["dh"]
+    wq, wk, wv, wo = (W.get(n, l) for n in ("wq", "wk", "wv", "wo"))
+    mids, res = [], []
+    for it in items:
+        n = it["h_in"].shape[0]
+        u = model.rmsnorm(it["h_in"], w["eps"])
+        q = model.rope((u @ wq.T).reshape(n, Hq, dh), it["pos"], w["theta"])
+        k = model.rope((u @ wk.T).reshape(n, Hkv, dh), it["pos"], w["theta"])
+        v = (u @ wv.T).reshape(n, Hkv, dh)
+        m = it["K"].shape[1]
+        allowed = (np.arange(m)[None, :] <= np.asarray(it["pos"])[:, None]) if it["causal"] else None
+        o = model.attention(q, np.asarray(it["K"], np.float64), np.asarray(it["V"], np.float64),
+                            allowed).reshape(n, Hq * dh)
+        mids.append(it["h_in"] + o @ wo.T)
+        res.append(dict(err_k=rel_l2_rows(it["k_got"].reshape(n, -1), k.reshape(n, -1)).max(),
+                        err_v=rel_l2_rows(it["v_got"].reshape(n, -1), v.reshape(n, -1)).max()))
+    h_mid = np.concatenate(mids)
+    ids = np.concatenate([it["ids"] for it in items]).astype(np.int64)
+    u2 = model.rmsnorm(h_mid, w["eps"])
+    f, r, _, _ = model.moe(w, W, l, u2, forced_ids=ids)
+    h_out = h_mid + f
+    i0 = 0
+    for it, rs in zip(items, res):
+        n = it["h_in"].shape[0]
+        rs["adopted"] = routing_adoptions(w, r[i0:i0 + n], ids[i0:i0 + n], tol, (l, it.get("name")))
+        rs["err_h"] = rel_l2_rows(it["h_out"], h_out[i0:i0 + n]).max()
+        rs["n"] = n
+        i0 += n
+        for key in ("err_k", "err_v", "err_h"):
+            assert rs[key] <= tol, (l, it.get("name"), key, rs[key])
+    return res
 
 
 def layer_rows(w, W, l, h_in, rows, K_all, V_all, pos, gpu_ids, tol):
@@ -19,13 +114,33 @@ def layer_rows(w, W, l, h_in, rows, K_all, V_all, pos, gpu_ids, tol):
     h = h_in[rows] + o @ W.get("wo", l).T
     u2 = model.rmsnorm(h, w["eps"])
     r = u2 @ W.get("wr", l).T
-    own = np.argsort(-r, axis=1, kind="stable")[:, :w["k"]]
-    kth = np.sort(r, axis=1)[:, ::-1][:, w["k"] - 1]
-    rms = np.sqrt(np.mean(r ** 2, axis=1))
-    adopted = 0
-    for t in range(len(rows)):
-        if set(gpu_ids[t]) != set(own[t]):
-            assert np.all(r[t, gpu_ids[t]] >= kth[t] - tol * rms[t]), (l, rows[t])
-            adopted += 1
+    adopted = routing_adoptions(w, r, gpu_ids, tol, l)
     f, _, _, _ = model.moe(w, W, l, u2, forced_ids=gpu_ids)
     return h + f, k, v, adopted
+
+
+class Summary:
+    """Largest errors and adoption counts over a test, printed as one line."""
+
+    def __init__(self, name):
+        self.name = name
+        self.err = {}
+        self.adopted = 0
+        self.decisions = 0
+
+    def add(self, key, value):
+        self.err[key] = max(self.err.get(key, 0.0), float(value))
+
+    def add_layer(self, res, prefix=""):
+        for r in res:
+            for key in ("err_k", "err_v", "err_h"):
+                self.add(prefix + key, r[key])
+            self.adopted += r["adopted"]
+            self.decisions += r["n"]
+
+    def report(self, max_adopt_frac):
+        line = {"case": self.name, "adopted": self.adopted, "decisions": self.decisions,
+                **{k: float(f"{v:.3e}") for k, v in sorted(self.err.items())}}
+        print(f"[parity] {line}", flush=True)
+        assert self.adopted <= max(2, max_adopt_frac * self.decisions), line
+        return line
