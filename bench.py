@@ -234,25 +234,80 @@ def kernel_fractions(w, per, per_step):
     return out
 
 
-def cpu_baseline(w):
-    """The oracle, as it stands, on exact work units of the same step, each
-    timed once and scaled by how often the step contains it."""
-    from oracle import model, sampler
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads(n):
+    """A context limiting numpy's BLAS to n threads (threadpoolctl), or a no-op."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_baseline(w, active_experts):
+    """The oracle, as it stands, timed on this host's cores (BLAS threads = the
+    affinity set, and once more single-threaded):
+    * the tiny fp32 model's whole loop (prefill, 48 passes, commit): passes/s;
+    * the sampler on 256 x 262144 fp32 logits: ms per call;
+    * the realistic-width bf16 step (the headline configuration), from exact
+      work units with their weights generated before the timer: layer-0
+      attention + router, 16 routed experts over their own rows, the shared
+      FFN, the LM head on a 4096-row vocabulary slice, and the sampler,
+      scaled by how often one step contains them (30 layers, the measured
+      number of active experts per layer, 64 vocabulary slices)."""
+    from oracle import loop, model, sampler
     from oracle.weights import Weights
 
     cores = len(os.sched_getaffinity(0))
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        blas = cores
-    W = Weights(w, cache=False)
+    out = {"cores": cores, "cpu_model": _cpu_model()}
+
+    # tiny model: the whole loop (weights generated before the timer)
+    wt = synth_inputs.workload("tiny")
+    Wt = Weights(wt)
+    Wt.get("embed"); Wt.get("lm")
+    for l in range(wt["L"]):
+        for n in ("wq", "wk", "wv", "wo", "wr"):
+            Wt.get(n, l)
+        for e in range(wt["E"]):
+            for n in ("wg", "wu", "wd"):
+                Wt.get(n, l, e)
+    pre = synth_inputs.prefix_ids(wt["V"], wt["P0"], wt["prefix_seed"])
+    z = synth_inputs.sampler_logits(w["C"], w["V"], 1)
+    for label, nt in (("", cores), ("_1thread", 1)):
+        with _blas_threads(nt):
+            t0 = time.perf_counter()
+            _, blocks = loop.generate(wt, Wt, pre, 1, wt["gen_seed"])
+            el = time.perf_counter() - t0
+            out["tiny_loop_passes_per_s" + label] = round(blocks[0]["steps"] / el, 3)
+            t0 = time.perf_counter()
+            sampler.sample(w, z, 1, 1, 0, 0)
+            out["sampler_ms_per_call" + label] = round((time.perf_counter() - t0) * 1e3, 1)
+
+    # realistic-width step from work units, weights generated first
+    W = Weights(w)
     rng = np.random.default_rng(0)
     C, d, dh, P0 = w["C"], w["d"], w["dh"], w["P0"]
     h = rng.standard_normal((C, d))
     Kp = rng.standard_normal((w["Hkv"], P0, dh)) * 0.3
     Vp = rng.standard_normal((w["Hkv"], P0, dh)) * 0.3
     pos = P0 + np.arange(C)
+    n_exp, n_slice = 16, 4096
+    for n in ("wq", "wk", "wv", "wo", "wr", "sg", "su", "sd"):
+        W.get(n, 0)
+    for e in range(n_exp):
+        for n in ("wg", "wu", "wd"):
+            W.get(n, 0, e)
+    lm_rows = W.rows("lm", np.arange(n_slice))
 
     t0 = time.perf_counter()                       # attention half of a layer + router
     u = model.rmsnorm(h, w["eps"])
@@ -267,38 +322,36 @@ def cpu_baseline(w):
     ids, gates = model.topk_route(u2 @ W.get("wr", 0).T, w["k"])
     t_attn = time.perf_counter() - t0
 
-    n_exp = 16                                     # routed experts 0..15, each over its own rows
-    t0 = time.perf_counter()
+    t0 = time.perf_counter()                       # routed experts 0..15, each over its own rows
     for e in range(n_exp):
         rows = np.nonzero(ids == e)[0]
         model.swiglu(u2[rows], W.get("wg", 0, e), W.get("wu", 0, e), W.get("wd", 0, e))
     t_expert = (time.perf_counter() - t0) / n_exp
 
     t0 = time.perf_counter()
-    if w["fs"]:
-        model.swiglu(u2, W.get("sg", 0), W.get("su", 0), W.get("sd", 0))
+    model.swiglu(u2, W.get("sg", 0), W.get("su", 0), W.get("sd", 0))
     t_shared = time.perf_counter() - t0
 
-    n_slice = 4096                                 # a vocabulary slice of the LM head
-    t0 = time.perf_counter()
-    model.lm_head(w, W, h2, vocab_rows=np.arange(n_slice))
+    t0 = time.perf_counter()                       # a vocabulary slice of the LM head
+    model.rmsnorm(h2, w["eps"]) @ lm_rows.T
     t_lm = time.perf_counter() - t0
 
-    z = synth_inputs.sampler_logits(C, w["V"], 1)
     t0 = time.perf_counter()
     sampler.sample(w, z, 1, 1, 0, 0)
     t_samp = time.perf_counter() - t0
 
-    step_s = w["L"] * (t_attn + w["E"] * t_expert + t_shared) + (w["V"] / n_slice) * t_lm + t_samp
-    sample_s = t_attn + n_exp * t_expert + t_shared + t_lm + t_samp
-    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(blas), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle incl. its weight generation; timed once each: layer-0 attention+router "
-                       f"({t_attn:.2f}s), {n_exp} routed experts ({t_expert:.2f}s each), shared FFN ({t_shared:.2f}s), "
-                       f"LM head on {n_slice} of {w['V']} vocab rows ({t_lm:.2f}s), sampler on 256x{w['V']} "
-                       f"({t_samp:.2f}s); step = {w['L']}x(attn+{w['E']}xexpert+shared) + "
-                       f"{w['V'] // n_slice}xLM slice + sampler = {step_s:.0f}s; {sample_s:.1f}s of CPU work; "
-                       f"host cores {cores}"),
-            "est_step_s": step_s}
+    step_s = w["L"] * (t_attn + active_experts * t_expert + t_shared) + (w["V"] / n_slice) * t_lm + t_samp
+    out.update({
+        "value": round(1.0 / step_s, 6), "unit": "steps/s", "kind": "oracle",
+        "sample": (f"fp64 numpy oracle on {cores} host cores ({out['cpu_model']}), weights generated before the "
+                   f"timer; timed once each: layer-0 attention+router ({t_attn:.3f}s), {n_exp} routed experts over "
+                   f"their rows ({t_expert * 1e3:.1f} ms each), shared FFN ({t_shared:.3f}s), LM head on {n_slice} "
+                   f"of {w['V']} vocab rows ({t_lm:.3f}s), sampler on 256x{w['V']} ({t_samp:.2f}s); step = "
+                   f"{w['L']}x(attn + {active_experts:.1f} active experts + shared) + {w['V'] // n_slice} LM slices "
+                   f"+ sampler = {step_s:.1f}s. Also: the tiny fp32 model's whole loop and the sampler alone, with "
+                   f"all cores and with one thread"),
+    })
+    return out
 
 
 def prefill_flops(w, n):
@@ -393,6 +446,60 @@ def serve_queue(w, n_queue, n_slots, seed=12):
     return res
 
 
+def workload_line(name, w, g, steps, warmup, prof_steps):
+    """The JSON fields of one measured workload from gpu_part's results."""
+    ms = g["elapsed"] / steps * 1e3
+    per = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in g["prof"].items()}       # avg ms per launch
+    per_step = {k: v[0] / prof_steps for k, v in g["prof"].items()}               # ms per step
+    dom = max(("expert_gate_up", "expert_down"), key=lambda n: per_step[n])
+    part = "gate_up" if dom == "expert_gate_up" else "down"
+    byts = expert_bytes(w, g["active"], part)
+    achieved = byts / (per[dom] * 1e-3) / 1e9
+    R, C = w["R"], w["C"]
+    gen = w.get("blocks", 1) > 1
+    committed = (R * C / g["block_s"]) if g["block_passes"] else None
+    wl = (f"{name}: {w['L']} MoE layers, d={w['d']}, {w['Hq']}/{w['Hkv']} heads x {w['dh']}, "
+          f"{w['E']} experts top-{w['k']} (hidden {w['fe']}) + shared {w['fs']}, vocab {w['V']}, "
+          f"{w['wdtype']} weights, {R} request(s) x prefix {w['P0']}, canvas {C}")
+    if gen:
+        wl += f", {w['blocks']} blocks"
+    roof = {"kernel": f"grouped expert GEMM ({part.replace('_', '/')})", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(part) if name == "step_bf16" else None,
+            "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5), "active_experts": g["active"],
+            # the same bytes against the read+write rate of a plain 1 GiB copy on this GPU
+            "measured_copy_gbs": round(g["copy_gbs"], 1), "frac_of_measured_copy": round(achieved / g["copy_gbs"], 4)}
+    if R * C * w["k"] / w["E"] >= 256:
+        # many rows per expert: the grouped GEMM runs on the bf16 MFMA pipe
+        tf = expert_flops(w, part) / (per[dom] * 1e-3) / 1e12
+        roof = {"kernel": roof["kernel"], "bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": int(expert_flops(w, part)), "avg_launch_ms": round(per[dom], 5),
+                "hbm_gbs": round(achieved, 1)}
+    return {
+        "value": round(committed, 3) if gen else round(1e3 / ms, 3),
+        "unit": "committed tok/s" if gen else "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if w["wdtype"] == "f32" else "bf16", "data": "synthetic",
+        "config": {"workload": wl, "weights": w["wdtype"], "requests": R, "canvas": C, "prefix": w["P0"],
+                   "blocks": w.get("blocks", 1)},
+        "steps_per_s": round(1e3 / ms, 3),
+        "canvas_tok_s": round(R * C * 1e3 / ms, 1),
+        "committed_tok_s": round(committed, 2) if committed else None,
+        "block_passes": g["block_passes"], "blocks": g["blocks"],
+        "prefill_ms": round(g["prefill_ms"], 2),
+        "prefill": prefill_line(w, g["prefill_ms"] / R),
+        "roofline": roof,
+        "ms_per_step_median": round(float(np.median(g["step_ms"])), 4),
+        "ms_per_step_p95": round(float(np.percentile(g["step_ms"], 95)), 4),
+        "kernel_fractions": kernel_fractions(w, per, per_step),
+        "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items() if v > 0},
+        "routing": g["route"],
+        "device": g["device"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +509,8 @@ def main():
     ap.add_argument("--workload", default="step_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block", action="store_true", help="skip the full-block measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="step_bf16 only: skip the gen_bf16 and batch_fp8 lines added to the default run")
     ap.add_argument("--copy-calib", action="store_true", help="only run the byte-counter calibration copy")
     ap.add_argument("--sweep", action="store_true",
                     help="also time one full block at 1, 2, 4 and 32 requests (the 32-request fp8 model)")
@@ -417,62 +526,22 @@ def main():
         sys.exit(2)
     w = synth_inputs.workload(args.workload)
     g = gpu_part(w, args.steps, args.warmup, args.prof_steps, do_block=not args.no_block)
-    ms = g["elapsed"] / args.steps * 1e3
-    per = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in g["prof"].items()}       # avg ms per launch
-    per_step = {k: v[0] / args.prof_steps for k, v in g["prof"].items()}          # ms per step
-    dom = max(("expert_gate_up", "expert_down"), key=lambda n: per_step[n])
-    part = "gate_up" if dom == "expert_gate_up" else "down"
-    byts = expert_bytes(w, g["active"], part)
-    achieved = byts / (per[dom] * 1e-3) / 1e9
-    R, C = w["R"], w["C"]
-    gen = w.get("blocks", 1) > 1
-    committed = (R * C / g["block_s"]) if g["block_passes"] else None
-    wl = (f"{args.workload}: {w['L']} MoE layers, d={w['d']}, {w['Hq']}/{w['Hkv']} heads x {w['dh']}, "
-          f"{w['E']} experts top-{w['k']} (hidden {w['fe']}) + shared {w['fs']}, vocab {w['V']}, "
-          f"{w['wdtype']} weights, {R} request(s) x prefix {w['P0']}, canvas {C}")
-    if gen:
-        wl += f", {w['blocks']} blocks"
-    roof = {"kernel": f"grouped expert GEMM ({part.replace('_', '/')})", "bound": "hbm",
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(part) if args.workload == "step_bf16" else None,
-            "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5), "active_experts": g["active"],
-            # the same bytes against the read+write rate of a plain 1 GiB copy on this GPU
-            "measured_copy_gbs": round(g["copy_gbs"], 1), "frac_of_measured_copy": round(achieved / g["copy_gbs"], 4)}
-    if R * C * w["k"] / w["E"] >= 256:
-        # many rows per expert: the grouped GEMM runs on the bf16 MFMA pipe
-        tf = expert_flops(w, part) / (per[dom] * 1e-3) / 1e12
-        roof = {"kernel": roof["kernel"], "bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "flops_per_launch": int(expert_flops(w, part)), "avg_launch_ms": round(per[dom], 5),
-                "hbm_gbs": round(achieved, 1)}
-    line = {
-        "metric": "canvas denoise steps/s + committed tok/s (256-tok block), % MFMA/HBM peak",
-        "value": round(committed, 3) if gen else round(1e3 / ms, 3),
-        "unit": "committed tok/s" if gen else "steps/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if w["wdtype"] == "f32" else "bf16", "data": "synthetic",
-        "config": {"workload": wl, "weights": w["wdtype"], "requests": R, "canvas": C, "prefix": w["P0"], "blocks": w.get("blocks", 1)},
-        "steps_per_s": round(1e3 / ms, 3),
-        "canvas_tok_s": round(R * C * 1e3 / ms, 1),
-        "committed_tok_s": round(committed, 2) if committed else None,
-        "block_passes": g["block_passes"], "blocks": g["blocks"],
-        "prefill_ms": round(g["prefill_ms"], 2),
-        "prefill": prefill_line(w, g["prefill_ms"] / R),
-        "roofline": roof,
-        "ms_per_step_median": round(float(np.median(g["step_ms"])), 4),
-        "ms_per_step_p95": round(float(np.percentile(g["step_ms"], 95)), 4),
-        "kernel_fractions": kernel_fractions(w, per, per_step),
-        "kernels_ms_per_step": {k: round(v, 4) for k, v in per_step.items() if v > 0},
-        "routing": g["route"],
-        "device": g["device"],
-    }
+    line = {"metric": "canvas denoise steps/s + committed tok/s (256-tok block), % MFMA/HBM peak"}
+    line.update(workload_line(args.workload, w, g, args.steps, args.warmup, args.prof_steps))
+    if args.workload == "step_bf16" and not args.no_extra:
+        # the other measured configurations, each timed the same way in this run
+        for name, steps, warmup, prof, block in (("gen_bf16", 3, 1, 2, True), ("batch_fp8", 10, 2, 3, False)):
+            log(f"extra workload {name}")
+            we = synth_inputs.workload(name)
+            ge = gpu_part(we, steps, warmup, prof, do_block=block)
+            ex = workload_line(name, we, ge, steps, warmup, prof)
+            for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data", "device",
+                      "routing"):
+                ex.pop(k, None)
+            line[name] = ex
     if not args.no_cpu_baseline and args.workload == "step_bf16":
         log("cpu baseline (oracle sample)")
-        cb = cpu_baseline(w)
-        cb.pop("est_step_s")
-        cb["value"] = float(f"{cb['value']:.6g}")
-        line["cpu_baseline"] = cb
+        line["cpu_baseline"] = cpu_baseline(w, g["active"])
     if args.sweep:
         line["concurrency_sweep"] = {"workload": "batch_fp8 model, one 256-token block per request after a "
                                                  f"{w['P0']}-token prefix",
