@@ -9,7 +9,7 @@ bench.py times.  The oracle checks what it can compute row by row:
 * for the first and the last request, 16 canvas rows each (two in every
   32-row tile of the request's canvas) at every layer, from the GPU's own
   layer inputs and K/V cache: the rows' keys/values and the layer output,
-  following the GPU's routing under the near-tie rule (at most 2% adopted);
+  following the GPU's routing under the near-tie rule (at most 4% adopted);
 * the LM head on sampled vocabulary rows of the last request;
 * the sampler on the last request's GPU logits (its own Philox stream).
 The same batch with MXFP4 experts (``batch_mxfp4``: 512 rows per expert, so
@@ -27,7 +27,7 @@ from oracle import model, philox
 from oracle.weights import Weights
 from tests.gpu_util import TOL, announce, rel_l2_rows, to_np
 from tests.oracle_rows import Summary, check_layer
-from tests.test_gpu_full_width import CANVAS_ROWS, check_sampler
+from tests.test_gpu_full_width import ADOPT_CAP, CANVAS_ROWS, check_sampler
 
 pytestmark = pytest.mark.gpu
 
@@ -101,4 +101,4 @@ def test_batch_full_width_every_layer(name):
     S.add("lm_head", rel_l2_rows(z[:, vrows], zref).max())
     assert S.err["lm_head"] <= tol
     check_sampler(w, z, am, lock, xn, H, infos[rl].mean_entropy, seed, 1, 0, rl)
-    S.report(0.02)
+    S.report(ADOPT_CAP[w["wdtype"]])

@@ -13,7 +13,7 @@ test, so it checks what it can compute row by row, at every layer:
   tile, both 128-row halves): the rows' keys/values in the cache and the
   layer output (attention over the whole cache, no mask);
 * routing: the GPU's top-k set equals the oracle's own, or lies within the
-  near-tie band (then the oracle follows it); at most 2% of the checked
+  near-tie band (then the oracle follows it); at most 4% of the checked
   decisions may be such adoptions;
 * the LM head on 512 sampled vocabulary rows from the GPU's final residual;
 * the sampler on the GPU's own logits (all 256 x 262144).
@@ -34,6 +34,9 @@ from tests.oracle_rows import Summary, check_layer, sample_threaded
 
 pytestmark = pytest.mark.gpu
 
+# largest share of checked routing decisions the GPU may take from the
+# near-tie band (its top-k set differs from the oracle's own)
+ADOPT_CAP = {"f32": 0.01, "bf16": 0.04, "fp8": 0.04, "mxfp4": 0.04}
 CANVAS_ROWS = np.array([2, 29, 35, 60, 66, 93, 101, 126, 130, 157, 163, 190, 197, 222, 229, 254])
 PREFILL_POS = np.array([0, 1, 777, 2047, 2048, 3001, 4094, 4095])
 
@@ -117,4 +120,4 @@ def test_step_full_width_every_layer(name):
     S.add("lm_head", rel_l2_rows(z[:, vrows], zref).max())
     assert S.err["lm_head"] <= tol
     check_sampler(w, z, am, lock, xn, H, info.mean_entropy, seed, 1, 0, 0)
-    S.report(0.02)
+    S.report(ADOPT_CAP[w["wdtype"]])

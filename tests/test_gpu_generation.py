@@ -21,7 +21,7 @@ oracle:
 test_generation_commit_every_layer checks the commit of block 0 and of block
 3 at every layer (the committed block's keys/values and each layer's output
 at 16 rows).  Tolerance bf16 2e-2 (per-row relative L2); routing follows the
-near-tie rule with at most 2% of the checked decisions adopted."""
+near-tie rule with at most 4% of the checked decisions adopted."""
 import numpy as np
 import pytest
 import torch
@@ -33,7 +33,7 @@ from oracle import model, philox
 from oracle.weights import Weights
 from tests.gpu_util import TOL, announce, rel_l2_rows, to_np
 from tests.oracle_rows import Summary, check_layer
-from tests.test_gpu_full_width import CANVAS_ROWS, check_sampler
+from tests.test_gpu_full_width import ADOPT_CAP, CANVAS_ROWS, check_sampler
 
 pytestmark = pytest.mark.gpu
 
@@ -149,7 +149,7 @@ def test_generation_lockstep():
             assert torch.equal(eng.vcache()[0, :, :, :, :Pp], prefix_kv[1]), b
         prefix_kv = (eng.kcache()[0, :, :, :P + C, :].clone(), eng.vcache()[0, :, :, :, :P + C].clone())
     g.close()
-    S.report(0.02)
+    S.report(ADOPT_CAP[w["wdtype"]])
 
 
 @pytest.mark.parametrize("block", [0, 3])
@@ -180,4 +180,4 @@ def test_generation_commit_every_layer(block):
         res = check_layer(w, l, layer_items(fw, l, P, C), tol)
         S.add_layer(res)
         print(f"layer {l}: {[{k2: float(f'{v:.2e}') for k2, v in r.items()} for r in res]}", flush=True)
-    S.report(0.02)
+    S.report(ADOPT_CAP[w["wdtype"]])
