@@ -80,6 +80,9 @@ def lib():
             "cd_sample_step": [P(cd_config), c_void_p, c_int32, c_void_p, c_uint64, c_int32, c_int32,
                                c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_void_p],
+            "cd_sample_step_noalloc": [P(cd_config), c_void_p, c_int32, c_void_p, c_uint64, c_int32, c_int32,
+                                       c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p],
             "cd_get_buffer": [c_void_p, c_int32, P(c_void_p), P(c_size_t)],
             "cd_get_length": [c_void_p, c_int32, P(c_int32)],
             "cd_get_config": [c_void_p, P(cd_config)],
@@ -106,7 +109,7 @@ def exported_names():
     return ["cd_weights_bytes", "cd_state_bytes", "cd_ctx_create", "cd_ctx_destroy", "cd_reset",
             "cd_synth_weights", "cd_set_weight", "cd_get_weight", "cd_prefill", "cd_init_canvas",
             "cd_denoise_step", "cd_read_step_info", "cd_commit_block", "cd_generate",
-            "cd_sample_workspace_bytes", "cd_sample_step", "cd_get_buffer", "cd_get_config", "cd_get_length",
+            "cd_sample_workspace_bytes", "cd_sample_step", "cd_sample_step_noalloc", "cd_get_buffer", "cd_get_config", "cd_get_length",
             "cd_set_trace", "cd_abort_canvas", "cd_release", "cd_move_request", "cd_serve", "cd_profile", "cd_profile_read",
             "cd_last_error"]
 
@@ -278,6 +281,13 @@ def cd_sample_step(cfg, logits, rows, prev_argmax, seed, step, block, req0, toke
     _check(lib().cd_sample_step(ctypes.byref(cfg), _ptr(logits), rows, _ptr(prev_argmax), seed, step,
                                 block, req0, _ptr(tokens), _ptr(argmax), _ptr(lock), _ptr(entropy),
                                 _ptr(pmax), _ptr(info), _ptr(workspace), _stream(stream)))
+
+
+def cd_sample_step_noalloc(cfg, logits, rows, prev_argmax, seed, step, block, req0, tokens, argmax, lock,
+                           entropy, pmax, info, stream=None):
+    _check(lib().cd_sample_step_noalloc(ctypes.byref(cfg), _ptr(logits), rows, _ptr(prev_argmax), seed, step,
+                                        block, req0, _ptr(tokens), _ptr(argmax), _ptr(lock), _ptr(entropy),
+                                        _ptr(pmax), _ptr(info), _stream(stream)))
 
 
 def cd_get_buffer(ctx, which):

@@ -1088,22 +1088,30 @@ int32_t cd_sample_workspace_bytes(int32_t rows, int32_t vocab, size_t* bytes) {
   return CD_OK;
 }
 
-int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows, const int32_t* d_prev_argmax,
-                       uint64_t seed, int32_t step, int32_t block, int32_t req0, int32_t* d_tokens,
-                       int32_t* d_argmax, uint8_t* d_lock, double* d_entropy, double* d_pmax,
-                       cd_step_info* d_info, void* d_workspace, void* stream) {
+// argument checks shared by the two sampler entry points
+static int32_t check_sample_args(const cd_config* cfg, const float* d_logits, int32_t rows, int32_t step,
+                                 int32_t block, int32_t req0, const int32_t* d_tokens, const int32_t* d_argmax,
+                                 const uint8_t* d_lock, const double* d_entropy, const double* d_pmax,
+                                 const cd_step_info* d_info) {
   if (!cfg) return fail(CD_ERR_INVALID_ARG, "null config");
   if (cfg->vocab < 128 || cfg->vocab % 128 || cfg->canvas_len < 1)
     return fail(CD_ERR_UNSUPPORTED, "vocab must be a positive multiple of 128");
   if (rows < 1 || rows % cfg->canvas_len) return fail(CD_ERR_INVALID_ARG, "rows must be a multiple of canvas_len");
-  if (!d_logits || !d_tokens || !d_argmax || !d_lock || !d_entropy || !d_pmax || !d_info || !d_workspace)
+  if (!d_logits || !d_tokens || !d_argmax || !d_lock || !d_entropy || !d_pmax || !d_info)
     return fail(CD_ERR_INVALID_ARG, "null buffer");
   if (step < 1 || block < 0 || req0 < 0) return fail(CD_ERR_INVALID_ARG, "bad step/block/request");
+  return CD_OK;
+}
+
+static int32_t sample_on(const cd_config* cfg, const float* d_logits, int32_t rows, const int32_t* d_prev_argmax,
+                         uint64_t seed, int32_t step, int32_t block, int32_t req0, int32_t* d_tokens,
+                         int32_t* d_argmax, uint8_t* d_lock, double* d_entropy, double* d_pmax,
+                         cd_step_info* d_info, float4* part, void* stream) {
   SampleArgs a;
   memset(&a, 0, sizeof a);
   a.logits = d_logits; a.rows = rows; a.V = cfg->vocab; a.C = cfg->canvas_len;
   a.n_chunks = sampler_chunks(cfg->vocab); a.chunk = cfg->vocab / a.n_chunks;
-  a.part = reinterpret_cast<float4*>(d_workspace);
+  a.part = part;
   a.prev_a = d_prev_argmax; a.tokens = d_tokens; a.argmax = d_argmax; a.lock = d_lock;
   a.entropy = d_entropy; a.pmax = d_pmax; a.info = d_info; a.canvas_in = nullptr; a.rq = nullptr;
   a.seed = seed; a.step = step; a.block = block; a.req0 = req0;
@@ -1112,6 +1120,36 @@ int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows
   launch_sampler_part(a, strm(stream));
   launch_sampler_final(a, strm(stream));
   return hip_status("sample step");
+}
+
+int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows, const int32_t* d_prev_argmax,
+                       uint64_t seed, int32_t step, int32_t block, int32_t req0, int32_t* d_tokens,
+                       int32_t* d_argmax, uint8_t* d_lock, double* d_entropy, double* d_pmax,
+                       cd_step_info* d_info, void* d_workspace, void* stream) {
+  if (int32_t st = check_sample_args(cfg, d_logits, rows, step, block, req0, d_tokens, d_argmax, d_lock, d_entropy,
+                                     d_pmax, d_info))
+    return st;
+  if (!d_workspace) return fail(CD_ERR_INVALID_ARG, "null workspace");
+  return sample_on(cfg, d_logits, rows, d_prev_argmax, seed, step, block, req0, d_tokens, d_argmax, d_lock,
+                   d_entropy, d_pmax, d_info, reinterpret_cast<float4*>(d_workspace), stream);
+}
+
+int32_t cd_sample_step_noalloc(const cd_config* cfg, const float* d_logits, int32_t rows,
+                               const int32_t* d_prev_argmax, uint64_t seed, int32_t step, int32_t block,
+                               int32_t req0, int32_t* d_tokens, int32_t* d_argmax, uint8_t* d_lock,
+                               double* d_entropy, double* d_pmax, cd_step_info* d_info, void* stream) {
+  if (int32_t st = check_sample_args(cfg, d_logits, rows, step, block, req0, d_tokens, d_argmax, d_lock, d_entropy,
+                                     d_pmax, d_info))
+    return st;
+  const int64_t partials = (int64_t)rows * sampler_chunks(cfg->vocab);
+  if (partials > SAMPLER_SCRATCH_PARTIALS)
+    return fail(CD_ERR_CAPACITY, "rows x chunks = %lld partials exceed the fixed buffer's %d (at most %d rows at "
+                "vocab %d)", (long long)partials, SAMPLER_SCRATCH_PARTIALS,
+                SAMPLER_SCRATCH_PARTIALS / sampler_chunks(cfg->vocab), cfg->vocab);
+  float4* part = nullptr;
+  if (sampler_scratch(&part)) return fail(CD_ERR_HIP, "fixed sampler buffer: device address lookup failed");
+  return sample_on(cfg, d_logits, rows, d_prev_argmax, seed, step, block, req0, d_tokens, d_argmax, d_lock,
+                   d_entropy, d_pmax, d_info, part, stream);
 }
 
 int32_t cd_get_buffer(cd_ctx* c, int32_t which, void** d_ptr, size_t* bytes) {

@@ -14,6 +14,8 @@
 // argmax stability against the previous pass and the stop flag.  A request
 // whose stop has fired takes no further pass: a later pass leaves its state
 // as it was and flags its record (after_stop).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "../../include/cd.h"
@@ -209,6 +211,27 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
       a.rq[rr].stopped = inf.stop;
     }
   }
+}
+
+// Fixed partial buffer of the allocation-free sampler entry point: one per
+// GPU, alive until the process ends.  Host code never uses this name as an
+// address (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) float4 scratch[SAMPLER_SCRATCH_PARTIALS];
+
+int sampler_scratch(float4** out) {
+  static std::mutex mu;
+  static float4* ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -4;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -4;
+    ptr[dev] = reinterpret_cast<float4*>(p);
+  }
+  *out = ptr[dev];
+  return 0;
 }
 
 void launch_sampler_part(const SampleArgs& a, hipStream_t s) {

@@ -200,6 +200,12 @@ struct SampleArgs {
   float ent_bound;
 };
 void launch_sampler_part(const SampleArgs& a, hipStream_t s);
+// Partials held by the library's own fixed device buffer (allocation-free
+// sampler entry point): at most this many (row, chunk) partials, 16 bytes each.
+constexpr int SAMPLER_SCRATCH_PARTIALS = 65536;
+// That buffer's device address on the current device (looked up once per
+// device with hipGetSymbolAddress); 0, or CD_ERR_HIP (-4) on failure.
+int sampler_scratch(float4** out);
 void launch_sampler_final(const SampleArgs& a, hipStream_t s);
 
 }  // namespace cd

@@ -286,6 +286,22 @@ int32_t cd_sample_step(const cd_config* cfg, const float* d_logits, int32_t rows
                        uint8_t* d_lock, double* d_entropy, double* d_pmax,
                        cd_step_info* d_info, void* d_workspace, void* stream);
 
+/* cd_sample_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The chunk partials go to a fixed
+ * buffer inside the library (one per GPU, 1 MiB, held until the process
+ * ends): rows * chunks must not exceed 65536, chunks = the number of
+ * 8192-logit pieces of a row (32 at vocab 262144, so at most 2048 rows);
+ * larger calls return CD_ERR_CAPACITY with nothing enqueued.  The buffer is
+ * fully written before it is read, so nothing needs clearing between calls;
+ * calls that overlap in time on one GPU (other streams, other threads) share
+ * the buffer and race.  No device memory is allocated or freed.  Arguments,
+ * outputs and results are those of cd_sample_step. */
+int32_t cd_sample_step_noalloc(const cd_config* cfg, const float* d_logits, int32_t rows,
+                               const int32_t* d_prev_argmax, uint64_t seed, int32_t step, int32_t block,
+                               int32_t req0, int32_t* d_tokens, int32_t* d_argmax, uint8_t* d_lock,
+                               double* d_entropy, double* d_pmax, cd_step_info* d_info, void* stream);
+
 /* Internal buffers exposed for inspection (device pointers into d_state). */
 enum { CD_BUF_LOGITS = 0,   /* f32 [max_requests*C][vocab] last pass logits */
        CD_BUF_CANVAS = 1,   /* i32 [max_requests][C] current canvas */
