@@ -314,7 +314,7 @@ def cd_set_trace(ctx, h_layers=None, topk_ids=None, topk_gates=None):
 
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "attn_merge", "o_proj", "router", "route",
                 "expert_gate_up", "expert_down", "combine", "shared_gate_up", "shared_down", "lm_head",
-                "sampler_part", "sampler_final", "other"]
+                "sampler_part", "sampler_final", "other", "act_quant"]
 
 
 def cd_abort_canvas(ctx, req):

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("CD_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["k_gemm.hip", "k_gemm_x.hip", "k_pack.hip", "k_attn.hip", "k_moe.hip", "k_misc.hip", "k_sampler.hip", "cd_api.cpp"]
+SOURCES = ["k_gemm.hip", "k_gemm_x.hip", "k_gemm_x8.hip", "k_pack.hip", "k_attn.hip", "k_moe.hip", "k_misc.hip", "k_sampler.hip", "cd_api.cpp"]
 # packed fp32 ops are disabled: hand-written float code must not be turned
 # into v_pk_* instructions
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

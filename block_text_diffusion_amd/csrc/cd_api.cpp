@@ -77,6 +77,11 @@ struct Plan {
   int64_t rq, canvas, argmax, lock, entropy, pmax, info, h, u, q, o, part_o, part_ml, rlog, topk_id,
       topk_gate, blk_cnt, seg_off, row_map, slot, tiles, n_tiles, aperm, yperm, sact, sout, logits, spart, rope,
       kcache, vcache, zero;
+  // fp8 activations of the W8A8 path (fp8 attention weights and forwards of
+  // more than 256 rows): E4M3 rows with one fp32 scale per row
+  bool x8;
+  int64_t xq, xqs, aq, aqs;
+  int x8_ld;
   int64_t max_rows, max_tiles, n_blk_max, n_chunks;
   int64_t kv_req_stride, kv_layer_stride;   // elements
   int64_t state_bytes;
@@ -215,6 +220,16 @@ Plan make_plan(const cd_config& c) {
   p.rope = s.take(8LL * p.ctx * (dh / 2));
   p.kcache = s.take((int64_t)ae * p.kv_req_stride * R);
   p.vcache = s.take((int64_t)ae * p.kv_req_stride * R);
+  // W8A8 needs fp8 attention weights, a forward that takes the LDS-staged
+  // kernel (more than 256 rows) and contraction widths the quantiser holds
+  const int qd = c.n_q_heads * dh;
+  p.x8 = p.wdt_attn == CD_FP8 && T > 256 && std::max(d, qd) <= 4096 && c.expert_hidden <= 4096 &&
+         qd % 64 == 0;
+  p.x8_ld = std::max(d, qd);
+  p.xq = p.x8 ? s.take((int64_t)T * p.x8_ld) : -1;
+  p.xqs = p.x8 ? s.take(4LL * T) : -1;
+  p.aq = p.x8 ? s.take(p.max_rows * (int64_t)c.expert_hidden) : -1;
+  p.aqs = p.x8 ? s.take(4LL * p.max_rows) : -1;
   p.state_bytes = s.off;
   return p;
 }
@@ -346,7 +361,11 @@ void note_launch(cd_ctx* c, int st) {
   if (st && !c->launch_err) c->launch_err = st;
 }
 
-void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
+// w8a8: the launch may quantise its activations to E4M3 (fp8 weights on the
+// LDS-staged kernel).  The QKV projection takes it; the output projection
+// keeps bf16 activations, since its output feeds the router directly and the
+// activation rounding moved near-tie routing decisions too far.
+void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s, bool w8a8 = false) {
   // the LDS-staged kernel needs enough (256-row slab, 256-column chunk)
   // items to fill the chip; the expert-combining epilogue gathers 8 rows per
   // output and prefers the many workgroups of the row-tiled kernel
@@ -355,6 +374,15 @@ void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
   if (lds_staged) {
     a.M = M;
     a.tiles = nullptr;
+    if (w8a8 && wdt == CD_FP8 && c->p.x8 && epi != EPI_F32) {
+      // W8A8: the activation rows quantised to E4M3 with a scale per row
+      uint8_t* xq = c->st<uint8_t>(c->p.xq);
+      float* xqs = c->st<float>(c->p.xqs);
+      { PROF(CD_PROF_QUANT); note_launch(c, launch_quant_fp8(a.X, a.ldx, M, a.K, xq, a.K, xqs, nullptr, s)); }
+      a.X = xq; a.ldx = a.K; a.xscale = xqs;
+      note_launch(c, launch_gemm_x8(epi, a, s));
+      return;
+    }
     note_launch(c, launch_gemm_x(wdt, c->p.adt, epi, a, s));
     return;
   }
@@ -368,12 +396,25 @@ void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s) {
 
 // rows: assignments of this forward (T * top_k); the grid is sized for the
 // most tiles they can form, so idle workgroups stay few
-void gemm_grouped(cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, hipStream_t s) {
+// x_rows: rows of X (the tokens for gate/up, the permuted rows for down);
+// x_rows_dev: their device count (down: the padded segments' end) or null
+void gemm_grouped(cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, int x_rows, const int32_t* x_rows_dev,
+                  hipStream_t s) {
   a.tiles = c->st<int32_t>(c->p.tiles);
   a.n_tiles = c->st<int32_t>(c->p.n_tiles);
   if (big_expert_tiles(rows, c->p.c.n_experts)) {
     a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + BIG_TILE_ROWS - 1) / BIG_TILE_ROWS +
                                                             std::min<int64_t>(rows, c->p.c.n_experts));
+    if (wdt == CD_FP8 && c->p.x8) {
+      // W8A8 (see gemm_dense); the down projection's input has its own buffer
+      const bool down = epi == EPI_ROWS;
+      uint8_t* xq = c->st<uint8_t>(down ? c->p.aq : c->p.xq);
+      float* xqs = c->st<float>(down ? c->p.aqs : c->p.xqs);
+      { PROF(CD_PROF_QUANT); note_launch(c, launch_quant_fp8(a.X, a.ldx, x_rows, a.K, xq, a.K, xqs, x_rows_dev, s)); }
+      a.X = xq; a.ldx = a.K; a.xscale = xqs;
+      note_launch(c, launch_gemm_x8(epi, a, s));
+      return;
+    }
     note_launch(c, launch_gemm_x(wdt, c->p.adt, epi, a, s));
     return;
   }
@@ -445,7 +486,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       a.max_ctx = p.ctx; a.Hq = g.n_q_heads; a.Hkv = g.n_kv_heads; a.dh = dh;
       a.rows_per_req = rows_per_req; a.pos0 = pos0; a.pos0_stride = pos_stride; a.rope_cs = rope;
       a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)dh));   // log2(e) / sqrt(dh)
-      { PROF(CD_PROF_QKV); gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s); }
+      { PROF(CD_PROF_QKV); gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s, true); }
       at.kc = kc; at.vc = vc;
     }
     { PROF(CD_PROF_ATTN); launch_attention(adt, at, s); }
@@ -506,14 +547,14 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       a.row_map = c->st<int32_t>(p.row_map);
       a.w_gstride = p.gu_stride; a.s_gstride = p.gu_npad; a.mx_off = p.gu_mx;
       PROF(CD_PROF_EXPERT_GU);
-      gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, (int64_t)T * k, s);
+      gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, (int64_t)T * k, T, nullptr, s);
     }
     {
       GemmArgs a = gemm_base(c->st<void>(p.aperm), g.expert_hidden, c->W + lw.dn, c->wt<float>(lw.dn_s),
                              g.expert_hidden, p.dn_npad, d, c->st<void>(p.yperm), d);
       a.w_gstride = p.dn_stride; a.s_gstride = p.dn_npad; a.mx_off = p.dn_mx;
       PROF(CD_PROF_EXPERT_DOWN);
-      gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, s);
+      gemm_grouped(c, p.wdt_exp, EPI_ROWS, a, (int64_t)T * k, (int)p.max_rows, c->st<int32_t>(p.seg_off) + E, s);
     }
     // h += sum_j gate_j * y_j (choice order) + shared FFN row; the same kernel
     // writes u = RMSNorm(h) for the next layer or the LM head (every reader

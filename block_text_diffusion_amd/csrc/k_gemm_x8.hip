@@ -1,0 +1,279 @@
+// fp8 x fp8 GEMM on 256-row work items (the batched fp8 model's QKV, O and
+// routed-expert projections):
+//   Y[m][n] = sx[m] * sw[n] * sum_k qx[m][k] qw[n][k]
+// qw: E4M3 weights in the packed fragment tiles (per-row scale sw, applied
+// by the epilogue like the register path's); qx: E4M3 activations with one
+// fp32 scale sx per row, written by k_quant_fp8 just before the launch.
+// The contraction runs on the 16x16x128 fp8 MFMA, twice the bf16 rate: a
+// stage is two 64-column k-tiles, and one MFMA takes both k-tiles' bytes of
+// a lane (32 per operand).  Weights and activations assign the same K
+// columns to a lane's bytes (the weight tile and activation fragment layouts
+// match), so the product is the dot product whatever order the hardware
+// gives the 128 bytes.  Otherwise the structure of k_gemm_x: work item =
+// 256 rows x 256 columns, eight waves (rows 0-127 / 128-255 x four
+// 16-column weight tiles each), activation fragments copied into LDS with
+// global_load_lds, weights into registers, DIST stages in flight.
+#include "common.h"
+#include "gemm_epi.h"
+#include "kernels.h"
+
+namespace cd {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mma_fp8(const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1,
+                                         f32x4 acc) {
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  // formats E4M3 / E4M3, no block scales
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+}
+
+constexpr int Q8_WAVES = 8, Q8_MTW = 8, Q8_NTW = 4;   // as k_gemm_x: 256 rows x 256 columns
+constexpr int Q8_NBUF = 3, Q8_DIST = 2;
+
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
+  constexpr int BLK = 32;                         // activation fragments per stage: 16 row tiles x 2 k-tiles
+  constexpr int BPW = BLK / Q8_WAVES;             // each wave copies 4
+  constexpr int LPS = BPW + 2 * Q8_NTW;           // vector loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[Q8_NBUF][BLK * 1024];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int nchunks = (a.Nt + 4 * Q8_NTW - 1) / (4 * Q8_NTW);
+  // work items dealt to the 8 XCDs chunk-major, as in k_gemm_x
+  int chunk, tile;
+  {
+    const int nt = a.tiles ? *a.n_tiles : (a.M + 255) / 256;
+    const int work = nt * nchunks;
+    const int w8 = (work + 7) & ~7;
+    const int bid = blockIdx.x;
+    if (bid >= w8) return;
+    const int logical = (bid & 7) * (w8 >> 3) + (bid >> 3);
+    if (logical >= work) return;
+    chunk = logical / nt;
+    tile = logical - chunk * nt;
+  }
+  int group = 0, row0, rows;
+  if (a.tiles) {
+    group = a.tiles[4 * tile];
+    row0 = a.tiles[4 * tile + 1];
+    rows = a.tiles[4 * tile + 2];
+  } else {
+    row0 = tile * 256;
+    rows = min(256, a.M - row0);
+  }
+  const int KT = a.K / 64;                  // 64-column k-tiles
+  const int nst = (KT + 1) / 2;             // stages of two k-tiles (the last may hold one)
+  const int nt0 = chunk * 4 * Q8_NTW + wn * Q8_NTW;
+  const bool row_live = wm * Q8_MTW * 16 < rows;
+  const uint8_t* wbase = a.W + (int64_t)group * a.w_gstride;
+  const uint8_t* wp[Q8_NTW];
+#pragma unroll
+  for (int j = 0; j < Q8_NTW; ++j) wp[j] = wbase + (int64_t)min(nt0 + j, a.Nt - 1) * KT * 1024 + lane * 16;
+  // fragment f = mt*2 + h: rows mt*16.. of k-tile 2s + h; rows past the
+  // tile's end read its last row (finite), their results are dropped
+  const uint8_t* xsrc[BPW];
+  int xh[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int f = wave * BPW + i;
+    const int mt = f >> 1;
+    xh[i] = f & 1;
+    const int r = min(mt * 16 + (lane & 15), rows - 1);
+    int src = a.row_map ? a.row_map[row0 + r] : row0 + r;
+    if (src < 0) src = 0;
+    xsrc[i] = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)src * a.ldx + (lane >> 4) * 16;
+  }
+
+  f32x4 acc[Q8_MTW][Q8_NTW];
+#pragma unroll
+  for (int mt = 0; mt < Q8_MTW; ++mt)
+#pragma unroll
+    for (int j = 0; j < Q8_NTW; ++j) acc[mt][j] = f32x4{0, 0, 0, 0};
+  u32x4 w[Q8_DIST][Q8_NTW][2];
+
+  // k-tile indices past the end are clamped to the last one: every copy
+  // stays in bounds (a missing second k-tile gets a copy of the last one,
+  // whose weights the MFMA then takes as zero)
+  auto issue = [&](int s) {
+    uint8_t* dst = xs[s % Q8_NBUF] + wave * BPW * 1024;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int kt = min(2 * s + xh[i], KT - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xsrc[i] + (int64_t)kt * 64),
+                                       (lds_void*)(dst + i * 1024), 16, 0, 0);
+    }
+  };
+  auto issue_w = [&](u32x4 (&ww)[Q8_NTW][2], int s) {
+#pragma unroll
+    for (int j = 0; j < Q8_NTW; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        ww[j][h] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)min(2 * s + h, KT - 1) * 1024);
+  };
+  // one stage: for each of the wave's 8 row tiles, the fragment pair (two
+  // k-tiles) from LDS and four MFMAs; the LDS reads run one row tile ahead
+  // of the MFMAs that use them.  SINGLE: the stage holds one k-tile (odd K
+  // at the last stage); the weights' second half is zero there, so the
+  // second fragment (a finite copy of the last k-tile) adds nothing.
+  auto compute = [&](const u32x4 (&ww)[Q8_NTW][2], const uint8_t* buf, bool single) {
+    u32x4 w1[Q8_NTW];
+#pragma unroll
+    for (int j = 0; j < Q8_NTW; ++j) w1[j] = single ? u32x4{0, 0, 0, 0} : ww[j][1];
+    const uint8_t* p0 = buf + ((wm * Q8_MTW) * 2 * 64 + lane) * 16;
+    u32x4 xa[2], xb[2];
+    auto rd = [&](u32x4 (&x)[2], int mt) {
+      x[0] = *reinterpret_cast<const u32x4*>(p0 + mt * 2048);
+      x[1] = *reinterpret_cast<const u32x4*>(p0 + mt * 2048 + 1024);
+    };
+    rd(xa, 0);
+#pragma unroll
+    for (int mt = 0; mt < Q8_MTW; mt += 2) {
+      rd(xb, mt + 1);
+#pragma unroll
+      for (int j = 0; j < Q8_NTW; ++j) acc[mt][j] = mma_fp8(ww[j][0], w1[j], xa[0], xa[1], acc[mt][j]);
+      if (mt + 2 < Q8_MTW) rd(xa, mt + 2);
+#pragma unroll
+      for (int j = 0; j < Q8_NTW; ++j) acc[mt + 1][j] = mma_fp8(ww[j][0], w1[j], xb[0], xb[1], acc[mt + 1][j]);
+    }
+    // order: reads of tile 0, then (reads of tile mt+1, MFMAs of tile mt)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int mt = 0; mt + 1 < Q8_MTW; ++mt) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, Q8_NTW, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, Q8_NTW, 0);
+  };
+
+#pragma unroll
+  for (int j = 0; j < Q8_DIST; ++j) {
+    issue(j);
+    issue_w(w[j], j);
+  }
+  for (int s0 = 0; s0 < nst; s0 += Q8_DIST) {
+#pragma unroll
+    for (int j = 0; j < Q8_DIST; ++j) {
+      const int s = s0 + j;
+      // stage s has landed for this wave; after the barrier for every wave,
+      // and the buffer of stage s-1 (which stage s+DIST reuses) is free
+      wait_vmcnt<(Q8_DIST - 1) * LPS>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(s + Q8_DIST);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < nst && row_live) compute(w[j], xs[s % Q8_NBUF], 2 * s + 1 >= KT);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(w[j], s + Q8_DIST);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();   // no LDS copy may still be in flight when the workgroup exits
+
+  const int nq = (lane >> 4) * 4;
+  const float* sc = a.wscale ? a.wscale + (int64_t)group * a.s_gstride : nullptr;
+#pragma unroll
+  for (int mt = 0; mt < Q8_MTW; ++mt) {
+    const int r = (wm * Q8_MTW + mt) * 16 + (lane & 15);
+    if (r >= rows) continue;
+    const int row = row0 + r;
+    int src = a.row_map ? a.row_map[row] : row;
+    if (src < 0) src = 0;
+    const float xsr = a.xscale[src];
+#pragma unroll
+    for (int j = 0; j < Q8_NTW; j += 2) {
+      if (nt0 + j >= a.Nt) break;     // Nt is even: tiles come in valid pairs
+      float v0[4], v1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { v0[q] = acc[mt][j][q] * xsr; v1[q] = acc[mt][j + 1][q] * xsr; }
+      if constexpr (EPI == EPI_SWIGLU) {
+        epi_swiglu<DT_BF16>(a, sc, row, (nt0 + j) * 16 + nq, v0, v1);
+      } else {
+        epi_store<DT_BF16, EPI>(a, sc, row, (nt0 + j) * 16 + nq, v0, 0);
+        epi_store<DT_BF16, EPI>(a, sc, row, (nt0 + j + 1) * 16 + nq, v1, 0);
+      }
+    }
+  }
+}
+
+template <int EPI>
+static void run_x8(const GemmArgs& a, hipStream_t s) {
+  const int chunks = (a.Nt + 4 * Q8_NTW - 1) / (4 * Q8_NTW);
+  const int tiles = a.tiles ? a.max_tiles : (a.M + 255) / 256;
+  const int blocks = (int)round_up((int64_t)tiles * chunks, 8);
+  hipLaunchKernelGGL((k_gemm_x8<EPI>), dim3(blocks), dim3(64 * Q8_WAVES), 0, s, a);
+}
+
+int launch_gemm_x8(int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.ksplit > 1 || !a.xscale || a.K % 64) return -5;
+  switch (epi) {
+    case EPI_RESID: run_x8<EPI_RESID>(a, s); break;
+    case EPI_SWIGLU: run_x8<EPI_SWIGLU>(a, s); break;
+    case EPI_QKV: run_x8<EPI_QKV>(a, s); break;
+    case EPI_ROWS: run_x8<EPI_ROWS>(a, s); break;
+    default: return -5;
+  }
+  return 0;
+}
+
+// ---- per-row E4M3 quantisation of bf16 activations ------------------------------
+// q[r][k] = e4m3(x[r][k] * 448 / amax_r) (nearest even, clamped to +-448),
+// s[r] = amax_r / 448 (1 for an all-zero row), so x ~= s[r] * q[r][k].  One
+// wave per row, the row held in registers (K <= 4096, a multiple of 64);
+// rows at or past *n_dev (if given) are skipped.
+__global__ __launch_bounds__(256) void k_quant_fp8(const uint16_t* x, int64_t ldx, int n, int K, uint8_t* q,
+                                                   int64_t ldq, float* s, const int32_t* n_dev) {
+  constexpr int NV = 8;   // 8-element chunks per lane: K <= 64 * 8 * 8
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n_dev) n = min(n, *n_dev);
+  if (row >= n) return;
+  const int nc = K / 8;
+  const uint16_t* xr = x + (int64_t)row * ldx;
+  uint4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const uint4*>(xr + 8 * min(lane + 64 * i, nc - 1));
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i >= nc) break;
+    const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      amax = fmaxf(amax, fmaxf(fabsf(bf2f(w4[t] & 0xFFFF)), fabsf(bf2f(w4[t] >> 16))));
+  }
+  amax = wave_max(amax);
+  const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+  if (lane == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+  uint8_t* qr = q + (int64_t)row * ldq;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i >= nc) break;
+    const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t o[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float f0 = fminf(fmaxf(bf2f(w4[2 * t] & 0xFFFF) * inv, -448.f), 448.f);
+      const float f1 = fminf(fmaxf(bf2f(w4[2 * t] >> 16) * inv, -448.f), 448.f);
+      const float f2 = fminf(fmaxf(bf2f(w4[2 * t + 1] & 0xFFFF) * inv, -448.f), 448.f);
+      const float f3 = fminf(fmaxf(bf2f(w4[2 * t + 1] >> 16) * inv, -448.f), 448.f);
+      uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
+      o[t] = p;
+    }
+    *reinterpret_cast<uint2*>(qr + 8 * (lane + 64 * i)) = make_uint2(o[0], o[1]);
+  }
+}
+
+int launch_quant_fp8(const void* x, int64_t ldx, int n, int K, uint8_t* q, int64_t ldq, float* s,
+                     const int32_t* n_dev, hipStream_t st) {
+  if (K % 64 || K > 64 * 8 * 8 || n < 1) return -5;
+  hipLaunchKernelGGL(k_quant_fp8, dim3((n + 3) / 4), dim3(256), 0, st, reinterpret_cast<const uint16_t*>(x), ldx, n,
+                     K, q, ldq, s, n_dev);
+  return 0;
+}
+
+}  // namespace cd

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void k_sample_part(SampleArgs a) {
         while (z[j] != vm) ++j;
         if (m != -INFINITY) {
           const float dd = m - vm;
-          const float f = exp2f(dd * L2E);
+          const float f = __builtin_amdgcn_exp2f(dd * L2E);
           U = f * (U + dd * S);
           S = f * S;
         }
@@ -76,8 +76,10 @@ __global__ __launch_bounds__(256) void k_sample_part(SampleArgs a) {
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        // v_exp_f32 directly: an exponent below -126 may come out as 0
+        // instead of a subnormal, a change of at most 2^-126 relative to S
         const float dz = z[q] - m;
-        const float e = exp2f(dz * L2E);
+        const float e = __builtin_amdgcn_exp2f(dz * L2E);
         S += e;
         U += e * dz;
       }
@@ -135,34 +137,41 @@ __global__ __launch_bounds__(256) void k_sample_final(SampleArgs a) {
   int nlock = 0, stable = 1, xeq = 1, nonfin = 0;
   for (int i = threadIdx.x; i < a.C; i += 256) {
     const int64_t row = (int64_t)rr * a.C + i;
-    // the row's chunk partials in groups of 8, each group loaded before use
-    // (indices clamped: a repeated last chunk leaves the maximum unchanged and
-    // is skipped in the sums), chunks taken in ascending order
+    // the row's chunk partials, up to 32 loaded at once (indices clamped: a
+    // repeated last chunk is skipped), merged in ascending chunk order into
+    // fp64 sums; exp(m_c - M) <= 1 in fp32 (exactly 1 for the max chunk)
     const float4* pr = a.part + row * a.n_chunks;
     const int nc = a.n_chunks;
-    double M = -INFINITY;
-    for (int c0 = 0; c0 < nc; c0 += 8) {
-      float mx[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) mx[u] = pr[min(c0 + u, nc - 1)].x;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) M = fmax(M, (double)mx[u]);
-    }
+    constexpr int NB = 32;
+    float M = -INFINITY;
     double S = 0.0, U = 0.0;
     int idx = 0x7FFFFFFF;
-    for (int c0 = 0; c0 < nc; c0 += 8) {
-      float4 pv[8];
+    for (int c0 = 0; c0 < nc; c0 += NB) {
+      float4 pv[NB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = pr[min(c0 + u, nc - 1)];
+      for (int u = 0; u < NB; ++u) pv[u] = pr[min(c0 + u, nc - 1)];
+      float Mb = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < NB; ++u) Mb = fmaxf(Mb, pv[u].x);
+      if (Mb > M) {   // a later batch holds a larger maximum: rescale the sums so far
+        if (M != -INFINITY) {
+          const double d = (double)M - (double)Mb;
+          const double f = (double)__expf((float)d);
+          U = f * (U + d * S);
+          S = f * S;
+        }
+        M = Mb;
+        idx = 0x7FFFFFFF;   // the first maximum lies in this batch or later
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
         const float4 p = pv[u];
         if (c0 + u >= nc || p.x == -INFINITY) continue;
-        const double d = (double)p.x - M;
-        const double f = exp(d);
+        const double d = (double)p.x - (double)M;
+        const double f = p.x == M ? 1.0 : (double)__expf(p.x - M);
         S += f * (double)p.y;
         U += f * ((double)p.z + d * (double)p.y);
-        if ((double)p.x == M) idx = min(idx, __float_as_int(p.w));
+        if (p.x == M) idx = min(idx, __float_as_int(p.w));
       }
     }
     const double H = log(S) - U / S;

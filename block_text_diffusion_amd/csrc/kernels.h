@@ -74,6 +74,7 @@ struct GemmArgs {
   int pos0_stride;         // int32 stride between requests in pos0
   const float* rope_cs;    // [max_ctx][dh/2] (cos, sin) pairs, or null
   float q_scale;           // EPI_QKV: factor on the query outputs before their rounding
+  const float* xscale;     // fp8 activations (launch_gemm_x8): scale of each source row of X
 };
 
 // Both launchers return 0, or CD_ERR_UNSUPPORTED (-5) for an MXFP4 launch with
@@ -81,6 +82,15 @@ struct GemmArgs {
 int launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
 // 256-row work items, activations staged in LDS (a.ksplit > 1: EPI_F32 partials)
 int launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s);
+// fp8 weights x fp8 activations (E4M3 rows of X, one fp32 scale per row in
+// a.xscale) on the 16x16x128 fp8 MFMA, 256-row work items as launch_gemm_x;
+// every epilogue but EPI_F32, no split contraction.  0 or CD_ERR_UNSUPPORTED.
+int launch_gemm_x8(int epi, const GemmArgs& a, hipStream_t s);
+// q = E4M3 rows of bf16 x with one scale per row (amax / 448), for
+// launch_gemm_x8; rows at or past *n_dev (if not null) are skipped.  K a
+// multiple of 64, at most 4096.  0 or CD_ERR_UNSUPPORTED.
+int launch_quant_fp8(const void* x, int64_t ldx, int n, int K, uint8_t* q, int64_t ldq, float* s,
+                     const int32_t* n_dev, hipStream_t st);
 // ---- weight synthesis / packing --------------------------------------------
 struct PackDesc {
   uint8_t* dst;        // packed tiles (or row-major for embedding)

@@ -335,7 +335,7 @@ int32_t cd_set_trace(cd_ctx* ctx, float* d_h_layers, int32_t* d_topk_ids, float*
 enum { CD_PROF_EMBED = 0, CD_PROF_RMSNORM, CD_PROF_QKV, CD_PROF_ATTN, CD_PROF_ATTN_MERGE, CD_PROF_O_PROJ,
        CD_PROF_ROUTER, CD_PROF_ROUTE, CD_PROF_EXPERT_GU, CD_PROF_EXPERT_DOWN, CD_PROF_COMBINE,
        CD_PROF_SHARED_GU, CD_PROF_SHARED_DOWN, CD_PROF_LM_HEAD, CD_PROF_SAMPLER_PART, CD_PROF_SAMPLER_FINAL,
-       CD_PROF_OTHER, CD_PROF_CLASSES };
+       CD_PROF_OTHER, CD_PROF_QUANT, CD_PROF_CLASSES };
 int32_t cd_profile(cd_ctx* ctx, int32_t enable);
 int32_t cd_profile_read(cd_ctx* ctx, double* ms, int32_t* launches, int32_t n_classes);
 
