@@ -1,11 +1,12 @@
 // Fused vocabulary-wide sampler.
 //
 // Pass 1 (k_sample_part): the fp32 logits are read exactly once.  Each row
-// is cut into chunks of at most 8192 logits, one 256-thread workgroup per
-// (row, chunk), so a 256-row canvas launches 8192 workgroups; each thread
-// streams 16-byte loads, four in flight, and keeps an online (max m, S = sum e^(z-m),
-// U = sum e^(z-m)(z-m), index of the first max).  Partials merge across the
-// wave with shuffles and across waves through LDS.
+// is cut into chunks of (normally) at most 8192 logits, one 256-thread
+// workgroup per (row, chunk), so a 256-row canvas launches 8192 workgroups;
+// each thread loads its 32 logits of a chunk with eight 16-byte loads in
+// flight and keeps (max m, S = sum e^(z-m), U = sum e^(z-m)(z-m), index of
+// the first max).  Partials merge across the wave with shuffles and across
+// waves through LDS.
 // Pass 2 (k_sample_final): one workgroup per request, one thread per canvas
 // position, merges that row's chunk partials in fp64 and derives
 // entropy H = ln S - U/S (nats), max prob 1/S and the argmax; locks when max
@@ -38,42 +39,46 @@ __device__ __forceinline__ Acc merge(Acc a, Acc b) {
 }
 
 __global__ __launch_bounds__(256) void k_sample_part(SampleArgs a) {
+  __shared__ float shM[4];
   __shared__ Acc sh[4];
-  const int chunk = blockIdx.x, row = blockIdx.y;
+  const int chunk = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const int64_t base = (int64_t)row * a.V + (int64_t)chunk * a.chunk;
-  const float4* z4 = reinterpret_cast<const float4*>(a.logits + base);
-  const float L2E = 1.4426950408889634f;
-  float m = -INFINITY, S = 0.f, U = 0.f;
-  int idx = 0x7FFFFFFF;
-  const int n4 = a.chunk / 4;
-  // Four 16-byte loads per thread are issued before any is used (indices
-  // clamped, so none is conditional; non-temporal: the logits are read once),
-  // then taken in the order i, i+256, ... as a one-load loop would.
-  constexpr int UNR = 4;
   typedef float f32v4 __attribute__((ext_vector_type(4)));
-  const f32v4* zv = reinterpret_cast<const f32v4*>(z4);
-  for (int i0 = threadIdx.x; i0 < n4; i0 += 256 * UNR) {
-    f32v4 vv[UNR];
+  const f32v4* zv = reinterpret_cast<const f32v4*>(a.logits + base);
+  const float L2E = 1.4426950408889634f;
+  const int n4 = a.chunk / 4;
+  // A thread takes its float4s of the chunk in blocks of NL (an 8192-logit
+  // chunk is one block): all NL 16-byte non-temporal loads are issued first
+  // (indices clamped, so none is conditional; repeats are skipped), the
+  // block's maximum is taken, and the exponentials are summed against the
+  // running maximum, so no per-element branch rescales the sums (they are
+  // rescaled once per block when the maximum grows).  The first argmax is
+  // searched for only by the threads that hold the workgroup's maximum.
+  constexpr int NL = 8, BLK = NL * 256;
+  float m = -INFINITY, S = 0.f, U = 0.f;
+  int mb = 0;   // first block of this thread that reached its maximum
+  f32v4 v[NL];
+  for (int b0 = 0; b0 < n4; b0 += BLK) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) vv[u] = __builtin_nontemporal_load(zv + min(i0 + u * 256, n4 - 1));
+    for (int u = 0; u < NL; ++u) v[u] = __builtin_nontemporal_load(zv + min(b0 + tid + u * 256, n4 - 1));
+    float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int i = i0 + u * 256;
-      if (i >= n4) break;
-      float z[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-      float vm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      if (vm > m) {
-        int j = 0;
-        while (z[j] != vm) ++j;
-        if (m != -INFINITY) {
-          const float dd = m - vm;
-          const float f = __builtin_amdgcn_exp2f(dd * L2E);
-          U = f * (U + dd * S);
-          S = f * S;
-        }
-        m = vm;
-        idx = chunk * a.chunk + 4 * i + j;
+    for (int u = 0; u < NL; ++u)
+      if (b0 + tid + u * 256 < n4) mx = fmaxf(mx, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+    if (mx > m) {
+      if (m != -INFINITY) {   // only when a chunk spans several blocks
+        const float dd = m - mx;
+        const float f = __builtin_amdgcn_exp2f(dd * L2E);
+        U = f * (U + dd * S);
+        S = f * S;
       }
+      m = mx;
+      mb = b0;
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      if (b0 + tid + u * 256 >= n4) continue;
+      const float z[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // v_exp_f32 directly: an exponent below -126 may come out as 0
@@ -85,7 +90,32 @@ __global__ __launch_bounds__(256) void k_sample_part(SampleArgs a) {
       }
     }
   }
-  // a NaN logit never passes the comparisons above; make it visible
+  // the workgroup's maximum (a NaN logit never wins a comparison; it shows
+  // up as a NaN sum instead)
+  float wm = m;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o, 64));
+  if ((tid & 63) == 0) shM[tid >> 6] = wm;
+  __syncthreads();
+  wm = fmaxf(fmaxf(shM[0], shM[1]), fmaxf(shM[2], shM[3]));
+  int idx = 0x7FFFFFFF;
+  if (m == wm && m != -INFINITY) {
+    // first element equal to the maximum in this thread's first block that
+    // reached it (reloaded when a later block has replaced the registers)
+    if (mb + BLK < n4) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) v[u] = zv[min(mb + tid + u * 256, n4 - 1)];
+    }
+#pragma unroll
+    for (int u = NL - 1; u >= 0; --u) {
+      const int i = mb + tid + u * 256;
+      if (i >= n4) continue;
+      if (v[u].w == m) idx = chunk * a.chunk + 4 * i + 3;
+      if (v[u].z == m) idx = chunk * a.chunk + 4 * i + 2;
+      if (v[u].y == m) idx = chunk * a.chunk + 4 * i + 1;
+      if (v[u].x == m) idx = chunk * a.chunk + 4 * i;
+    }
+  }
   Acc acc = {m, S, U, idx};
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -96,9 +126,9 @@ __global__ __launch_bounds__(256) void k_sample_part(SampleArgs a) {
     b.idx = __shfl_xor(acc.idx, o, 64);
     acc = merge(acc, b);
   }
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
+  if ((tid & 63) == 0) sh[tid >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     Acc r = merge(merge(sh[0], sh[1]), merge(sh[2], sh[3]));
     a.part[(int64_t)row * a.n_chunks + chunk] = make_float4(r.m, r.S, r.U, __int_as_float(r.idx));
   }
