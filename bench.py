@@ -28,6 +28,7 @@ import synth_inputs
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def log(msg):
@@ -215,9 +216,9 @@ def expert_flops(w, part):
 
 
 def kernel_fractions(w, per, per_step):
-    """MFMA fractions of the compute-shaped kernels at this workload (bf16
-    dense peak; fp8 weights are widened to bf16 for the MFMA): canvas
-    attention and the LM head, from their event-timed durations."""
+    """MFMA fractions of the compute-shaped kernels at this workload against
+    the bf16 dense peak (both run on the bf16 MFMA in every weight format):
+    canvas attention and the LM head, from their event-timed durations."""
     R, C, L = w["R"], w["C"], w["L"]
     T = R * C
     nk = w["P0"] + C
@@ -466,22 +467,31 @@ def workload_line(name, w, g, steps, warmup, prof_steps):
     roof = {"kernel": f"grouped expert GEMM ({part.replace('_', '/')})", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(part) if name == "step_bf16" else None,
+            # the counters were taken at step_bf16; a gen_bf16 pass runs the same launch shapes
+            "traffic": measured_traffic(part) if name in ("step_bf16", "gen_bf16") else None,
             "bytes_per_launch": int(byts), "avg_launch_ms": round(per[dom], 5), "active_experts": g["active"],
             # the same bytes against the read+write rate of a plain 1 GiB copy on this GPU
             "measured_copy_gbs": round(g["copy_gbs"], 1), "frac_of_measured_copy": round(achieved / g["copy_gbs"], 4)}
+    w8a8 = False
     if R * C * w["k"] / w["E"] >= 256:
-        # many rows per expert: the grouped GEMM runs on the bf16 MFMA pipe
+        # many rows per expert: the grouped GEMM is bound by its MFMA pipe; with
+        # fp8 weights it runs W8A8 on the fp8 MFMA (activations quantised per
+        # row), else on the bf16 MFMA
+        w8a8 = w["wdtype"] == "fp8"
+        peak = FP8_PEAK_TFLOPS if w8a8 else BF16_PEAK_TFLOPS
         tf = expert_flops(w, part) / (per[dom] * 1e-3) / 1e12
-        roof = {"kernel": roof["kernel"], "bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+        roof = {"kernel": roof["kernel"] + (", fp8 x fp8" if w8a8 else ""), "bound": "mfma", "achieved": round(tf, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
                 "flops_per_launch": int(expert_flops(w, part)), "avg_launch_ms": round(per[dom], 5),
                 "hbm_gbs": round(achieved, 1)}
     return {
         "value": round(committed, 3) if gen else round(1e3 / ms, 3),
         "unit": "committed tok/s" if gen else "steps/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if w["wdtype"] == "f32" else "bf16", "data": "synthetic",
+        "vs_baseline": None,
+        # arithmetic type: fp8 x fp8 MFMA for the QKV and routed-expert GEMMs of the
+        # W8A8 batch, bf16 for everything else
+        "dtype": "f32" if w["wdtype"] == "f32" else ("fp8+bf16" if w8a8 else "bf16"), "data": "synthetic",
         "config": {"workload": wl, "weights": w["wdtype"], "requests": R, "canvas": C, "prefix": w["P0"],
                    "blocks": w.get("blocks", 1)},
         "steps_per_s": round(1e3 / ms, 3),
