@@ -17,6 +17,7 @@ import numpy as np
 
 from oracle import model
 from oracle import sampler as osamp
+from oracle.rounding import round_bf16, round_e4m3
 from oracle.weights import Weights
 from tests.gpu_util import rel_l2_rows
 
@@ -145,3 +146,95 @@ class Summary:
         print(f"[parity] {line}", flush=True)
         assert self.adopted <= max(2, max_adopt_frac * self.decisions), line
         return line
+
+
+# ---- the W8A8 path of the batched fp8 model, modelled in the test -----------------
+# The oracle does not emulate GPU roundings (reading R18), so with activations
+# quantised to E4M3 its keys and outputs differ from the GPU's by the
+# quantisation itself (about 3e-2).  The functions below model the GPU's
+# arithmetic step by step on the same inputs -- bf16 activation rows, the
+# per-row E4M3 quantiser, bf16 intermediate and output rows -- with the
+# oracle's stored weights and its rounding functions, so that the W8A8 kernels
+# are checked against what they are meant to compute to about the bf16 output
+# rounding.
+
+def e4m3_rows(x):
+    """Model of the activation quantiser: each row in bf16, scaled by
+    448 / max|row| in fp32, clamped to +-448 and rounded to E4M3 (nearest
+    even); returned as the codes times the row scale max|row| / 448 (fp32)."""
+    xb = round_bf16(np.asarray(x, np.float64)).astype(np.float32)
+    amax = np.abs(xb).max(axis=1)
+    live = amax > 0
+    safe = np.where(live, amax, np.float32(1))
+    inv = np.where(live, np.float32(448) / safe, np.float32(1)).astype(np.float32)
+    f = np.clip(xb * inv[:, None], np.float32(-448), np.float32(448)).astype(np.float32)
+    codes = round_e4m3(f.astype(np.float64))
+    scale = np.where(live, safe / np.float32(448), np.float32(1)).astype(np.float32)
+    return codes * scale[:, None].astype(np.float64)
+
+
+def check_layer_w8a8(w, l, items, tol_kv, tol_h, experts, qkv8=True):
+    """Layer l along the GPU's arithmetic for the rows of items (as in
+    check_layer): queries, keys and values from E4M3-quantised bf16 rows
+    (qkv8; else from the bf16 rows);
+    attention over the GPU's cache, its output rounded to bf16 before the
+    output projection; the MoE input rounded to bf16; when experts is set the
+    routed experts' gate/up input quantised per token row and their down input
+    (the bf16 SwiGLU rows) per row, else both in bf16; bf16 expert output
+    rows; the shared FFN in bf16.  Routing follows the GPU's choice; the
+    gates are the softmax of the modelled router logits over it.  Asserts the
+    keys/values within tol_kv and (tol_h not None) the layer output within
+    tol_h; returns the largest errors."""
+    W = Weights(w, cache=False)
+    Hq, Hkv, dh, eps = w["Hq"], w["Hkv"], w["dh"], w["eps"]
+    wq, wk, wv = (W.get(n, l) for n in ("wq", "wk", "wv"))
+    out = {"err_k8": 0.0, "err_v8": 0.0}
+    mids = []
+    for it in items:
+        n = it["h_in"].shape[0]
+        u = model.rmsnorm(it["h_in"], eps)
+        uq = e4m3_rows(u) if qkv8 else round_bf16(u)
+        q = model.rope((uq @ wq.T).reshape(n, Hq, dh), it["pos"], w["theta"])
+        k = model.rope((uq @ wk.T).reshape(n, Hkv, dh), it["pos"], w["theta"])
+        v = (uq @ wv.T).reshape(n, Hkv, dh)
+        ek = rel_l2_rows(it["k_got"].reshape(n, -1), k.reshape(n, -1)).max()
+        ev = rel_l2_rows(it["v_got"].reshape(n, -1), v.reshape(n, -1)).max()
+        assert ek <= tol_kv and ev <= tol_kv, (l, it.get("name"), "w8a8 k/v", ek, ev)
+        out["err_k8"] = max(out["err_k8"], float(ek))
+        out["err_v8"] = max(out["err_v8"], float(ev))
+        if tol_h is not None:
+            m = it["K"].shape[1]
+            allowed = (np.arange(m)[None, :] <= np.asarray(it["pos"])[:, None]) if it["causal"] else None
+            o = model.attention(q, np.asarray(it["K"], np.float64), np.asarray(it["V"], np.float64), allowed)
+            mids.append(it["h_in"] + round_bf16(o.reshape(n, Hq * dh)) @ W.get("wo", l).T)
+    if tol_h is None:
+        return out
+    h_mid = np.concatenate(mids)
+    ids = np.concatenate([it["ids"] for it in items]).astype(np.int64)
+    u2 = round_bf16(model.rmsnorm(h_mid, eps))
+    r = u2 @ W.get("wr", l).T
+    sel = np.take_along_axis(r, ids, axis=1)
+    gates = np.exp(sel - sel.max(axis=1, keepdims=True))
+    gates /= gates.sum(axis=1, keepdims=True)
+    xin = e4m3_rows(u2) if experts else u2
+    f = np.zeros_like(u2)
+    for e in np.unique(ids):
+        rows, slot = np.nonzero(ids == e)
+        g = xin[rows] @ W.get("wg", l, e).T
+        up = xin[rows] @ W.get("wu", l, e).T
+        hid = round_bf16(model.silu(g) * up)
+        y = round_bf16((e4m3_rows(hid) if experts else hid) @ W.get("wd", l, e).T)
+        f[rows] += gates[rows, slot][:, None] * y
+    if w["fs"] > 0:
+        hs = round_bf16(model.silu(u2 @ W.get("sg", l).T) * (u2 @ W.get("su", l).T))
+        f += hs @ W.get("sd", l).T
+    h_out = h_mid + f
+    i0 = 0
+    out["err_h8"] = 0.0
+    for it in items:
+        n = it["h_in"].shape[0]
+        eh = rel_l2_rows(it["h_out"], h_out[i0:i0 + n]).max()
+        assert eh <= tol_h, (l, it.get("name"), "w8a8 h", eh)
+        out["err_h8"] = max(out["err_h8"], float(eh))
+        i0 += n
+    return out

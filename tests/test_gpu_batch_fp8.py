@@ -15,7 +15,13 @@ bench.py times.  The oracle checks what it can compute row by row:
 The same batch with MXFP4 experts (``batch_mxfp4``: 512 rows per expert, so
 the expert GEMMs run the LDS-staged kernel's MXFP4 path at K = 2816 and 704)
 is checked the same way.  Tolerance: fp8 and MXFP4 6e-2 (per-row relative
-L2).  The largest errors are printed as one "[parity]" line."""
+L2).  At this batch the QKV projection (and, with fp8 experts, the routed
+experts) quantise their activation rows to E4M3 (reading R18), which the
+oracle does not emulate; the same rows are therefore also taken along the
+GPU's arithmetic (bf16 activation rows, the per-row E4M3 quantiser, bf16
+intermediate rows, tests/oracle_rows.check_layer_w8a8): keys and values at
+every layer within 6e-3, the layer output at the first and last layer within
+2e-2.  The largest errors are printed as one "[parity]" line."""
 import numpy as np
 import pytest
 import torch
@@ -26,8 +32,8 @@ from block_text_diffusion_amd.engine import Engine
 from oracle import model, philox
 from oracle.weights import Weights
 from tests.gpu_util import TOL, announce, rel_l2_rows, to_np
-from tests.oracle_rows import Summary, check_layer
-from tests.test_gpu_full_width import ADOPT_CAP, CANVAS_ROWS, check_sampler
+from tests.oracle_rows import Summary, check_layer, check_layer_w8a8
+from tests.test_gpu_full_width import ADOPT_CAP, CANVAS_ROWS, W8A8_TOL_H, W8A8_TOL_KV, check_sampler
 
 pytestmark = pytest.mark.gpu
 
@@ -93,7 +99,14 @@ def test_batch_full_width_every_layer(name):
                               k_got=K[:, pos].transpose(1, 0, 2), v_got=Vv[:, pos].transpose(1, 0, 2)))
         res = check_layer(w, l, items, tol)
         S.add_layer(res)
-        print(f"layer {l}: {[{k2: float(f'{v:.2e}') for k2, v in r_.items()} for r_ in res]}", flush=True)
+        # the QKV GEMM (fp8 attention weights) and, with fp8 experts, the routed
+        # experts run W8A8 at 8192 rows: the same rows along the GPU's arithmetic
+        m8 = check_layer_w8a8(w, l, items, W8A8_TOL_KV, W8A8_TOL_H if l in (0, L - 1) else None,
+                              experts=w["wdtype"] == "fp8")
+        for key, val in m8.items():
+            S.add(key, val)
+        print(f"layer {l}: {[{k2: float(f'{v:.2e}') for k2, v in r_.items()} for r_ in res]} "
+              f"w8a8 model: {({k2: float(f'{v:.2e}') for k2, v in m8.items()})}", flush=True)
 
     # LM head (bf16) on sampled vocabulary rows of the last request
     vrows = np.sort(np.random.default_rng(1).choice(V, size=256, replace=False))

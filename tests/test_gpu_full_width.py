@@ -19,7 +19,12 @@ test, so it checks what it can compute row by row, at every layer:
 * the sampler on the GPU's own logits (all 256 x 262144).
 The same step with MXFP4 experts and fp8 attention (``step_mxfp4``) is
 checked the same way.  Tolerance: bf16 2e-2, MXFP4 6e-2 (per-row relative
-L2).  The largest errors are printed as one "[parity]" line."""
+L2).  Its 4096-row prefill runs the QKV projection W8A8 (activation rows
+quantised to E4M3, reading R18), which the oracle does not emulate, so the
+prompt rows are also taken along the GPU's arithmetic (check_layer_w8a8):
+keys and values within 6e-3 at every layer, the layer output within 2e-2 at
+the first and last layer.  The largest errors are printed as one "[parity]"
+line."""
 import numpy as np
 import pytest
 import torch
@@ -30,13 +35,16 @@ from block_text_diffusion_amd.engine import Engine
 from oracle import model, philox
 from oracle.weights import Weights
 from tests.gpu_util import TOL, announce, rel_l2_rows, to_np
-from tests.oracle_rows import Summary, check_layer, sample_threaded
+from tests.oracle_rows import Summary, check_layer, check_layer_w8a8, sample_threaded
 
 pytestmark = pytest.mark.gpu
 
 # largest share of checked routing decisions the GPU may take from the
 # near-tie band (its top-k set differs from the oracle's own)
 ADOPT_CAP = {"f32": 0.01, "bf16": 0.04, "fp8": 0.04, "mxfp4": 0.04}
+# the GPU arithmetic modelled in the test (check_layer_w8a8): what is left is
+# the bf16 rounding of the outputs and fp32 accumulation
+W8A8_TOL_KV, W8A8_TOL_H = 6e-3, 2e-2
 CANVAS_ROWS = np.array([2, 29, 35, 60, 66, 93, 101, 126, 130, 157, 163, 190, 197, 222, 229, 254])
 PREFILL_POS = np.array([0, 1, 777, 2047, 2048, 3001, 4094, 4095])
 
@@ -112,7 +120,16 @@ def test_step_full_width_every_layer(name):
         res = check_layer(w, l, items, tol)
         S.add_layer(res[:1], "canvas_")
         S.add_layer(res[1:], "prefill_")
-        print(f"layer {l}: {[{k2: float(f'{v:.2e}') for k2, v in r.items()} for r in res]}", flush=True)
+        m8 = {}
+        if w["wdtype"] in ("fp8", "mxfp4"):
+            # the 4096-row prefill runs the QKV GEMM of the fp8 attention weights
+            # W8A8: its rows along the GPU's arithmetic
+            m8 = check_layer_w8a8(w, l, items[1:], W8A8_TOL_KV, W8A8_TOL_H if l in (0, L - 1) else None,
+                                  experts=w["wdtype"] == "fp8")
+            for key, val in m8.items():
+                S.add("prefill_" + key, val)
+        print(f"layer {l}: {[{k2: float(f'{v:.2e}') for k2, v in r.items()} for r in res]} "
+              f"w8a8 model: {({k2: float(f'{v:.2e}') for k2, v in m8.items()})}", flush=True)
 
     # LM head on sampled vocabulary rows
     vrows = np.sort(np.random.default_rng(0).choice(V, size=512, replace=False))

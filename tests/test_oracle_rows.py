@@ -70,3 +70,23 @@ def test_sample_threaded_equals_plain_sampler():
     for k in ("H", "a", "pmax", "margin", "lock", "x_next"):
         assert np.array_equal(a[k], b[k]), k
     assert abs(a["Hbar"] - b["Hbar"]) <= 1e-12 * a["Hbar"]
+
+
+def test_activation_quantiser_model_rows():
+    # the test-side model of the E4M3 activation quantiser: every value is an
+    # E4M3 code times the row scale max|bf16 row| / 448 (fp32), the largest
+    # magnitude maps to the code 448, and a zero row stays zero
+    from oracle.rounding import round_bf16, round_e4m3
+    from tests.oracle_rows import e4m3_rows
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 2816)) * np.array([1e-3, 1.0, 10.0, 1e4, 0.5])[:, None]
+    x[4] = 0.0
+    q = e4m3_rows(x)
+    amax = np.abs(round_bf16(x)).max(axis=1)
+    for i in range(4):
+        s = np.float64(np.float32(amax[i]) / np.float32(448))
+        codes = q[i] / s
+        assert np.array_equal(round_e4m3(codes), codes)
+        assert np.abs(codes).max() == 448.0
+        assert 0.01 < np.linalg.norm(q[i] - x[i]) / np.linalg.norm(x[i]) < 0.05
+    assert not q[4].any()
