@@ -93,6 +93,7 @@ def lib():
             "cd_serve": [c_void_p, c_int32, c_void_p, P(ctypes.c_int64), P(c_int32), P(c_int32),
                          P(c_uint64), c_int32, c_void_p, P(ctypes.c_int64), P(c_int32), c_void_p],
             "cd_profile": [c_void_p, c_int32],
+            "cd_set_graphs": [c_void_p, c_int32],
             "cd_profile_read": [c_void_p, c_void_p, c_void_p, c_int32],
         }
         for name, args in sig.items():
@@ -110,7 +111,7 @@ def exported_names():
             "cd_synth_weights", "cd_set_weight", "cd_get_weight", "cd_prefill", "cd_init_canvas",
             "cd_denoise_step", "cd_read_step_info", "cd_commit_block", "cd_generate",
             "cd_sample_workspace_bytes", "cd_sample_step", "cd_sample_step_noalloc", "cd_get_buffer", "cd_get_config", "cd_get_length",
-            "cd_set_trace", "cd_abort_canvas", "cd_release", "cd_move_request", "cd_serve", "cd_profile", "cd_profile_read",
+            "cd_set_trace", "cd_abort_canvas", "cd_release", "cd_move_request", "cd_serve", "cd_profile", "cd_set_graphs", "cd_profile_read",
             "cd_last_error"]
 
 
@@ -323,6 +324,10 @@ def cd_abort_canvas(ctx, req):
 
 def cd_profile(ctx, enable):
     _check(lib().cd_profile(ctx, 1 if enable else 0))
+
+
+def cd_set_graphs(ctx, enable):
+    _check(lib().cd_set_graphs(ctx, 1 if enable else 0))
 
 
 def cd_profile_read(ctx):

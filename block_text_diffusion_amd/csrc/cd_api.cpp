@@ -260,16 +260,33 @@ struct cd_ctx {
   float* trace_h = nullptr;
   int32_t* trace_ids = nullptr;
   float* trace_gates = nullptr;
-  // a second stream (default priority) of the library's own: the shared FFN's
-  // gate/up projection runs there while the router, routing and expert GEMMs
-  // run on the caller's stream; the two join before the shared down
-  // projection, inside the same call.  Created on first use; if that fails
-  // the projection runs on the caller's stream.
+  // a second stream (default priority) of the library's own: above 256 rows
+  // the shared FFN runs there while the router, routing and expert GEMMs run
+  // on the caller's stream; the two join before the combine, inside the same
+  // call.  Created on first use; if that fails the shared FFN runs on the
+  // caller's stream.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool side_tried = false;
   // first refusal of a kernel launcher during the current call (0 = none)
   int32_t launch_err = 0;
+  // Denoise passes replayed as HIP graphs.  A pass's launches depend on the
+  // host only through (first slot, number of slots, longest context, active
+  // slots): every other argument is a fixed address in the two buffers or a
+  // constant of the plan, and the per-request state is read on the device.
+  // One captured graph therefore serves every pass with the same four values
+  // (all the passes of a block).  Captured on a stream of the library's own,
+  // launched on the caller's.
+  struct PassGraph {
+    int r0, n_req, nkeys;
+    uint64_t act[4];
+    hipGraphExec_t exec;
+    uint64_t used;
+  };
+  bool graphs = true;
+  hipStream_t cap = nullptr;
+  std::vector<PassGraph> pass_graphs;
+  uint64_t graph_clock = 0;
   template <class T> T* st(int64_t off) const { return reinterpret_cast<T*>(S + off); }
   template <class T> T* wt(int64_t off) const { return off < 0 ? nullptr : reinterpret_cast<T*>(W + off); }
 };
@@ -497,11 +514,14 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
     { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
-    // The shared FFN depends only on u: both its projections run on the side
-    // stream (its fp32 output rows go to a buffer of their own) while the
-    // router, the routing and the expert GEMMs run here; the combine then adds
-    // the routed experts and the shared FFN into the residual.
-    const bool fork = g.shared_hidden && ensure_side(c);
+    // The shared FFN depends only on u.  Above 256 rows both its projections
+    // run on the side stream (its fp32 output rows go to a buffer of their
+    // own) while the router, the routing and the expert GEMMs run here, which
+    // are then bound by their MFMAs; at 256 rows and below everything here is
+    // bound by HBM and the shared FFN's weight stream only slows the expert
+    // GEMMs it would overlap, so it runs in line.  Either way the combine then
+    // adds the routed experts and the shared FFN into the residual.
+    const bool fork = g.shared_hidden && T > 256 && ensure_side(c);
     if (g.shared_hidden) {
       hipStream_t ss = fork ? c->side : s;
       if (fork) {
@@ -621,6 +641,81 @@ int32_t finish(cd_ctx* c, const char* where) {
 // ride along: their rows go through the forward (whatever ids their canvas
 // holds, keys/values written past their committed length), but the sampler
 // leaves their state untouched.
+void release_graphs(cd_ctx* c) {
+  if (c->pass_graphs.empty()) return;
+  hipDeviceSynchronize();   // a graph may still run on some stream
+  for (auto& pg : c->pass_graphs) hipGraphExecDestroy(pg.exec);
+  c->pass_graphs.clear();
+}
+
+constexpr size_t MAX_PASS_GRAPHS = 16;
+
+// The pass as a graph: 0 when it was launched on s, 1 when it was not captured
+// (graphs then stay off for this context and the caller runs the pass
+// directly), or an error status.
+int32_t step_graph(cd_ctx* c, int r0, int n_req, hipStream_t s) {
+  const cd_config& g = c->p.c;
+  int nkeys = 0;
+  uint64_t act[4] = {0, 0, 0, 0};
+  for (int r = r0; r < r0 + n_req; ++r) {
+    nkeys = std::max(nkeys, c->req[r].P + g.canvas_len);
+    if (c->req[r].active) act[r >> 6] |= 1ull << (r & 63);
+  }
+  cd_ctx::PassGraph* hit = nullptr;
+  for (auto& pg : c->pass_graphs)
+    if (pg.r0 == r0 && pg.n_req == n_req && pg.nkeys == nkeys && !memcmp(pg.act, act, sizeof act)) hit = &pg;
+  if (!hit) {
+    ensure_side(c);   // the shared FFN's stream and events exist before the capture
+    if (!c->cap && hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking) != hipSuccess) {
+      c->cap = nullptr;
+      c->graphs = false;
+      (void)hipGetLastError();
+      return 1;
+    }
+    if (hipStreamBeginCapture(c->cap, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+      c->graphs = false;
+      (void)hipGetLastError();
+      return 1;
+    }
+    forward(c, r0, n_req, g.canvas_len, c->st<int32_t>(c->p.canvas) + (int64_t)r0 * g.canvas_len, false, true,
+            true, c->cap);
+    sample(c, r0, n_req, c->cap);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(c->cap, &graph);
+    if (c->launch_err) {
+      if (graph) hipGraphDestroy(graph);
+      return finish(c, "denoise step");
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = (ec == hipSuccess && graph) ? hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) : ec;
+    if (graph) hipGraphDestroy(graph);
+    if (ei != hipSuccess || !exec) {
+      c->graphs = false;
+      (void)hipGetLastError();
+      return 1;
+    }
+    if (c->pass_graphs.size() >= MAX_PASS_GRAPHS) {
+      // drop the least recently used graph
+      size_t lru = 0;
+      for (size_t i = 1; i < c->pass_graphs.size(); ++i)
+        if (c->pass_graphs[i].used < c->pass_graphs[lru].used) lru = i;
+      hipDeviceSynchronize();
+      hipGraphExecDestroy(c->pass_graphs[lru].exec);
+      c->pass_graphs.erase(c->pass_graphs.begin() + lru);
+    }
+    cd_ctx::PassGraph pg;
+    pg.r0 = r0; pg.n_req = n_req; pg.nkeys = nkeys;
+    memcpy(pg.act, act, sizeof act);
+    pg.exec = exec;
+    pg.used = 0;
+    c->pass_graphs.push_back(pg);
+    hit = &c->pass_graphs.back();
+  }
+  hit->used = ++c->graph_clock;
+  if (hipGraphLaunch(hit->exec, s) != hipSuccess) return hip_status("graph launch");
+  return 0;
+}
+
 int32_t step_internal(cd_ctx* c, int r0, int n_req, hipStream_t s) {
   const cd_config& g = c->p.c;
   int n_active = 0;
@@ -635,9 +730,15 @@ int32_t step_internal(cd_ctx* c, int r0, int n_req, hipStream_t s) {
     ++n_active;
   }
   if (!n_active) return fail(CD_ERR_BAD_STATE, "no request in 0..%d has an active canvas", r0 + n_req - 1);
-  forward(c, r0, n_req, g.canvas_len, c->st<int32_t>(c->p.canvas) + (int64_t)r0 * g.canvas_len, false, true,
-          true, s);
-  sample(c, r0, n_req, s);
+  // per-launch profiling events and trace copies are taken eagerly
+  int32_t st = 1;
+  if (c->graphs && !c->prof && !c->trace_h && !c->trace_ids && !c->trace_gates) st = step_graph(c, r0, n_req, s);
+  if (st > 1 || st < 0) return st;
+  if (st == 1) {
+    forward(c, r0, n_req, g.canvas_len, c->st<int32_t>(c->p.canvas) + (int64_t)r0 * g.canvas_len, false, true,
+            true, s);
+    sample(c, r0, n_req, s);
+  }
   for (int r = r0; r < r0 + n_req; ++r)
     if (c->req[r].active) c->req[r].t++;
   return finish(c, "denoise step");
@@ -743,6 +844,8 @@ int32_t cd_ctx_create(const cd_config* cfg, void* d_weights, void* d_state, cd_c
 
 int32_t cd_ctx_destroy(cd_ctx* ctx) {
   if (ctx) {
+    release_graphs(ctx);
+    if (ctx->cap) hipStreamDestroy(ctx->cap);
     if (ctx->side) {
       hipStreamSynchronize(ctx->side);
       hipStreamDestroy(ctx->side);
@@ -932,6 +1035,13 @@ int32_t cd_abort_canvas(cd_ctx* c, int32_t req) {
   if (!q.active) return fail(CD_ERR_BAD_STATE, "request %d has no active canvas", req);
   q.active = false;
   q.t = 0;
+  return CD_OK;
+}
+
+int32_t cd_set_graphs(cd_ctx* c, int32_t enable) {
+  if (int32_t st = check_ctx(c)) return st;
+  if (!enable) release_graphs(c);
+  c->graphs = enable != 0;
   return CD_OK;
 }
 

@@ -327,6 +327,20 @@ int32_t cd_get_length(cd_ctx* ctx, int32_t req, int32_t* P);
  * off; cd_set_trace(ctx, NULL, NULL, NULL) switches tracing off. */
 int32_t cd_set_trace(cd_ctx* ctx, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates);
 
+/* Graph replay of denoise passes (on by default).  The launches of one pass
+ * depend on the host only through the first slot, the number of slots, the
+ * longest context among them and which of them hold a canvas; the first pass
+ * with a new combination of these is captured into a HIP graph on a stream of
+ * the library's own and every later one replays it with one launch on the
+ * caller's stream (at most 16 graphs are kept per context, least recently
+ * used dropped first).  The results are the same as those of the launches
+ * made one by one.  Passes run while profiling (cd_profile) or tracing
+ * (cd_set_trace) is on, and passes of a context where a capture failed, are
+ * launched one by one.  enable = 0 releases the context's graphs (waiting
+ * for the device) and launches every later pass one by one.  Not thread-safe
+ * per context, like every other call. */
+int32_t cd_set_graphs(cd_ctx* ctx, int32_t enable);
+
 /* Per-kernel timing with HIP events recorded on the call's stream around
  * every launch (enable = 1 starts a fresh window, 0 stops recording).
  * cd_profile_read waits for the recorded events and returns, per kernel
