@@ -284,6 +284,7 @@ struct cd_ctx {
     uint64_t used;
   };
   bool graphs = true;
+  bool capturing = false;   // a pass is being captured on cap
   hipStream_t cap = nullptr;
   std::vector<PassGraph> pass_graphs;
   uint64_t graph_clock = 0;
@@ -514,14 +515,18 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
     { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
-    // The shared FFN depends only on u.  Above 256 rows both its projections
-    // run on the side stream (its fp32 output rows go to a buffer of their
-    // own) while the router, the routing and the expert GEMMs run here, which
-    // are then bound by their MFMAs; at 256 rows and below everything here is
-    // bound by HBM and the shared FFN's weight stream only slows the expert
-    // GEMMs it would overlap, so it runs in line.  Either way the combine then
-    // adds the routed experts and the shared FFN into the residual.
-    const bool fork = g.shared_hidden && T > 256 && ensure_side(c);
+    // The shared FFN depends only on u, so its two projections can run on the
+    // side stream (its fp32 output rows go to a buffer of their own) while
+    // the router and the routing run here; the combine then adds the routed
+    // experts and the shared FFN into the residual.  Above 256 rows the branch
+    // joins before the combine: the expert GEMMs it then also overlaps are
+    // bound by their MFMAs.  At 256 rows and below those GEMMs are bound by
+    // HBM and would only be slowed by the shared FFN's weight stream, so the
+    // branch joins before them, covering just the latency-bound routing; that
+    // pays only inside a captured graph (an edge instead of the runtime's
+    // event wait), so a pass launched one by one runs the shared FFN in line.
+    const bool fork = g.shared_hidden && (T > 256 || c->capturing) && ensure_side(c);
+    const bool early_join = fork && T <= 256;
     if (g.shared_hidden) {
       hipStream_t ss = fork ? c->side : s;
       if (fork) {
@@ -561,6 +566,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       ra.trace_gates = c->trace_gates + (int64_t)l * T * k;
     }
     { PROF(CD_PROF_ROUTE); launch_route(ra, s); }
+    if (early_join) hipStreamWaitEvent(s, c->ev_join, 0);
     {
       GemmArgs a = gemm_base(u, d, c->W + lw.gu, c->wt<float>(lw.gu_s), d, p.gu_npad, 2 * g.expert_hidden,
                              c->st<void>(p.aperm), g.expert_hidden);
@@ -579,7 +585,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
     // h += sum_j gate_j * y_j (choice order) + shared FFN row; the same kernel
     // writes u = RMSNorm(h) for the next layer or the LM head (every reader
     // of this layer's u ran before it on this stream or joined above)
-    if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
+    if (fork && !early_join) hipStreamWaitEvent(s, c->ev_join, 0);
     {
       u_ready = l + 1 < g.n_layers || head;
       PROF(CD_PROF_COMBINE);
@@ -677,9 +683,11 @@ int32_t step_graph(cd_ctx* c, int r0, int n_req, hipStream_t s) {
       (void)hipGetLastError();
       return 1;
     }
+    c->capturing = true;
     forward(c, r0, n_req, g.canvas_len, c->st<int32_t>(c->p.canvas) + (int64_t)r0 * g.canvas_len, false, true,
             true, c->cap);
     sample(c, r0, n_req, c->cap);
+    c->capturing = false;
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(c->cap, &graph);
     if (c->launch_err) {
