@@ -342,6 +342,13 @@ def cpu_baseline(w, active_experts):
     t_samp = time.perf_counter() - t0
 
     step_s = w["L"] * (t_attn + active_experts * t_expert + t_shared) + (w["V"] / n_slice) * t_lm + t_samp
+    # the other configurations from the same units: a block of the four-block
+    # generation at the 48-pass cap (48 passes plus the commit's forward, a
+    # pass without the LM head and sampler), and one 32-request pass counted
+    # for requests 0 and 31 only
+    forward_s = w["L"] * (t_attn + active_experts * t_expert + t_shared)
+    out["gen_block_s_from_units"] = round(48 * step_s + forward_s, 1)
+    out["batch_pass_2_of_32_s_from_units"] = round(2 * step_s, 1)
     out.update({
         "value": round(1.0 / step_s, 6), "unit": "steps/s", "kind": "oracle",
         "sample": (f"fp64 numpy oracle on {cores} host cores ({out['cpu_model']}), weights generated before the "
