@@ -483,11 +483,13 @@ def workload_line(name, w, g, steps, warmup, prof_steps):
     if R * C * w["k"] / w["E"] >= 256:
         # many rows per expert: the grouped GEMM is bound by its MFMA pipe; with
         # fp8 weights it runs W8A8 on the fp8 MFMA (activations quantised per
-        # row), else on the bf16 MFMA
-        w8a8 = w["wdtype"] == "fp8"
+        # row), with MXFP4 weights fp4 x fp8 on the block-scaled MFMA (whose
+        # rate with one fp8 operand is the fp8 rate), else on the bf16 MFMA
+        w8a8 = w["wdtype"] in ("fp8", "mxfp4")
         peak = FP8_PEAK_TFLOPS if w8a8 else BF16_PEAK_TFLOPS
         tf = expert_flops(w, part) / (per[dom] * 1e-3) / 1e12
-        roof = {"kernel": roof["kernel"] + (", fp8 x fp8" if w8a8 else ""), "bound": "mfma", "achieved": round(tf, 2),
+        kind = {"fp8": ", fp8 x fp8", "mxfp4": ", fp4 x fp8 (block-scaled)"}.get(w["wdtype"], "")
+        roof = {"kernel": roof["kernel"] + kind, "bound": "mfma", "achieved": round(tf, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
                 "flops_per_launch": int(expert_flops(w, part)), "avg_launch_ms": round(per[dom], 5),
                 "hbm_gbs": round(achieved, 1)}
@@ -496,9 +498,11 @@ def workload_line(name, w, g, steps, warmup, prof_steps):
         "unit": "committed tok/s" if gen else "steps/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        # arithmetic type: fp8 x fp8 MFMA for the QKV and routed-expert GEMMs of the
-        # W8A8 batch, bf16 for everything else
-        "dtype": "f32" if w["wdtype"] == "f32" else ("fp8+bf16" if w8a8 else "bf16"), "data": "synthetic",
+        # arithmetic type: fp8 x fp8 MFMA for the QKV GEMM and the routed experts of
+        # the W8A8 batch (fp4 x fp8 with MXFP4 experts), bf16 for everything else
+        "dtype": "f32" if w["wdtype"] == "f32" else (
+            ("fp8+fp4+bf16" if w["wdtype"] == "mxfp4" else "fp8+bf16") if w8a8 else "bf16"),
+        "data": "synthetic",
         "config": {"workload": wl, "weights": w["wdtype"], "requests": R, "canvas": C, "prefix": w["P0"],
                    "blocks": w.get("blocks", 1)},
         "steps_per_s": round(1e3 / ms, 3),

@@ -86,7 +86,7 @@ def lib():
             "cd_get_buffer": [c_void_p, c_int32, P(c_void_p), P(c_size_t)],
             "cd_get_length": [c_void_p, c_int32, P(c_int32)],
             "cd_get_config": [c_void_p, P(cd_config)],
-            "cd_set_trace": [c_void_p, c_void_p, c_void_p, c_void_p],
+            "cd_set_trace": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
             "cd_abort_canvas": [c_void_p, c_int32],
             "cd_release": [c_void_p, c_int32, c_void_p],
             "cd_move_request": [c_void_p, c_int32, c_int32, c_void_p],
@@ -309,8 +309,8 @@ def cd_get_length(ctx, req):
     return P.value
 
 
-def cd_set_trace(ctx, h_layers=None, topk_ids=None, topk_gates=None):
-    _check(lib().cd_set_trace(ctx, _ptr(h_layers), _ptr(topk_ids), _ptr(topk_gates)))
+def cd_set_trace(ctx, h_layers=None, topk_ids=None, topk_gates=None, h_mid=None):
+    _check(lib().cd_set_trace(ctx, _ptr(h_layers), _ptr(topk_ids), _ptr(topk_gates), _ptr(h_mid)))
 
 
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "attn_merge", "o_proj", "router", "route",

@@ -258,6 +258,7 @@ struct cd_ctx {
   std::vector<hipEvent_t> pool;       // reusable events
   size_t pool_used = 0;
   float* trace_h = nullptr;
+  float* trace_hmid = nullptr;
   int32_t* trace_ids = nullptr;
   float* trace_gates = nullptr;
   // a second stream (default priority) of the library's own: above 256 rows
@@ -398,7 +399,7 @@ void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s, b
       float* xqs = c->st<float>(c->p.xqs);
       { PROF(CD_PROF_QUANT); note_launch(c, launch_quant_fp8(a.X, a.ldx, M, a.K, xq, a.K, xqs, nullptr, s)); }
       a.X = xq; a.ldx = a.K; a.xscale = xqs;
-      note_launch(c, launch_gemm_x8(epi, a, s));
+      note_launch(c, launch_gemm_x8(wdt, epi, a, s));
       return;
     }
     note_launch(c, launch_gemm_x(wdt, c->p.adt, epi, a, s));
@@ -423,14 +424,15 @@ void gemm_grouped(cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, int x_r
   if (big_expert_tiles(rows, c->p.c.n_experts)) {
     a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + BIG_TILE_ROWS - 1) / BIG_TILE_ROWS +
                                                             std::min<int64_t>(rows, c->p.c.n_experts));
-    if (wdt == CD_FP8 && c->p.x8) {
-      // W8A8 (see gemm_dense); the down projection's input has its own buffer
+    if ((wdt == CD_FP8 || wdt == CD_MXFP4) && c->p.x8) {
+      // W8A8 (see gemm_dense), or MXFP4 weights x E4M3 activations on the
+      // block-scaled MFMA; the down projection's input has its own buffer
       const bool down = epi == EPI_ROWS;
       uint8_t* xq = c->st<uint8_t>(down ? c->p.aq : c->p.xq);
       float* xqs = c->st<float>(down ? c->p.aqs : c->p.xqs);
       { PROF(CD_PROF_QUANT); note_launch(c, launch_quant_fp8(a.X, a.ldx, x_rows, a.K, xq, a.K, xqs, x_rows_dev, s)); }
       a.X = xq; a.ldx = a.K; a.xscale = xqs;
-      note_launch(c, launch_gemm_x8(epi, a, s));
+      note_launch(c, launch_gemm_x8(wdt, epi, a, s));
       return;
     }
     note_launch(c, launch_gemm_x(wdt, c->p.adt, epi, a, s));
@@ -514,6 +516,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       PROF(CD_PROF_O_PROJ);
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
+    if (trace && c->trace_hmid) launch_copy_f32(h, c->trace_hmid + (int64_t)l * T * d, (int64_t)T * d, s);
     { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
     // The shared FFN depends only on u, so its two projections can run on the
     // side stream (its fp32 output rows go to a buffer of their own) while
@@ -740,7 +743,8 @@ int32_t step_internal(cd_ctx* c, int r0, int n_req, hipStream_t s) {
   if (!n_active) return fail(CD_ERR_BAD_STATE, "no request in 0..%d has an active canvas", r0 + n_req - 1);
   // per-launch profiling events and trace copies are taken eagerly
   int32_t st = 1;
-  if (c->graphs && !c->prof && !c->trace_h && !c->trace_ids && !c->trace_gates) st = step_graph(c, r0, n_req, s);
+  if (c->graphs && !c->prof && !c->trace_h && !c->trace_hmid && !c->trace_ids && !c->trace_gates)
+    st = step_graph(c, r0, n_req, s);
   if (st > 1 || st < 0) return st;
   if (st == 1) {
     forward(c, r0, n_req, g.canvas_len, c->st<int32_t>(c->p.canvas) + (int64_t)r0 * g.canvas_len, false, true,
@@ -1350,9 +1354,11 @@ int32_t cd_get_length(cd_ctx* c, int32_t req, int32_t* P) {
   return CD_OK;
 }
 
-int32_t cd_set_trace(cd_ctx* c, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates) {
+int32_t cd_set_trace(cd_ctx* c, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates,
+                     float* d_h_mid_layers) {
   if (int32_t st = check_ctx(c)) return st;
   c->trace_h = d_h_layers;
+  c->trace_hmid = d_h_mid_layers;
   c->trace_ids = d_topk_ids;
   c->trace_gates = d_topk_gates;
   return CD_OK;

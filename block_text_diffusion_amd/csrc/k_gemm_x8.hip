@@ -1,5 +1,5 @@
 // fp8 x fp8 GEMM on 256-row work items (the batched fp8 model's QKV, O and
-// routed-expert projections):
+// routed-expert projections; the MXFP4 model's routed experts with F4):
 //   Y[m][n] = sx[m] * sw[n] * sum_k qx[m][k] qw[n][k]
 // qw: E4M3 weights in the packed fragment tiles (per-row scale sw, applied
 // by the epilogue like the register path's); qx: E4M3 activations with one
@@ -13,6 +13,20 @@
 // 256 rows x 256 columns, eight waves (rows 0-127 / 128-255 x four
 // 16-column weight tiles each), activation fragments copied into LDS with
 // global_load_lds, weights into registers, DIST stages in flight.
+//
+// F4: MXFP4 weights (E2M1 codes, one E8M0 scale per 32 columns of a row) on
+// the same MFMA with block scales: Y[m][n] = sx[m] * sum_k qx[m][k] *
+// e2m1[n][k] * 2^(e[n][k/32] - 127).  With E2M1 in the weight operand, a
+// lane's 32 codes are the 32 consecutive columns 128s + 32q.. (q = lane/16)
+// of its row, one MX block, and its scale operand is that block's exponent;
+// an E4M3 operand gives the lane's bytes 0-15 columns 128s + 16q.. and
+// bytes 16-31 columns 128s + 64 + 16q.. (a bounded probe of one-hot
+// operands on the GPU showed both), which is the activation fragment
+// layout above, so the activations are staged unchanged.  The MXFP4 tile
+// (16 rows x 64 columns, 8 code bytes per lane for columns 16c.. of the
+// tile) gives a lane its 32 columns as two 8-byte chunks 128 bytes apart,
+// and the scale dword of its (row, 32-column half) holds four k-tiles'
+// exponents.
 #include "common.h"
 #include "gemm_epi.h"
 #include "kernels.h"
@@ -28,15 +42,25 @@ __device__ __forceinline__ f32x4 mma_fp8(const u32x4& a0, const u32x4& a1, const
   // formats E4M3 / E4M3, no block scales
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
 }
+// E2M1 weights (32 codes in the first four dwords) with their E8M0 block
+// exponent in the low byte of ws, E4M3 activations at unit scale (127)
+__device__ __forceinline__ f32x4 mma_fp4(const u32x4& w, uint32_t ws, const u32x4& b0, const u32x4& b1,
+                                         f32x4 acc) {
+  const i32x8 a = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, 0, (int)ws, 0, 127);
+}
 
 constexpr int Q8_WAVES = 8, Q8_MTW = 8, Q8_NTW = 4;   // as k_gemm_x: 256 rows x 256 columns
 constexpr int Q8_NBUF = 3, Q8_DIST = 2;
 
-template <int EPI>
+template <int EPI, bool F4>
 __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
   constexpr int BLK = 32;                         // activation fragments per stage: 16 row tiles x 2 k-tiles
   constexpr int BPW = BLK / Q8_WAVES;             // each wave copies 4
-  constexpr int LPS = BPW + 2 * Q8_NTW;           // vector loads per wave per stage
+  // vector loads per wave per stage: fp8, two 16-byte halves per weight
+  // tile; F4, two 8-byte code chunks and a scale dword
+  constexpr int LPS = BPW + (F4 ? 3 : 2) * Q8_NTW;
   __shared__ __attribute__((aligned(1024))) uint8_t xs[Q8_NBUF][BLK * 1024];
 
   const int lane = threadIdx.x & 63;
@@ -71,8 +95,19 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
   const bool row_live = wm * Q8_MTW * 16 < rows;
   const uint8_t* wbase = a.W + (int64_t)group * a.w_gstride;
   const uint8_t* wp[Q8_NTW];
+  const uint8_t* mxp[Q8_NTW];
+  const int qa = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < Q8_NTW; ++j) wp[j] = wbase + (int64_t)min(nt0 + j, a.Nt - 1) * KT * 1024 + lane * 16;
+  for (int j = 0; j < Q8_NTW; ++j) {
+    const int64_t t = min(nt0 + j, a.Nt - 1);
+    if constexpr (F4) {
+      wp[j] = wbase + t * KT * 512 + ((lane & 15) + 32 * (qa & 1)) * 8;
+      mxp[j] = wbase + a.mx_off + t * ((KT + 3) / 4) * 128 + ((lane & 15) * 2 + (qa & 1)) * 4;
+    } else {
+      wp[j] = wbase + t * KT * 1024 + lane * 16;
+      mxp[j] = nullptr;
+    }
+  }
   // fragment f = mt*2 + h: rows mt*16.. of k-tile 2s + h; rows past the
   // tile's end read its last row (finite), their results are dropped
   const uint8_t* xsrc[BPW];
@@ -93,7 +128,8 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
   for (int mt = 0; mt < Q8_MTW; ++mt)
 #pragma unroll
     for (int j = 0; j < Q8_NTW; ++j) acc[mt][j] = f32x4{0, 0, 0, 0};
-  u32x4 w[Q8_DIST][Q8_NTW][2];
+  u32x4 w[Q8_DIST][Q8_NTW][F4 ? 1 : 2];
+  uint32_t wsd[Q8_DIST][Q8_NTW];   // F4: the scale dwords
 
   // k-tile indices past the end are clamped to the last one: every copy
   // stays in bounds (a missing second k-tile gets a copy of the last one,
@@ -107,22 +143,52 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
                                        (lds_void*)(dst + i * 1024), 16, 0, 0);
     }
   };
-  auto issue_w = [&](u32x4 (&ww)[Q8_NTW][2], int s) {
+  // F4: the lane's k-tile is 2s + q/2, clamped like the copies (the codes
+  // of a k-tile past the end are zeroed by compute)
+  auto issue_w = [&](u32x4 (&ww)[Q8_NTW][F4 ? 1 : 2], uint32_t (&sd)[Q8_NTW], int s) {
+    if constexpr (F4) {
+      const int ktc = min(2 * s + (qa >> 1), KT - 1);
 #pragma unroll
-    for (int j = 0; j < Q8_NTW; ++j)
+      for (int j = 0; j < Q8_NTW; ++j) {
+        const uint2 c0 = *reinterpret_cast<const uint2*>(wp[j] + (int64_t)ktc * 512);
+        const uint2 c1 = *reinterpret_cast<const uint2*>(wp[j] + (int64_t)ktc * 512 + 128);
+        ww[j][0] = u32x4{c0.x, c0.y, c1.x, c1.y};
+        sd[j] = *reinterpret_cast<const uint32_t*>(mxp[j] + (int64_t)(ktc >> 2) * 128);
+      }
+    } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        ww[j][h] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)min(2 * s + h, KT - 1) * 1024);
+      for (int j = 0; j < Q8_NTW; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ww[j][h] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)min(2 * s + h, KT - 1) * 1024);
+    }
   };
   // one stage: for each of the wave's 8 row tiles, the fragment pair (two
   // k-tiles) from LDS and four MFMAs; the LDS reads run one row tile ahead
   // of the MFMAs that use them.  SINGLE: the stage holds one k-tile (odd K
   // at the last stage); the weights' second half is zero there, so the
-  // second fragment (a finite copy of the last k-tile) adds nothing.
-  auto compute = [&](const u32x4 (&ww)[Q8_NTW][2], const uint8_t* buf, bool single) {
+  // second fragment (a finite copy of the last k-tile) adds nothing.  F4:
+  // the lanes whose k-tile is past the end (q/2 = 1 there) take zero codes;
+  // each lane's exponent is byte (k-tile mod 4) of its scale dword.
+  auto compute = [&](const u32x4 (&ww)[Q8_NTW][F4 ? 1 : 2], const uint32_t (&sd)[Q8_NTW], const uint8_t* buf,
+                     bool single, int s) {
     u32x4 w1[Q8_NTW];
+    uint32_t es[Q8_NTW];
+    if constexpr (F4) {
+      const bool zero = single && (qa >> 1);
+      const int sh = 8 * (min(2 * s + (qa >> 1), KT - 1) & 3);
 #pragma unroll
-    for (int j = 0; j < Q8_NTW; ++j) w1[j] = single ? u32x4{0, 0, 0, 0} : ww[j][1];
+      for (int j = 0; j < Q8_NTW; ++j) {
+        w1[j] = zero ? u32x4{0, 0, 0, 0} : ww[j][0];
+        es[j] = sd[j] >> sh;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < Q8_NTW; ++j) {
+        w1[j] = single ? u32x4{0, 0, 0, 0} : ww[j][F4 ? 0 : 1];
+        es[j] = 0;
+      }
+    }
     const uint8_t* p0 = buf + ((wm * Q8_MTW) * 2 * 64 + lane) * 16;
     u32x4 xa[2], xb[2];
     auto rd = [&](u32x4 (&x)[2], int mt) {
@@ -134,10 +200,14 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
     for (int mt = 0; mt < Q8_MTW; mt += 2) {
       rd(xb, mt + 1);
 #pragma unroll
-      for (int j = 0; j < Q8_NTW; ++j) acc[mt][j] = mma_fp8(ww[j][0], w1[j], xa[0], xa[1], acc[mt][j]);
+      for (int j = 0; j < Q8_NTW; ++j)
+        acc[mt][j] = F4 ? mma_fp4(w1[j], es[j], xa[0], xa[1], acc[mt][j])
+                        : mma_fp8(ww[j][0], w1[j], xa[0], xa[1], acc[mt][j]);
       if (mt + 2 < Q8_MTW) rd(xa, mt + 2);
 #pragma unroll
-      for (int j = 0; j < Q8_NTW; ++j) acc[mt + 1][j] = mma_fp8(ww[j][0], w1[j], xb[0], xb[1], acc[mt + 1][j]);
+      for (int j = 0; j < Q8_NTW; ++j)
+        acc[mt + 1][j] = F4 ? mma_fp4(w1[j], es[j], xb[0], xb[1], acc[mt + 1][j])
+                            : mma_fp8(ww[j][0], w1[j], xb[0], xb[1], acc[mt + 1][j]);
     }
     // order: reads of tile 0, then (reads of tile mt+1, MFMAs of tile mt)
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -152,7 +222,7 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < Q8_DIST; ++j) {
     issue(j);
-    issue_w(w[j], j);
+    issue_w(w[j], wsd[j], j);
   }
   for (int s0 = 0; s0 < nst; s0 += Q8_DIST) {
 #pragma unroll
@@ -165,9 +235,9 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       issue(s + Q8_DIST);
       __builtin_amdgcn_sched_barrier(0);
-      if (s < nst && row_live) compute(w[j], xs[s % Q8_NBUF], 2 * s + 1 >= KT);
+      if (s < nst && row_live) compute(w[j], wsd[j], xs[s % Q8_NBUF], 2 * s + 1 >= KT, s);
       __builtin_amdgcn_sched_barrier(0);
-      issue_w(w[j], s + Q8_DIST);
+      issue_w(w[j], wsd[j], s + Q8_DIST);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -199,21 +269,30 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
   }
 }
 
-template <int EPI>
+template <int EPI, bool F4>
 static void run_x8(const GemmArgs& a, hipStream_t s) {
   const int chunks = (a.Nt + 4 * Q8_NTW - 1) / (4 * Q8_NTW);
   const int tiles = a.tiles ? a.max_tiles : (a.M + 255) / 256;
   const int blocks = (int)round_up((int64_t)tiles * chunks, 8);
-  hipLaunchKernelGGL((k_gemm_x8<EPI>), dim3(blocks), dim3(64 * Q8_WAVES), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_x8<EPI, F4>), dim3(blocks), dim3(64 * Q8_WAVES), 0, s, a);
 }
 
-int launch_gemm_x8(int epi, const GemmArgs& a, hipStream_t s) {
-  if (a.ksplit > 1 || !a.xscale || a.K % 64) return -5;
+int launch_gemm_x8(int wdt, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.ksplit > 1 || !a.xscale || a.K % 64 || (wdt != DT_FP8 && wdt != DT_FP4)) return -5;
+  if (wdt == DT_FP4) {
+    // routed experts only
+    switch (epi) {
+      case EPI_SWIGLU: run_x8<EPI_SWIGLU, true>(a, s); break;
+      case EPI_ROWS: run_x8<EPI_ROWS, true>(a, s); break;
+      default: return -5;
+    }
+    return 0;
+  }
   switch (epi) {
-    case EPI_RESID: run_x8<EPI_RESID>(a, s); break;
-    case EPI_SWIGLU: run_x8<EPI_SWIGLU>(a, s); break;
-    case EPI_QKV: run_x8<EPI_QKV>(a, s); break;
-    case EPI_ROWS: run_x8<EPI_ROWS>(a, s); break;
+    case EPI_RESID: run_x8<EPI_RESID, false>(a, s); break;
+    case EPI_SWIGLU: run_x8<EPI_SWIGLU, false>(a, s); break;
+    case EPI_QKV: run_x8<EPI_QKV, false>(a, s); break;
+    case EPI_ROWS: run_x8<EPI_ROWS, false>(a, s); break;
     default: return -5;
   }
   return 0;

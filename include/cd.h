@@ -322,10 +322,13 @@ int32_t cd_get_length(cd_ctx* ctx, int32_t req, int32_t* P);
 
 /* Optional parity trace: when set, every forward (prefill, denoise pass,
  * commit recompute) over T rows writes each layer's input residual rows
- * (f32 [L][T][d]) and routing (i32 ids / f32 gates [L][T][top_k]) to these
- * caller buffers, sized for the largest T used.  NULL pointers switch a part
- * off; cd_set_trace(ctx, NULL, NULL, NULL) switches tracing off. */
-int32_t cd_set_trace(cd_ctx* ctx, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates);
+ * (f32 [L][T][d]), its routing (i32 ids / f32 gates [L][T][top_k]) and its
+ * residual rows after the attention block, the input of the MoE block's
+ * RMSNorm (f32 [L][T][d]), to these caller buffers, sized for the largest T
+ * used.  NULL pointers switch a part off; cd_set_trace(ctx, NULL, NULL,
+ * NULL, NULL) switches tracing off. */
+int32_t cd_set_trace(cd_ctx* ctx, float* d_h_layers, int32_t* d_topk_ids, float* d_topk_gates,
+                     float* d_h_mid_layers);
 
 /* Graph replay of denoise passes (on by default).  The launches of one pass
  * depend on the host only through the first slot, the number of slots, the

@@ -13,10 +13,10 @@ bench.py times.  The oracle checks what it can compute row by row:
 * the LM head on sampled vocabulary rows of the last request;
 * the sampler on the last request's GPU logits (its own Philox stream).
 The same batch with MXFP4 experts (``batch_mxfp4``: 512 rows per expert, so
-the expert GEMMs run the LDS-staged kernel's MXFP4 path at K = 2816 and 704)
-is checked the same way.  Tolerance: fp8 and MXFP4 6e-2 (per-row relative
-L2).  At this batch the QKV projection (and, with fp8 experts, the routed
-experts) quantise their activation rows to E4M3 (reading R18), which the
+the expert GEMMs run MXFP4 weights on the block-scaled fp4 x fp8 MFMA at
+K = 2816 and 704) is checked the same way.  Tolerance: fp8 and MXFP4 6e-2
+(per-row relative L2).  At this batch the QKV projection and the routed
+experts quantise their activation rows to E4M3 (reading R18), which the
 oracle does not emulate; the same rows are therefore also taken along the
 GPU's arithmetic (bf16 activation rows, the per-row E4M3 quantiser, bf16
 intermediate rows, tests/oracle_rows.check_layer_w8a8): keys and values at
@@ -33,7 +33,8 @@ from oracle import model, philox
 from oracle.weights import Weights
 from tests.gpu_util import TOL, announce, rel_l2_rows, to_np
 from tests.oracle_rows import Summary, check_layer, check_layer_w8a8
-from tests.test_gpu_full_width import ADOPT_CAP, CANVAS_ROWS, W8A8_TOL_H, W8A8_TOL_KV, check_sampler
+from tests.test_gpu_full_width import (ADOPT_CAP, CANVAS_ROWS, W8A8_MOE_MEDIAN, W8A8_TOL_H, W8A8_TOL_KV,
+                                       W8A8_TOL_MOE, check_sampler)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,9 +62,10 @@ def test_batch_full_width_every_layer(name):
 
     T = R * C
     th = torch.zeros(L, T, d, dtype=torch.float32, device="cuda")
+    thm = torch.zeros(L, T, d, dtype=torch.float32, device="cuda")
     tid = torch.zeros(L, T, k, dtype=torch.int32, device="cuda")
     tg = torch.zeros(L, T, k, dtype=torch.float32, device="cuda")
-    B.cd_set_trace(eng.ctx, th, tid, tg)
+    B.cd_set_trace(eng.ctx, th, tid, tg, thm)
     B.cd_denoise_step(eng.ctx, R, eng.info)
     infos = eng.step_info(R)
     B.cd_set_trace(eng.ctx)
@@ -73,7 +75,7 @@ def test_batch_full_width_every_layer(name):
     got = {}
     for r, rows in ROWS.items():
         gr = torch.from_numpy(r * C + rows).cuda()
-        got[r] = dict(h=to_np(th[:, gr]), fin=to_np(hid[gr]), ids=to_np(tid[:, gr]),
+        got[r] = dict(h=to_np(th[:, gr]), hm=to_np(thm[:, gr]), fin=to_np(hid[gr]), ids=to_np(tid[:, gr]),
                       K=eng.kcache()[r, :, :, :P0 + C, :].cpu(), V=eng.vcache()[r, :, :, :, :P0 + C].cpu())
     rl = R - 1
     z = eng.logits(R)[rl * C:(rl + 1) * C].cpu().numpy()
@@ -82,11 +84,12 @@ def test_batch_full_width_every_layer(name):
     lock = to_np(eng.view(B.CD_BUF_LOCK, torch.uint8, (R, C))[rl]).astype(bool)
     xn = eng.canvas()[rl].cpu().numpy()
     H = to_np(eng.view(B.CD_BUF_ENTROPY, torch.float64, (R, C))[rl])
-    del th, tid, tg, hid
+    del th, thm, tid, tg, hid
     eng.close()
     del eng
 
     S = Summary(name)
+    moe_rows = []
     for l in range(L):
         items = []
         for r, rows in ROWS.items():
@@ -95,14 +98,16 @@ def test_batch_full_width_every_layer(name):
             Vv = g["V"][l].float().numpy().astype(np.float64).transpose(0, 2, 1)
             pos = P0 + rows
             items.append(dict(name=f"req{r}", h_in=g["h"][l], h_out=g["h"][l + 1] if l + 1 < L else g["fin"],
-                              pos=pos, K=K, V=Vv, causal=False, ids=g["ids"][l],
+                              h_mid=g["hm"][l], pos=pos, K=K, V=Vv, causal=False, ids=g["ids"][l],
                               k_got=K[:, pos].transpose(1, 0, 2), v_got=Vv[:, pos].transpose(1, 0, 2)))
         res = check_layer(w, l, items, tol)
         S.add_layer(res)
-        # the QKV GEMM (fp8 attention weights) and, with fp8 experts, the routed
-        # experts run W8A8 at 8192 rows: the same rows along the GPU's arithmetic
+        # the QKV GEMM (fp8 attention weights) runs W8A8 at 8192 rows, and the
+        # routed experts (fp8 or MXFP4 weights) on E4M3 activations: the same
+        # rows along the GPU's arithmetic
         m8 = check_layer_w8a8(w, l, items, W8A8_TOL_KV, W8A8_TOL_H if l in (0, L - 1) else None,
-                              experts=w["wdtype"] == "fp8")
+                              experts=True, tol_moe=W8A8_TOL_MOE)
+        moe_rows.append(m8.pop("moe_rows", np.zeros(0)))
         for key, val in m8.items():
             S.add(key, val)
         print(f"layer {l}: {[{k2: float(f'{v:.2e}') for k2, v in r_.items()} for r_ in res]} "
@@ -114,4 +119,7 @@ def test_batch_full_width_every_layer(name):
     S.add("lm_head", rel_l2_rows(z[:, vrows], zref).max())
     assert S.err["lm_head"] <= tol
     check_sampler(w, z, am, lock, xn, H, infos[rl].mean_entropy, seed, 1, 0, rl)
+    med = float(np.median(np.concatenate(moe_rows)))
+    S.add("moe8_median", med)
+    assert med <= W8A8_MOE_MEDIAN, ("w8a8 moe median", med)
     S.report(ADOPT_CAP[w["wdtype"]])

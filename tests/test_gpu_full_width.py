@@ -19,8 +19,9 @@ test, so it checks what it can compute row by row, at every layer:
 * the sampler on the GPU's own logits (all 256 x 262144).
 The same step with MXFP4 experts and fp8 attention (``step_mxfp4``) is
 checked the same way.  Tolerance: bf16 2e-2, MXFP4 6e-2 (per-row relative
-L2).  Its 4096-row prefill runs the QKV projection W8A8 (activation rows
-quantised to E4M3, reading R18), which the oracle does not emulate, so the
+L2).  Its 4096-row prefill runs the QKV projection W8A8 and the MXFP4
+experts on the block-scaled fp4 x fp8 MFMA (activation rows quantised to
+E4M3, reading R18), which the oracle does not emulate, so the
 prompt rows are also taken along the GPU's arithmetic (check_layer_w8a8):
 keys and values within 6e-3 at every layer, the layer output within 2e-2 at
 the first and last layer.  The largest errors are printed as one "[parity]"
@@ -45,6 +46,12 @@ ADOPT_CAP = {"f32": 0.01, "bf16": 0.04, "fp8": 0.04, "mxfp4": 0.04}
 # the GPU arithmetic modelled in the test (check_layer_w8a8): what is left is
 # the bf16 rounding of the outputs and fp32 accumulation
 W8A8_TOL_KV, W8A8_TOL_H = 6e-3, 2e-2
+# the MoE block modelled from the GPU's own input rows (the traced residual
+# after the attention block): per row within 3e-2 (a few E4M3 steps of
+# single elements of the down projection's input, moved by fp32 rounding
+# upstream), median over the checked rows within 2e-3 (the bf16 rounding of
+# the expert outputs and fp32 summation order)
+W8A8_TOL_MOE, W8A8_MOE_MEDIAN = 3e-2, 2e-3
 CANVAS_ROWS = np.array([2, 29, 35, 60, 66, 93, 101, 126, 130, 157, 163, 190, 197, 222, 229, 254])
 PREFILL_POS = np.array([0, 1, 777, 2047, 2048, 3001, 4094, 4095])
 
@@ -72,13 +79,15 @@ def test_step_full_width_every_layer(name):
     B.cd_synth_weights(eng.ctx, w["weight_seed"])
     prefix = synth_inputs.prefix_ids(V, P0, w["prefix_seed"])
     th = torch.zeros(L * P0 * d, dtype=torch.float32, device="cuda")
+    thm = torch.zeros(L * P0 * d, dtype=torch.float32, device="cuda")
     tid = torch.zeros(L * P0 * k, dtype=torch.int32, device="cuda")
     tg = torch.zeros(L * P0 * k, dtype=torch.float32, device="cuda")
-    B.cd_set_trace(eng.ctx, th, tid, tg)
+    B.cd_set_trace(eng.ctx, th, tid, tg, thm)
     B.cd_prefill(eng.ctx, 0, torch.from_numpy(prefix).cuda())
     torch.cuda.synchronize()
     pp = torch.from_numpy(PREFILL_POS).cuda()
     p_h = to_np(th.view(L, P0, d)[:, pp])
+    p_hm = to_np(thm.view(L, P0, d)[:, pp])
     p_ids = to_np(tid.view(L, P0, k)[:, pp])
     p_fin = to_np(eng.view(B.CD_BUF_HIDDEN, torch.float32, (P0, d))[pp])
     seed = w["gen_seed"]
@@ -106,6 +115,7 @@ def test_step_full_width_every_layer(name):
 
     S = Summary(name)
     cpos = P0 + CANVAS_ROWS
+    moe_rows = []
     for l in range(L):
         K = Kc[l].float().numpy().astype(np.float64)                     # [Hkv][P0+C][dh]
         Vv = Vc[l].float().numpy().astype(np.float64).transpose(0, 2, 1)
@@ -113,7 +123,8 @@ def test_step_full_width_every_layer(name):
             dict(name="canvas", h_in=c_h[l], h_out=c_h[l + 1] if l + 1 < L else hfinal[CANVAS_ROWS], pos=cpos,
                  K=K, V=Vv, causal=False, ids=c_ids[l], k_got=K[:, cpos].transpose(1, 0, 2),
                  v_got=Vv[:, cpos].transpose(1, 0, 2)),
-            dict(name="prefill", h_in=p_h[l], h_out=p_h[l + 1] if l + 1 < L else p_fin, pos=PREFILL_POS,
+            dict(name="prefill", h_in=p_h[l], h_out=p_h[l + 1] if l + 1 < L else p_fin, h_mid=p_hm[l],
+                 pos=PREFILL_POS,
                  K=K[:, :P0], V=Vv[:, :P0], causal=True, ids=p_ids[l],
                  k_got=K[:, PREFILL_POS].transpose(1, 0, 2), v_got=Vv[:, PREFILL_POS].transpose(1, 0, 2)),
         ]
@@ -123,9 +134,11 @@ def test_step_full_width_every_layer(name):
         m8 = {}
         if w["wdtype"] in ("fp8", "mxfp4"):
             # the 4096-row prefill runs the QKV GEMM of the fp8 attention weights
-            # W8A8: its rows along the GPU's arithmetic
+            # W8A8 and the routed experts on E4M3 activations (fp8 or MXFP4
+            # weights): its rows along the GPU's arithmetic
             m8 = check_layer_w8a8(w, l, items[1:], W8A8_TOL_KV, W8A8_TOL_H if l in (0, L - 1) else None,
-                                  experts=w["wdtype"] == "fp8")
+                                  experts=True, tol_moe=W8A8_TOL_MOE)
+            moe_rows.append(m8.pop("moe_rows", np.zeros(0)))
             for key, val in m8.items():
                 S.add("prefill_" + key, val)
         print(f"layer {l}: {[{k2: float(f'{v:.2e}') for k2, v in r.items()} for r in res]} "
@@ -137,4 +150,8 @@ def test_step_full_width_every_layer(name):
     S.add("lm_head", rel_l2_rows(z[:, vrows], zref).max())
     assert S.err["lm_head"] <= tol
     check_sampler(w, z, am, lock, xn, H, info.mean_entropy, seed, 1, 0, 0)
+    if moe_rows:
+        med = float(np.median(np.concatenate(moe_rows)))
+        S.add("prefill_moe8_median", med)
+        assert med <= W8A8_MOE_MEDIAN, ("w8a8 moe median", med)
     S.report(ADOPT_CAP[w["wdtype"]])
