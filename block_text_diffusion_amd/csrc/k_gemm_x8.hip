@@ -67,7 +67,11 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int nchunks = (a.Nt + 4 * Q8_NTW - 1) / (4 * Q8_NTW);
-  // work items dealt to the 8 XCDs chunk-major, as in k_gemm_x
+  // work items dealt to the 8 XCDs tile-major: a row tile's column chunks run
+  // back to back on one XCD, so its (gathered) activation rows come into that
+  // XCD's L2 once; the row tiles of one expert are adjacent as well, so its
+  // weight chunks are shared there too (same-process A/B against chunk-major:
+  // 70.9 -> 70.0 ms per 32-request MXFP4 pass, 77.6 -> 76.2 ms fp8)
   int chunk, tile;
   {
     const int nt = a.tiles ? *a.n_tiles : (a.M + 255) / 256;
@@ -77,8 +81,8 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
     if (bid >= w8) return;
     const int logical = (bid & 7) * (w8 >> 3) + (bid >> 3);
     if (logical >= work) return;
-    chunk = logical / nt;
-    tile = logical - chunk * nt;
+    tile = logical / nchunks;
+    chunk = logical - tile * nchunks;
   }
   int group = 0, row0, rows;
   if (a.tiles) {
