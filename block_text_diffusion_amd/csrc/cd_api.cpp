@@ -261,11 +261,11 @@ struct cd_ctx {
   float* trace_hmid = nullptr;
   int32_t* trace_ids = nullptr;
   float* trace_gates = nullptr;
-  // a second stream (default priority) of the library's own: above 256 rows
-  // the shared FFN runs there while the router, routing and expert GEMMs run
-  // on the caller's stream; the two join before the combine, inside the same
-  // call.  Created on first use; if that fails the shared FFN runs on the
-  // caller's stream.
+  // a second stream (default priority) of the library's own: above 256 rows,
+  // and in captured passes, the shared FFN runs there while the router,
+  // routing and expert GEMMs run on the caller's stream; the two join before
+  // the combine, inside the same call.  Created on first use; if that fails
+  // the shared FFN runs on the caller's stream.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool side_tried = false;
@@ -521,15 +521,14 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
     // The shared FFN depends only on u, so its two projections can run on the
     // side stream (its fp32 output rows go to a buffer of their own) while
     // the router and the routing run here; the combine then adds the routed
-    // experts and the shared FFN into the residual.  Above 256 rows the branch
-    // joins before the combine: the expert GEMMs it then also overlaps are
-    // bound by their MFMAs.  At 256 rows and below those GEMMs are bound by
-    // HBM and would only be slowed by the shared FFN's weight stream, so the
-    // branch joins before them, covering just the latency-bound routing; that
-    // pays only inside a captured graph (an edge instead of the runtime's
-    // event wait), so a pass launched one by one runs the shared FFN in line.
+    // experts and the shared FFN into the residual.  The branch joins before
+    // the combine.  Above 256 rows the expert GEMMs it overlaps are bound by
+    // their MFMAs.  At 256 rows and below it mostly fills the latency-bound
+    // routing (the rest of it overlaps the start of the HBM-bound expert
+    // GEMMs), which pays only inside a captured graph (edges instead of the
+    // runtime's event waits), so a pass launched one by one runs the shared
+    // FFN in line.
     const bool fork = g.shared_hidden && (T > 256 || c->capturing) && ensure_side(c);
-    const bool early_join = fork && T <= 256;
     if (g.shared_hidden) {
       hipStream_t ss = fork ? c->side : s;
       if (fork) {
@@ -569,7 +568,6 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       ra.trace_gates = c->trace_gates + (int64_t)l * T * k;
     }
     { PROF(CD_PROF_ROUTE); launch_route(ra, s); }
-    if (early_join) hipStreamWaitEvent(s, c->ev_join, 0);
     {
       GemmArgs a = gemm_base(u, d, c->W + lw.gu, c->wt<float>(lw.gu_s), d, p.gu_npad, 2 * g.expert_hidden,
                              c->st<void>(p.aperm), g.expert_hidden);
@@ -588,7 +586,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
     // h += sum_j gate_j * y_j (choice order) + shared FFN row; the same kernel
     // writes u = RMSNorm(h) for the next layer or the LM head (every reader
     // of this layer's u ran before it on this stream or joined above)
-    if (fork && !early_join) hipStreamWaitEvent(s, c->ev_join, 0);
+    if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
     {
       u_ready = l + 1 < g.n_layers || head;
       PROF(CD_PROF_COMBINE);
