@@ -361,17 +361,22 @@ void launch_route(const RouteArgs& a, hipStream_t s) {
 }
 
 // h[t] += sum_j gate[t][j] * Y[slot[t][j]] (j in order: deterministic), then
-// + add[t] (the shared FFN's fp32 row) when given.  A token's gates and slots
-// (k <= 16) are loaded once, and the k expert rows of a column group in
-// batches of 8 before any is added, so the loads overlap.  When u is given
-// the workgroup also writes the RMSNorm (unit gain) of the new row into it,
-// the input of the next layer or of the LM head.
-template <int AT>
-__global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* slot, const float* gate,
-                                                 const float* add, int k, int d, float* h, void* u, float eps) {
+// + add[t] (the shared FFN's fp32 row) when given.  When u is given the
+// workgroup also writes the RMSNorm (unit gain) of the new row into it, the
+// input of the next layer or of the LM head.
+//
+// NI > 0: the row's NI column groups (1024 columns each, d <= 1024 NI) stay in
+// registers.  After the gates and slots, every load of the row (h, the k
+// expert rows in batches of 8, the shared row) is issued before the first
+// use, and the norm is taken from the registers, so a token costs two memory
+// round trips.  NI = 0 (d > 4096): one column group at a time.
+template <int AT, int NI>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ Yp, const int32_t* __restrict__ slot,
+                                                 const float* __restrict__ gate, const float* __restrict__ add,
+                                                 int k, int d, float* __restrict__ h, void* __restrict__ u,
+                                                 float eps) {
   __shared__ float red[4];
   const int t = blockIdx.x;
-  float ss = 0.f;
   float g[16];
   int64_t yr[16];
 #pragma unroll
@@ -380,42 +385,15 @@ __global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* 
     g[j] = gate[(int64_t)t * k + jc];
     yr[j] = slot[(int64_t)t * k + jc];
   }
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    float4 acc = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
-#pragma unroll
-    for (int j0 = 0; j0 < 16; j0 += 8) {
-      if (j0 >= k) break;
-      float4 y[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if constexpr (AT == DT_F32) {
-          y[q] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Yp) + yr[j0 + q] * d + c);
-        } else {
-          const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Yp) + yr[j0 + q] * d + c);
-          y[q] = make_float4(bf2f(b.x & 0xFFFF), bf2f(b.x >> 16), bf2f(b.y & 0xFFFF), bf2f(b.y >> 16));
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (j0 + q < k) {
-          acc.x += g[j0 + q] * y[q].x; acc.y += g[j0 + q] * y[q].y; acc.z += g[j0 + q] * y[q].z; acc.w += g[j0 + q] * y[q].w;
-        }
+  auto row8 = [&](int64_t r, int c) -> float4 {
+    if constexpr (AT == DT_F32) {
+      return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Yp) + r * d + c);
+    } else {
+      const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Yp) + r * d + c);
+      return make_float4(bf2f(b.x & 0xFFFF), bf2f(b.x >> 16), bf2f(b.y & 0xFFFF), bf2f(b.y >> 16));
     }
-    if (add) {
-      const float4 v = *reinterpret_cast<const float4*>(add + (int64_t)t * d + c);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = acc;
-    ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
-  }
-  if (!u) return;
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
-  // each thread reads back the elements of h it wrote itself
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
+  };
+  auto put_u = [&](int c, const float4& v, float inv) {
     if constexpr (AT == DT_F32) {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(u) + (int64_t)t * d + c) =
           make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
@@ -425,13 +403,100 @@ __global__ __launch_bounds__(256) void k_combine(const void* Yp, const int32_t* 
       p.y = pack_bf16(v.z * inv, v.w * inv);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(u) + (int64_t)t * d + c) = p;
     }
+  };
+  float ss = 0.f;
+  if constexpr (NI > 0) {
+    float4 acc[NI], sh[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = min(threadIdx.x * 4 + 1024 * i, d - 4);   // past the row's end: a valid column, unused
+      acc[i] = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
+      sh[i] = add ? *reinterpret_cast<const float4*>(add + (int64_t)t * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += 8) {
+      if (j0 >= k) break;
+      float4 y[NI][8];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[i][q] = row8(yr[j0 + q], min(threadIdx.x * 4 + 1024 * i, d - 4));
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (j0 + q < k) {
+            const float gq = g[j0 + q];
+            acc[i].x += gq * y[i][q].x; acc[i].y += gq * y[i][q].y; acc[i].z += gq * y[i][q].z; acc[i].w += gq * y[i][q].w;
+          }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = threadIdx.x * 4 + 1024 * i;
+      if (c >= d) continue;
+      if (add) { acc[i].x += sh[i].x; acc[i].y += sh[i].y; acc[i].z += sh[i].z; acc[i].w += sh[i].w; }
+      *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = acc[i];
+      ss += acc[i].x * acc[i].x + acc[i].y * acc[i].y + acc[i].z * acc[i].z + acc[i].w * acc[i].w;
+    }
+    if (!u) return;
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = threadIdx.x * 4 + 1024 * i;
+      if (c < d) put_u(c, acc[i], inv);
+    }
+  } else {
+    for (int c = threadIdx.x * 4; c < d; c += 1024) {
+      float4 acc = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
+#pragma unroll
+      for (int j0 = 0; j0 < 16; j0 += 8) {
+        if (j0 >= k) break;
+        float4 y[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[q] = row8(yr[j0 + q], c);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (j0 + q < k) {
+            acc.x += g[j0 + q] * y[q].x; acc.y += g[j0 + q] * y[q].y; acc.z += g[j0 + q] * y[q].z; acc.w += g[j0 + q] * y[q].w;
+          }
+      }
+      if (add) {
+        const float4 v = *reinterpret_cast<const float4*>(add + (int64_t)t * d + c);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = acc;
+      ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+    }
+    if (!u) return;
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+    // each thread reads back the elements of h it wrote itself
+    for (int c = threadIdx.x * 4; c < d; c += 1024) put_u(c, *reinterpret_cast<const float4*>(h + (int64_t)t * d + c), inv);
+  }
+}
+
+template <int AT>
+static void run_combine(const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k, int d,
+                        float* h, void* u, float eps, hipStream_t s) {
+  const dim3 g(T), b(256);
+  switch ((d + 1023) / 1024) {
+    case 1: hipLaunchKernelGGL((k_combine<AT, 1>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
+    case 2: hipLaunchKernelGGL((k_combine<AT, 2>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
+    case 3: hipLaunchKernelGGL((k_combine<AT, 3>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
+    case 4: hipLaunchKernelGGL((k_combine<AT, 4>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
+    default: hipLaunchKernelGGL((k_combine<AT, 0>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
   }
 }
 
 void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k,
                     int d, float* h, void* u, float eps, hipStream_t s) {
-  if (adt == DT_F32) hipLaunchKernelGGL(k_combine<DT_F32>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h, u, eps);
-  else hipLaunchKernelGGL(k_combine<DT_BF16>, dim3(T), dim3(256), 0, s, Yp, slot, gate, add, k, d, h, u, eps);
+  if (adt == DT_F32) run_combine<DT_F32>(Yp, slot, gate, add, T, k, d, h, u, eps, s);
+  else run_combine<DT_BF16>(Yp, slot, gate, add, T, k, d, h, u, eps, s);
 }
 
 }  // namespace cd
