@@ -384,7 +384,23 @@ void note_launch(cd_ctx* c, int st) {
 // LDS-staged kernel).  The QKV projection takes it; the output projection
 // keeps bf16 activations, since its output feeds the router directly and the
 // activation rounding moved near-tie routing decisions too far.
-void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s, bool w8a8 = false) {
+// Whether a dense launch (as gemm_dense decides) or a grouped expert launch (as
+// gemm_grouped decides) runs W8A8 on E4M3 activation rows; the forward asks
+// before the launch so that the kernel producing those rows also writes them
+// in E4M3.
+bool dense_takes_x8(const cd_ctx* c, int wdt, int epi, int64_t Nt, int M, int ksplit, bool w8a8) {
+  const int64_t x_items = (int64_t)((M + 255) / 256) * ((Nt + 15) / 16);
+  const bool lds_staged = ksplit <= 1 && ((M > 256 && x_items >= 256) || (Nt + 7) / 8 >= 512);
+  return lds_staged && w8a8 && wdt == CD_FP8 && c->p.x8 && epi != EPI_F32;
+}
+bool grouped_takes_x8(const cd_ctx* c, int wdt, int64_t rows) {
+  return big_expert_tiles(rows, c->p.c.n_experts) && (wdt == CD_FP8 || wdt == CD_MXFP4) && c->p.x8;
+}
+
+// quantised: the activation rows are already in the E4M3 buffer (written by
+// the kernel that produced them), so the W8A8 path skips its quantiser.
+void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s, bool w8a8 = false,
+                bool quantised = false) {
   // the LDS-staged kernel needs enough (256-row slab, 256-column chunk)
   // items to fill the chip; the expert-combining epilogue gathers 8 rows per
   // output and prefers the many workgroups of the row-tiled kernel
@@ -397,7 +413,10 @@ void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s, b
       // W8A8: the activation rows quantised to E4M3 with a scale per row
       uint8_t* xq = c->st<uint8_t>(c->p.xq);
       float* xqs = c->st<float>(c->p.xqs);
-      { PROF(CD_PROF_QUANT); note_launch(c, launch_quant_fp8(a.X, a.ldx, M, a.K, xq, a.K, xqs, nullptr, s)); }
+      if (!quantised) {
+        PROF(CD_PROF_QUANT);
+        note_launch(c, launch_quant_fp8(a.X, a.ldx, M, a.K, xq, a.K, xqs, nullptr, s));
+      }
       a.X = xq; a.ldx = a.K; a.xscale = xqs;
       note_launch(c, launch_gemm_x8(wdt, epi, a, s));
       return;
@@ -418,7 +437,7 @@ void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s, b
 // x_rows: rows of X (the tokens for gate/up, the permuted rows for down);
 // x_rows_dev: their device count (down: the padded segments' end) or null
 void gemm_grouped(cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, int x_rows, const int32_t* x_rows_dev,
-                  hipStream_t s) {
+                  hipStream_t s, bool quantised = false) {
   a.tiles = c->st<int32_t>(c->p.tiles);
   a.n_tiles = c->st<int32_t>(c->p.n_tiles);
   if (big_expert_tiles(rows, c->p.c.n_experts)) {
@@ -430,7 +449,10 @@ void gemm_grouped(cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, int x_r
       const bool down = epi == EPI_ROWS;
       uint8_t* xq = c->st<uint8_t>(down ? c->p.aq : c->p.xq);
       float* xqs = c->st<float>(down ? c->p.aqs : c->p.xqs);
-      { PROF(CD_PROF_QUANT); note_launch(c, launch_quant_fp8(a.X, a.ldx, x_rows, a.K, xq, a.K, xqs, x_rows_dev, s)); }
+      if (!(quantised && !down)) {
+        PROF(CD_PROF_QUANT);
+        note_launch(c, launch_quant_fp8(a.X, a.ldx, x_rows, a.K, xq, a.K, xqs, x_rows_dev, s));
+      }
       a.X = xq; a.ldx = a.K; a.xscale = xqs;
       note_launch(c, launch_gemm_x8(wdt, epi, a, s));
       return;
@@ -489,12 +511,22 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
   at.part_ml = c->st<float>(p.part_ml);
 
   { PROF(CD_PROF_EMBED); launch_embed(p.wdt_other, c->W + p.embed, ids, T, g.vocab, d, h, s); }
+  // When the QKV projection or the routed experts run W8A8, the kernel that
+  // writes their input u (the RMSNorm, or the combine for the next layer)
+  // also writes its E4M3 rows and scales into the activation buffer they read.
+  const bool qkv8 = dense_takes_x8(c, p.wdt_attn, EPI_QKV, p.qkv_npad / 16, T, 1, true);
+  const bool gu8 = grouped_takes_x8(c, p.wdt_exp, (int64_t)T * k);
+  uint8_t* xq = p.x8 ? c->st<uint8_t>(p.xq) : nullptr;
+  float* xqs = p.x8 ? c->st<float>(p.xqs) : nullptr;
   // u holds RMSNorm(h) once a combine has written it for the next consumer
   bool u_ready = false;
   for (int l = 0; l < g.n_layers; ++l) {
     const LayerOff& lw = p.layer[l];
     if (trace && c->trace_h) launch_copy_f32(h, c->trace_h + (int64_t)l * T * d, (int64_t)T * d, s);
-    if (!u_ready) { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
+    if (!u_ready) {
+      PROF(CD_PROF_RMSNORM);
+      launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s, qkv8 ? xq : nullptr, xqs);
+    }
     u_ready = false;
     // QKV + rotary, K/V scattered into the cache at positions P_r + i
     {
@@ -506,7 +538,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       a.max_ctx = p.ctx; a.Hq = g.n_q_heads; a.Hkv = g.n_kv_heads; a.dh = dh;
       a.rows_per_req = rows_per_req; a.pos0 = pos0; a.pos0_stride = pos_stride; a.rope_cs = rope;
       a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)dh));   // log2(e) / sqrt(dh)
-      { PROF(CD_PROF_QKV); gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s, true); }
+      { PROF(CD_PROF_QKV); gemm_dense(c, p.wdt_attn, EPI_QKV, a, T, s, true, qkv8); }
       at.kc = kc; at.vc = vc;
     }
     { PROF(CD_PROF_ATTN); launch_attention(adt, at, s); }
@@ -517,7 +549,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       gemm_dense(c, p.wdt_attn, EPI_RESID, a, T, s);
     }
     if (trace && c->trace_hmid) launch_copy_f32(h, c->trace_hmid + (int64_t)l * T * d, (int64_t)T * d, s);
-    { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s); }
+    { PROF(CD_PROF_RMSNORM); launch_rmsnorm(adt, h, T, d, g.rms_eps, u, s, gu8 ? xq : nullptr, xqs); }
     // The shared FFN depends only on u, so its two projections can run on the
     // side stream (its fp32 output rows go to a buffer of their own) while
     // the router and the routing run here; the combine then adds the routed
@@ -574,7 +606,7 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
       a.row_map = c->st<int32_t>(p.row_map);
       a.w_gstride = p.gu_stride; a.s_gstride = p.gu_npad; a.mx_off = p.gu_mx;
       PROF(CD_PROF_EXPERT_GU);
-      gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, (int64_t)T * k, T, nullptr, s);
+      gemm_grouped(c, p.wdt_exp, EPI_SWIGLU, a, (int64_t)T * k, T, nullptr, s, gu8);
     }
     {
       GemmArgs a = gemm_base(c->st<void>(p.aperm), g.expert_hidden, c->W + lw.dn, c->wt<float>(lw.dn_s),
@@ -589,10 +621,11 @@ void forward(cd_ctx* c, int r0, int n_req, int rows_per_req, const int32_t* ids,
     if (fork) hipStreamWaitEvent(s, c->ev_join, 0);
     {
       u_ready = l + 1 < g.n_layers || head;
+      const bool q8 = qkv8 && l + 1 < g.n_layers;   // the next layer's QKV input in E4M3
       PROF(CD_PROF_COMBINE);
       launch_combine(adt, c->st<void>(p.yperm), c->st<int32_t>(p.slot), c->st<float>(p.topk_gate),
                      g.shared_hidden ? c->st<float>(p.sout) : nullptr, T, k, d, h, u_ready ? u : nullptr,
-                     g.rms_eps, s);
+                     g.rms_eps, s, q8 ? xq : nullptr, xqs);
     }
   }
   if (head) {

@@ -79,4 +79,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---- per-row E4M3 activation quantisation ----------------------------------
+// Four values already rounded to bf16 (as fp32), scaled by inv = 448 / amax of
+// their row, clamped to +-448 and rounded to E4M3 (nearest even), packed low
+// byte first.  Every producer of E4M3 activation rows uses this, so a row
+// quantised by the standalone quantiser or by the kernel that writes it gets
+// the same codes.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float inv) {
+  const float f0 = fminf(fmaxf(a * inv, -448.f), 448.f);
+  const float f1 = fminf(fmaxf(b * inv, -448.f), 448.f);
+  const float f2 = fminf(fmaxf(c * inv, -448.f), 448.f);
+  const float f3 = fminf(fmaxf(d * inv, -448.f), 448.f);
+  uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
+}
+// the row's quantisation factor and stored scale from its max |value|
+__device__ __forceinline__ float e4m3_inv(float amax) { return amax > 0.f ? 448.0f / amax : 1.0f; }
+__device__ __forceinline__ float e4m3_scale(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
+
 }  // namespace cd

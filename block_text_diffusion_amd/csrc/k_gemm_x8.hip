@@ -335,8 +335,8 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const uint16_t* x, int64_t ld
       amax = fmaxf(amax, fmaxf(fabsf(bf2f(w4[t] & 0xFFFF)), fabsf(bf2f(w4[t] >> 16))));
   }
   amax = wave_max(amax);
-  const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
-  if (lane == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+  const float inv = e4m3_inv(amax);
+  if (lane == 0) s[row] = e4m3_scale(amax);
   uint8_t* qr = q + (int64_t)row * ldq;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -344,15 +344,9 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const uint16_t* x, int64_t ld
     const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
     uint32_t o[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float f0 = fminf(fmaxf(bf2f(w4[2 * t] & 0xFFFF) * inv, -448.f), 448.f);
-      const float f1 = fminf(fmaxf(bf2f(w4[2 * t] >> 16) * inv, -448.f), 448.f);
-      const float f2 = fminf(fmaxf(bf2f(w4[2 * t + 1] & 0xFFFF) * inv, -448.f), 448.f);
-      const float f3 = fminf(fmaxf(bf2f(w4[2 * t + 1] >> 16) * inv, -448.f), 448.f);
-      uint32_t p = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-      p = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, p, true);
-      o[t] = p;
-    }
+    for (int t = 0; t < 2; ++t)
+      o[t] = e4m3x4(bf2f(w4[2 * t] & 0xFFFF), bf2f(w4[2 * t] >> 16), bf2f(w4[2 * t + 1] & 0xFFFF),
+                    bf2f(w4[2 * t + 1] >> 16), inv);
     *reinterpret_cast<uint2*>(qr + 8 * (lane + 64 * i)) = make_uint2(o[0], o[1]);
   }
 }

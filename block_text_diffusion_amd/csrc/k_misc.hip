@@ -25,7 +25,8 @@ void launch_embed(int edt, const void* E, const int32_t* ids, int T, int V, int 
 // the scaling: every load of the row is issued before the first use, at
 // clamped addresses so none of them is conditional.
 template <int AT>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int T, int d, float eps, void* u) {
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int T, int d, float eps, void* u, uint8_t* q8,
+                                                 float* s8) {
   constexpr int NV = 16;   // float4 per lane held in registers
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -52,6 +53,34 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int T, int d, f
       if ((lane + 64 * j) * 4 < d) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    if constexpr (AT == DT_BF16) {
+      if (q8) {
+        // also the E4M3 row of the bf16 values with its scale (the input of
+        // an fp8 GEMM), as the standalone quantiser would compute it
+        uint2 p[NV];
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          p[j].x = pack_bf16(v[j].x * inv, v[j].y * inv);
+          p[j].y = pack_bf16(v[j].z * inv, v[j].w * inv);
+          if ((lane + 64 * j) * 4 < d)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf2f(p[j].x & 0xFFFF)), fabsf(bf2f(p[j].x >> 16))),
+                                     fmaxf(fabsf(bf2f(p[j].y & 0xFFFF)), fabsf(bf2f(p[j].y >> 16)))));
+        }
+        amax = wave_max(amax);
+        const float qi = e4m3_inv(amax);
+        if (lane == 0) s8[t] = e4m3_scale(amax);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int c = (lane + 64 * j) * 4;
+          if (c >= d) continue;
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(u) + (int64_t)t * d + c) = p[j];
+          *reinterpret_cast<uint32_t*>(q8 + (int64_t)t * d + c) =
+              e4m3x4(bf2f(p[j].x & 0xFFFF), bf2f(p[j].x >> 16), bf2f(p[j].y & 0xFFFF), bf2f(p[j].y >> 16), qi);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
       if ((lane + 64 * j) * 4 < d) put((lane + 64 * j) * 4, v[j], inv);
@@ -65,10 +94,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* h, int T, int d, f
     for (int c = lane * 4; c < d; c += 256) put(c, *reinterpret_cast<const float4*>(x + c), inv);
   }
 }
-void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s) {
+void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s, uint8_t* q8, float* s8) {
   const dim3 grid((T + 3) / 4);
-  if (adt == DT_F32) hipLaunchKernelGGL(k_rmsnorm<DT_F32>, grid, dim3(256), 0, s, h, T, d, eps, u);
-  else hipLaunchKernelGGL(k_rmsnorm<DT_BF16>, grid, dim3(256), 0, s, h, T, d, eps, u);
+  if (adt == DT_F32) hipLaunchKernelGGL(k_rmsnorm<DT_F32>, grid, dim3(256), 0, s, h, T, d, eps, u, nullptr, nullptr);
+  else hipLaunchKernelGGL(k_rmsnorm<DT_BF16>, grid, dim3(256), 0, s, h, T, d, eps, u, d <= 4096 ? q8 : nullptr, s8);
 }
 
 // cs[pos][i] = (cos, sin)(pos * theta^(-2i/dh)), computed in fp64

@@ -374,8 +374,8 @@ template <int AT, int NI>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ Yp, const int32_t* __restrict__ slot,
                                                  const float* __restrict__ gate, const float* __restrict__ add,
                                                  int k, int d, float* __restrict__ h, void* __restrict__ u,
-                                                 float eps) {
-  __shared__ float red[4];
+                                                 float eps, uint8_t* __restrict__ q8, float* __restrict__ s8) {
+  __shared__ float red[4], red8[4];
   const int t = blockIdx.x;
   float g[16];
   int64_t yr[16];
@@ -443,6 +443,37 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ Yp, co
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+    if constexpr (AT == DT_BF16) {
+      if (q8) {
+        // also the E4M3 row of the bf16 values with its scale (the input of
+        // the next layer's fp8 QKV GEMM), as the standalone quantiser would
+        uint2 p[NI];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          p[i].x = pack_bf16(acc[i].x * inv, acc[i].y * inv);
+          p[i].y = pack_bf16(acc[i].z * inv, acc[i].w * inv);
+          if (threadIdx.x * 4 + 1024 * i < d)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf2f(p[i].x & 0xFFFF)), fabsf(bf2f(p[i].x >> 16))),
+                                     fmaxf(fabsf(bf2f(p[i].y & 0xFFFF)), fabsf(bf2f(p[i].y >> 16)))));
+        }
+        amax = wave_max(amax);
+        if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red8[0], red8[1]), fmaxf(red8[2], red8[3]));
+        const float qi = e4m3_inv(amax);
+        if (threadIdx.x == 0) s8[t] = e4m3_scale(amax);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int c = threadIdx.x * 4 + 1024 * i;
+          if (c >= d) continue;
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(u) + (int64_t)t * d + c) = p[i];
+          *reinterpret_cast<uint32_t*>(q8 + (int64_t)t * d + c) =
+              e4m3x4(bf2f(p[i].x & 0xFFFF), bf2f(p[i].x >> 16), bf2f(p[i].y & 0xFFFF), bf2f(p[i].y >> 16), qi);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int c = threadIdx.x * 4 + 1024 * i;
@@ -482,21 +513,23 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ Yp, co
 
 template <int AT>
 static void run_combine(const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k, int d,
-                        float* h, void* u, float eps, hipStream_t s) {
+                        float* h, void* u, float eps, uint8_t* q8, float* s8, hipStream_t s) {
   const dim3 g(T), b(256);
   switch ((d + 1023) / 1024) {
-    case 1: hipLaunchKernelGGL((k_combine<AT, 1>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
-    case 2: hipLaunchKernelGGL((k_combine<AT, 2>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
-    case 3: hipLaunchKernelGGL((k_combine<AT, 3>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
-    case 4: hipLaunchKernelGGL((k_combine<AT, 4>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
-    default: hipLaunchKernelGGL((k_combine<AT, 0>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps); break;
+    case 1: hipLaunchKernelGGL((k_combine<AT, 1>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps, q8, s8); break;
+    case 2: hipLaunchKernelGGL((k_combine<AT, 2>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps, q8, s8); break;
+    case 3: hipLaunchKernelGGL((k_combine<AT, 3>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps, q8, s8); break;
+    case 4: hipLaunchKernelGGL((k_combine<AT, 4>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps, q8, s8); break;
+    default:   // d > 4096: no E4M3 rows (the fp8 GEMMs take d <= 4096)
+      hipLaunchKernelGGL((k_combine<AT, 0>), g, b, 0, s, Yp, slot, gate, add, k, d, h, u, eps, nullptr, nullptr);
+      break;
   }
 }
 
 void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k,
-                    int d, float* h, void* u, float eps, hipStream_t s) {
-  if (adt == DT_F32) run_combine<DT_F32>(Yp, slot, gate, add, T, k, d, h, u, eps, s);
-  else run_combine<DT_BF16>(Yp, slot, gate, add, T, k, d, h, u, eps, s);
+                    int d, float* h, void* u, float eps, hipStream_t s, uint8_t* q8, float* s8) {
+  if (adt == DT_F32) run_combine<DT_F32>(Yp, slot, gate, add, T, k, d, h, u, eps, nullptr, nullptr, s);
+  else run_combine<DT_BF16>(Yp, slot, gate, add, T, k, d, h, u, eps, u ? q8 : nullptr, s8, s);
 }
 
 }  // namespace cd

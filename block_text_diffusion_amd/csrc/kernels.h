@@ -159,12 +159,17 @@ void launch_route(const RouteArgs& a, hipStream_t s);
 
 // ---- misc ---------------------------------------------------------------------------
 void launch_embed(int edt, const void* E, const int32_t* ids, int T, int V, int d, float* h, hipStream_t s);
-void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s);
+// u[t] = RMSNorm(h[t]) (unit gain) in the activation type; with bf16
+// activations, d <= 4096 and q8 given, also the E4M3 rows of u (row stride d)
+// and their scales s8, exactly as launch_quant_fp8 would make them from u
+void launch_rmsnorm(int adt, const float* h, int T, int d, float eps, void* u, hipStream_t s, uint8_t* q8 = nullptr,
+                    float* s8 = nullptr);
 void launch_rope_table(float* cs, int max_ctx, int dh, float theta, hipStream_t s);
 // h[t] += sum_j gate[t][j] * Yp[slot[t][j]] (choice order) + add[t] (fp32 row, or null);
-// when u is not null also u[t] = RMSNorm(h[t]) (unit gain) in the activation type
+// when u is not null also u[t] = RMSNorm(h[t]) (unit gain) in the activation type,
+// and (bf16, d <= 4096, q8 given) its E4M3 rows and scales as launch_rmsnorm
 void launch_combine(int adt, const void* Yp, const int32_t* slot, const float* gate, const float* add, int T, int k,
-                    int d, float* h, void* u, float eps, hipStream_t s);
+                    int d, float* h, void* u, float eps, hipStream_t s, uint8_t* q8 = nullptr, float* s8 = nullptr);
 void launch_attn_merge(int adt, const AttnArgs& a, hipStream_t s);
 void launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 
