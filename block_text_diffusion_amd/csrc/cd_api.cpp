@@ -370,46 +370,46 @@ int router_split(const cd_config& g, int T) {
   return sp;
 }
 
+void note_launch(cd_ctx* c, int st) {
+  if (st && !c->launch_err) c->launch_err = st;
+}
+
 // Dense GEMM.  The LM head (thousands of 128-column chunks) at up to 256
 // rows takes the LDS-staged kernel: one workgroup per chunk holds all rows,
 // so the activations are read once per chunk.  Every other layer takes the
 // row-tiled kernel: at the canvas batch, 32-row tiles give each weight chunk
 // 8 workgroups on one XCD (one HBM read, the rest from its L2) and fill the
-// chip without splitting the contraction.
-void note_launch(cd_ctx* c, int st) {
-  if (st && !c->launch_err) c->launch_err = st;
+// chip without splitting the contraction.  Larger batches take the
+// LDS-staged kernel when there are enough (256-row slab, 256-column chunk)
+// items to fill the chip; the expert-combining epilogue gathers 8 rows per
+// output and keeps the many workgroups of the row-tiled kernel.
+bool dense_lds_staged(int M, int64_t Nt, int ksplit) {
+  const int64_t x_items = (int64_t)((M + 255) / 256) * ((Nt + 15) / 16);
+  return ksplit <= 1 && ((M > 256 && x_items >= 256) || (Nt + 7) / 8 >= 512);
+}
+// Whether a dense launch (as gemm_dense decides) or a grouped expert launch (as
+// gemm_grouped decides) runs W8A8 on E4M3 activation rows; the forward asks
+// before the launch so that the kernel producing those rows also writes them
+// in E4M3.
+bool dense_takes_x8(const cd_ctx* c, int wdt, int epi, int64_t Nt, int M, int ksplit, bool w8a8) {
+  return dense_lds_staged(M, Nt, ksplit) && w8a8 && wdt == CD_FP8 && c->p.x8 && epi != EPI_F32;
+}
+bool grouped_takes_x8(const cd_ctx* c, int wdt, int64_t rows) {
+  return big_expert_tiles(rows, c->p.c.n_experts) && (wdt == CD_FP8 || wdt == CD_MXFP4) && c->p.x8;
 }
 
 // w8a8: the launch may quantise its activations to E4M3 (fp8 weights on the
 // LDS-staged kernel).  The QKV projection takes it; the output projection
 // keeps bf16 activations, since its output feeds the router directly and the
 // activation rounding moved near-tie routing decisions too far.
-// Whether a dense launch (as gemm_dense decides) or a grouped expert launch (as
-// gemm_grouped decides) runs W8A8 on E4M3 activation rows; the forward asks
-// before the launch so that the kernel producing those rows also writes them
-// in E4M3.
-bool dense_takes_x8(const cd_ctx* c, int wdt, int epi, int64_t Nt, int M, int ksplit, bool w8a8) {
-  const int64_t x_items = (int64_t)((M + 255) / 256) * ((Nt + 15) / 16);
-  const bool lds_staged = ksplit <= 1 && ((M > 256 && x_items >= 256) || (Nt + 7) / 8 >= 512);
-  return lds_staged && w8a8 && wdt == CD_FP8 && c->p.x8 && epi != EPI_F32;
-}
-bool grouped_takes_x8(const cd_ctx* c, int wdt, int64_t rows) {
-  return big_expert_tiles(rows, c->p.c.n_experts) && (wdt == CD_FP8 || wdt == CD_MXFP4) && c->p.x8;
-}
-
 // quantised: the activation rows are already in the E4M3 buffer (written by
 // the kernel that produced them), so the W8A8 path skips its quantiser.
 void gemm_dense(cd_ctx* c, int wdt, int epi, GemmArgs a, int M, hipStream_t s, bool w8a8 = false,
                 bool quantised = false) {
-  // the LDS-staged kernel needs enough (256-row slab, 256-column chunk)
-  // items to fill the chip; the expert-combining epilogue gathers 8 rows per
-  // output and prefers the many workgroups of the row-tiled kernel
-  const int64_t x_items = (int64_t)((M + 255) / 256) * ((a.Nt + 15) / 16);
-  const bool lds_staged = a.ksplit <= 1 && ((M > 256 && x_items >= 256) || a.n_chunks >= 512);
-  if (lds_staged) {
+  if (dense_lds_staged(M, a.Nt, a.ksplit)) {
     a.M = M;
     a.tiles = nullptr;
-    if (w8a8 && wdt == CD_FP8 && c->p.x8 && epi != EPI_F32) {
+    if (dense_takes_x8(c, wdt, epi, a.Nt, M, a.ksplit, w8a8)) {
       // W8A8: the activation rows quantised to E4M3 with a scale per row
       uint8_t* xq = c->st<uint8_t>(c->p.xq);
       float* xqs = c->st<float>(c->p.xqs);
@@ -443,7 +443,7 @@ void gemm_grouped(cd_ctx* c, int wdt, int epi, GemmArgs a, int64_t rows, int x_r
   if (big_expert_tiles(rows, c->p.c.n_experts)) {
     a.max_tiles = (int)std::min<int64_t>(c->p.max_tiles, (rows + BIG_TILE_ROWS - 1) / BIG_TILE_ROWS +
                                                             std::min<int64_t>(rows, c->p.c.n_experts));
-    if ((wdt == CD_FP8 || wdt == CD_MXFP4) && c->p.x8) {
+    if (grouped_takes_x8(c, wdt, rows)) {
       // W8A8 (see gemm_dense), or MXFP4 weights x E4M3 activations on the
       // block-scaled MFMA; the down projection's input has its own buffer
       const bool down = epi == EPI_ROWS;

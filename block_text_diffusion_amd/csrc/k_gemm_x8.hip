@@ -173,8 +173,8 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
           ww[j][h] = *reinterpret_cast<const u32x4*>(wp[j] + (int64_t)min(2 * s + h, KT - 1) * 1024);
     }
   };
-  // one stage: for each of the wave's 8 row tiles, the fragment pair (two
-  // k-tiles) from LDS and four MFMAs; the LDS reads run one row tile ahead
+  // one stage: for each of the wave's 16 row tiles, the fragment pair (two
+  // k-tiles) from LDS and two MFMAs; the LDS reads run one row tile ahead
   // of the MFMAs that use them.  SINGLE: the stage holds one k-tile (odd K
   // at the last stage); the weights' second half is zero there, so the
   // second fragment (a finite copy of the last k-tile) adds nothing.  F4:
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < Q8_NTW; ++j) {
-        w1[j] = single ? u32x4{0, 0, 0, 0} : ww[j][F4 ? 0 : 1];
+        w1[j] = single ? u32x4{0, 0, 0, 0} : ww[j][1];
         es[j] = 0;
       }
     }
