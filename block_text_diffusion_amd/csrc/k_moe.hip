@@ -223,7 +223,7 @@ __global__ __launch_bounds__(1024) void k_route_one(RouteArgs a) {
       tl[0] = tid;
       tl[1] = off + i * a.mrows;
       tl[2] = min(a.mrows, total - i * a.mrows);
-      tl[3] = 0;
+      tl[3] = i | (((total + a.mrows - 1) / a.mrows) << 16);
     }
   }
   // padding rows of every segment (fewer than mrows each): wave w takes
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) void k_route_scan(RouteArgs a, int n_blk) {
       tl[0] = tid;
       tl[1] = off + i * a.mrows;
       tl[2] = min(a.mrows, total - i * a.mrows);
-      tl[3] = 0;
+      tl[3] = i | (((total + a.mrows - 1) / a.mrows) << 16);
     }
   }
   // padding rows of every segment (fewer than mrows each): wave w takes

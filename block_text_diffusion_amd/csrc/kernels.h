@@ -54,7 +54,9 @@ struct GemmArgs {
   int64_t mx_off;          // MXFP4: bytes from a group's tiles to its E8M0 scales
   int K, Nt, N, n_chunks;  // Nt = packed 16-row tiles; N = logical outputs
   // work tiles: grouped (device table) or dense (M rows)
-  const int32_t* tiles;    // [max_tiles][4]: group, row0, rows, 0
+  // [max_tiles][4]: group, row0, rows, and (index of the tile inside its
+  // group) | (the group's tile count << 16); tiles are sorted by group
+  const int32_t* tiles;
   const int32_t* n_tiles;  // device count for grouped launches
   int max_tiles;
   int M;
@@ -148,7 +150,7 @@ struct RouteArgs {
   int32_t* seg_off;      // [E+1] padded segment offsets
   int32_t* row_map;      // [max_rows] token of each permuted row, -1 pad
   int32_t* slot;         // [T][k] permuted row of assignment (t, j)
-  int32_t* tiles;        // [max_tiles][4]
+  int32_t* tiles;        // [max_tiles][4], as GemmArgs::tiles
   int32_t* n_tiles;      // [1]
   int mrows;             // rows per GEMM tile
   int max_rows, max_tiles;
