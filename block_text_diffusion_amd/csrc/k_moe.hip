@@ -223,6 +223,9 @@ __global__ __launch_bounds__(1024) void k_route_one(RouteArgs a) {
       tl[0] = tid;
       tl[1] = off + i * a.mrows;
       tl[2] = min(a.mrows, total - i * a.mrows);
+      // index inside the expert | the expert's tile count << 16 (the
+      // row-tiled GEMM's expert-major order; it reads this only below 256 rows
+      // per expert on average, where an expert has fewer than 16 E <= 4096 tiles)
       tl[3] = i | (((total + a.mrows - 1) / a.mrows) << 16);
     }
   }
@@ -324,6 +327,9 @@ __global__ __launch_bounds__(256) void k_route_scan(RouteArgs a, int n_blk) {
       tl[0] = tid;
       tl[1] = off + i * a.mrows;
       tl[2] = min(a.mrows, total - i * a.mrows);
+      // index inside the expert | the expert's tile count << 16 (the
+      // row-tiled GEMM's expert-major order; it reads this only below 256 rows
+      // per expert on average, where an expert has fewer than 16 E <= 4096 tiles)
       tl[3] = i | (((total + a.mrows - 1) / a.mrows) << 16);
     }
   }
