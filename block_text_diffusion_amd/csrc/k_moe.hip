@@ -72,15 +72,24 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
         if (s0 + q < a.nsplit) v[i] += part[i][q];
   }
   // candidate i of this lane: (logit, expert id); an expert past E or already
-  // taken is (-inf, INT_MAX), which no available expert ties with or loses to
+  // taken is (-inf, INT_MAX), which no available expert ties with or loses to.
+  // A NaN logit ranks as -inf, so the k ids stay distinct experts in [0, E),
+  // and it makes the row's gates NaN, so the fault reaches the logits and the
+  // sampler's non-finite check instead of vanishing into finite gates.
   int eid[NPL];
+  float poison = 0.f;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = l16 + 16 * i;
     const bool live = e < a.E;
     eid[i] = live ? e : 0x7FFFFFFF;
+    poison = (live && v[i] != v[i]) ? __builtin_nanf("") : poison;
     v[i] = (live && v[i] == v[i]) ? v[i] : -INFINITY;
   }
+  row_add<DPP_QUAD_XOR1>(poison);
+  row_add<DPP_QUAD_XOR2>(poison);
+  row_add<DPP_ROW_HALF_MIRROR>(poison);
+  row_add<DPP_ROW_MIRROR>(poison);
   float my_v = -INFINITY;
   int my_id = 0;
   for (int j = 0; j < a.k; ++j) {
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
   row_add<DPP_ROW_HALF_MIRROR>(sum);
   row_add<DPP_ROW_MIRROR>(sum);
   if (l16 < a.k) {
-    g = g / sum;
+    g = g / sum + poison;
     a.topk_id[(int64_t)t * a.k + l16] = my_id;
     a.topk_gate[(int64_t)t * a.k + l16] = g;
     if (a.trace_ids) a.trace_ids[(int64_t)t * a.k + l16] = my_id;
