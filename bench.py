@@ -68,6 +68,45 @@ def measured_copy_gbs(nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def vendor_gemm(w, reps=96):
+    """The vendor library's GEMM (torch.nn.functional.linear, hipBLASLt or
+    rocBLAS as torch picks it) on the dense projection shapes of one canvas
+    pass (256 rows), for comparison with the library's own launches.  Each
+    shape is timed twice: 'cold' rotates over enough weight copies (at least
+    1 GB) that every launch reads its weights from HBM, as every launch inside
+    a denoise pass does (a pass streams about 50 GB); 'warm' reuses one weight
+    matrix, which then stays in the 256 MB last-level cache.  Times are
+    averages over back-to-back launches between two events."""
+    import torch
+    M = w["C"]
+    shapes = {"qkv": ((w["Hq"] + 2 * w["Hkv"]) * w["dh"], w["d"]), "o_proj": (w["d"], w["Hq"] * w["dh"]),
+              "shared_gate_up": (2 * w["fs"], w["d"]), "shared_down": (w["d"], w["fs"])}
+    out = {"library": str(torch.backends.cuda.preferred_blas_library()), "rows": M}
+    for name, (N, K) in shapes.items():
+        x = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        n_copies = max(24, -(-(1 << 30) // (N * K * 2)))
+        ws = [torch.randn(N, K, device="cuda").to(torch.bfloat16) for _ in range(n_copies)]
+        res = {"N": N, "K": K, "weight_mb": round(N * K * 2 / 1e6, 2), "copies": n_copies}
+        for mode in ("cold", "warm"):
+            for i in range(8):
+                torch.nn.functional.linear(x, ws[i % n_copies if mode == "cold" else 0])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(reps):
+                torch.nn.functional.linear(x, ws[i % n_copies if mode == "cold" else 0])
+            e1.record()
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            res[f"{mode}_us"] = round(us, 2)
+            res[f"{mode}_tbs"] = round(N * K * 2 / (us * 1e-6) / 1e12, 3)
+        out[name] = res
+        log(f"vendor gemm {name}: {res}")
+        del ws, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def gpu_part(w, steps, warmup, prof_steps, do_block=True):
     import torch
     from block_text_diffusion_amd import binding as B
@@ -539,6 +578,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="step_bf16 only: skip the gen_bf16 and batch_fp8 lines added to the default run")
     ap.add_argument("--copy-calib", action="store_true", help="only run the byte-counter calibration copy")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor library's GEMM on the dense projection shapes (cold and warm)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time one full block at 1, 2, 4 and 32 requests (the 32-request fp8 model)")
     ap.add_argument("--serve", action="store_true",
@@ -546,6 +587,9 @@ def main():
     args = ap.parse_args()
     if args.copy_calib:
         copy_calibration()
+        return
+    if args.vendor_gemm:
+        print(json.dumps({"vendor_gemm": vendor_gemm(synth_inputs.workload(args.workload))}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the canvas denoise step here runs on a single MI355X "
