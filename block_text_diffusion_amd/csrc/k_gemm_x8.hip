@@ -1,4 +1,4 @@
-// fp8 x fp8 GEMM on 256-row work items (the batched fp8 model's QKV, O and
+// fp8 x fp8 GEMM on 128-row work items (the batched fp8 model's QKV, O and
 // routed-expert projections; the MXFP4 model's routed experts with F4):
 //   Y[m][n] = sx[m] * sw[n] * sum_k qx[m][k] qw[n][k]
 // qw: E4M3 weights in the packed fragment tiles (per-row scale sw, applied
@@ -10,9 +10,9 @@
 // columns to a lane's bytes (the weight tile and activation fragment layouts
 // match), so the product is the dot product whatever order the hardware
 // gives the 128 bytes.  Otherwise the structure of k_gemm_x: work item =
-// 256 rows x 256 columns, eight waves (all 256 rows x two 16-column weight
+// 128 rows x 256 columns, eight waves (all 128 rows x two 16-column weight
 // tiles each), activation fragments copied into LDS with global_load_lds,
-// weights into registers, DIST stages in flight.
+// weights into registers, DIST stages in flight; two workgroups per CU.
 //
 // F4: MXFP4 weights (E2M1 codes, one E8M0 scale per 32 columns of a row) on
 // the same MFMA with block scales: Y[m][n] = sx[m] * sum_k qx[m][k] *
@@ -51,19 +51,31 @@ __device__ __forceinline__ f32x4 mma_fp4(const u32x4& w, uint32_t ws, const u32x
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, 0, (int)ws, 0, 127);
 }
 
-// 256 rows x 256 columns per work item; every wave takes all 16 row tiles and
-// two of the 16 weight tiles, so each weight byte is loaded once per
-// workgroup (with two row halves of four tiles each, both halves loaded the
-// same weights: 96 instead of 64 KB of global loads per CU and stage; the
+// Q8_ROWS rows x 256 columns per work item; every wave takes all Q8_MTW row
+// tiles and two of the 16 weight tiles, so each weight byte is loaded once
+// per workgroup (with two row halves of four tiles each, both halves loaded
+// the same weights: 96 instead of 64 KB of global loads per CU and stage; the
 // single row group reads twice the activation fragments from LDS and ran the
-// 32-request passes 2.4% and the 4096-row prefills 3% faster)
-constexpr int Q8_WAVES = 8, Q8_MTW = 16, Q8_NTW = 2, Q8_WN = 8;
+// 32-request passes 2.4% and the 4096-row prefills 3% faster).  A 256-row
+// tile of the routing table (or a 256-row slab of a dense launch) is
+// Q8_PIECES work items of Q8_ROWS rows.  128-row items (64 accumulator
+// VGPRs, 128 VGPRs in all, 48 KB of LDS) let two workgroups share a CU, so
+// one item's first loads and its epilogue overlap the other's MFMAs.  Same
+// box against 256-row items (one workgroup per CU): 32-request fp8 pass
+// 72.6 -> 68.6 ms (expert gate/up 16.8 -> 15.2, down 14.6 -> 12.5, QKV
+// 4.93 -> 4.41 ms), MXFP4 pass 67.2 -> 64.9 ms, fp8-model 4096-token prefill
+// 34.1 -> 31.5 ms; results bit-identical (each output keeps its MFMA
+// sequence).  Keeping 256-row items for the MXFP4 down projection alone was
+// slower (pass 67.5 vs 66.5 ms, down 12.7 vs 11.6 ms, same box).
+constexpr int Q8_WAVES = 8, Q8_MTW = 8, Q8_NTW = 2, Q8_WN = 8;
 constexpr int Q8_NBUF = 3, Q8_DIST = 2;
+constexpr int Q8_ROWS = 16 * Q8_MTW, Q8_PIECES = 256 / Q8_ROWS;
+static_assert(Q8_PIECES * Q8_ROWS == 256, "a 256-row tile splits into whole work items");
 
 template <int EPI, bool F4>
-__global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
-  constexpr int BLK = 32;                         // activation fragments per stage: 16 row tiles x 2 k-tiles
-  constexpr int BPW = BLK / Q8_WAVES;             // each wave copies 4
+__global__ __launch_bounds__(512, 256 / Q8_ROWS) void k_gemm_x8(const GemmArgs a) {
+  constexpr int BLK = 2 * Q8_MTW;                 // activation fragments per stage: row tiles x 2 k-tiles
+  constexpr int BPW = BLK / Q8_WAVES;             // each wave copies BPW
   // vector loads per wave per stage: fp8, two 16-byte halves per weight
   // tile; F4, two 8-byte code chunks and a scale dword
   constexpr int LPS = BPW + (F4 ? 3 : 2) * Q8_NTW;
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
   // 70.9 -> 70.0 ms per 32-request MXFP4 pass, 77.6 -> 76.2 ms fp8)
   int chunk, tile;
   {
-    const int nt = a.tiles ? *a.n_tiles : (a.M + 255) / 256;
+    const int nt = a.tiles ? *a.n_tiles * Q8_PIECES : (a.M + Q8_ROWS - 1) / Q8_ROWS;
     const int work = nt * nchunks;
     const int w8 = (work + 7) & ~7;
     const int bid = blockIdx.x;
@@ -92,12 +104,17 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
   }
   int group = 0, row0, rows;
   if (a.tiles) {
-    group = a.tiles[4 * tile];
-    row0 = a.tiles[4 * tile + 1];
-    rows = a.tiles[4 * tile + 2];
+    // piece `part` of table tile t: its rows part*Q8_ROWS.. (a tile with
+    // fewer rows leaves its last pieces empty; the whole workgroup returns
+    // before its first barrier)
+    const int t = tile / Q8_PIECES, part = tile - t * Q8_PIECES;
+    group = a.tiles[4 * t];
+    row0 = a.tiles[4 * t + 1] + part * Q8_ROWS;
+    rows = min(Q8_ROWS, a.tiles[4 * t + 2] - part * Q8_ROWS);
+    if (rows <= 0) return;
   } else {
-    row0 = tile * 256;
-    rows = min(256, a.M - row0);
+    row0 = tile * Q8_ROWS;
+    rows = min(Q8_ROWS, a.M - row0);
   }
   const int KT = a.K / 64;                  // 64-column k-tiles
   const int nst = (KT + 1) / 2;             // stages of two k-tiles (the last may hold one)
@@ -282,7 +299,7 @@ __global__ __launch_bounds__(512) void k_gemm_x8(const GemmArgs a) {
 template <int EPI, bool F4>
 static void run_x8(const GemmArgs& a, hipStream_t s) {
   const int chunks = (a.Nt + 15) / 16;
-  const int tiles = a.tiles ? a.max_tiles : (a.M + 255) / 256;
+  const int tiles = a.tiles ? a.max_tiles * Q8_PIECES : (a.M + Q8_ROWS - 1) / Q8_ROWS;
   const int blocks = (int)round_up((int64_t)tiles * chunks, 8);
   hipLaunchKernelGGL((k_gemm_x8<EPI, F4>), dim3(blocks), dim3(64 * Q8_WAVES), 0, s, a);
 }
