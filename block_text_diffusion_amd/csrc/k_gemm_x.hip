@@ -2,7 +2,8 @@
 // Y[m][n] = sum_k X[m][k] * W[n][k].  A work item is a 256-row slab of a
 // dense launch, or a 256-row tile of one expert (grouped launch), times a
 // 256-column chunk, so every weight byte feeds 256 rows and every activation
-// byte 256 columns.  Used for the LM head at the canvas batch and for every
+// byte 256 columns (with fp8 weights the items are 128-row halves of these,
+// see XRows).  Used for the LM head at the canvas batch and for every
 // GEMM at more than 256 rows (batched canvases, prefill).
 //  * per k-tile stage the workgroup copies the 16 activation fragments
 //    (16 rows x KF columns each, 1 KB, already in MFMA operand order) from
@@ -30,14 +31,29 @@
 
 namespace cd {
 
-constexpr int XMT = 16;   // 16-row tiles: 256 rows
 constexpr int XWAVES = 8; // two waves per SIMD: one's waits overlap the other's MFMAs
-constexpr int XMTW = 8;   // row tiles per wave (waves 0-3: rows 0-127, waves 4-7: rows 128-255)
 constexpr int XNTW = 4;   // weight tiles per wave: a workgroup covers 256 columns, so the
                           // activations are re-read from L2 once per 256 output columns
 
+// Rows per work item.  bf16 / fp32 weights (staged in LDS, 128 KB per
+// workgroup): 256 rows, 16 row tiles, eight per wave (waves 0-3 rows 0-127,
+// waves 4-7 rows 128-255).  fp8 weights (in registers): 128 rows, four row
+// tiles per wave, so the accumulators take 64 instead of 128 VGPRs and two
+// workgroups share a CU, one's first loads and epilogue overlapping the
+// other's MFMAs (the 32-request pass's output projection 6.71 -> 5.46 ms,
+// same box; the bf16 instantiations ran slower that way: canvas LM head
+// 0.44-0.46 -> 0.49 ms, 32-request LM head 12.5 -> 13.7 ms).  A 256-row tile
+// of the routing table is then PIECES work items.
+template <int WT>
+struct XRows {
+  static constexpr int MT = WT == DT_FP8 ? 8 : 16;   // 16-row tiles per work item
+  static constexpr int MTW = MT / 2;                 // row tiles per wave
+  static constexpr int PIECES = 16 / MT, PER_CU = 16 / MT;
+};
+
 template <int WT, int AT, int EPI>
-__global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
+__global__ __launch_bounds__(512, (XRows<WT>::PER_CU)) void k_gemm_x(const GemmArgs a) {
+  constexpr int XMT = XRows<WT>::MT, XMTW = XRows<WT>::MTW, XPIECES = XRows<WT>::PIECES;
   constexpr int KF = 64 / (WT == DT_F32 ? 4 : WT == DT_BF16 ? 2 : 1);
   constexpr bool F4 = WT == DT_FP4;                   // MXFP4: 512-byte tiles + a scale byte per lane
   constexpr int TB = F4 ? 512 : 1024;                 // bytes per weight tile
@@ -66,7 +82,7 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   int ks, chunk, tile;
   {
     int nt;
-    if (a.tiles) nt = *a.n_tiles;
+    if (a.tiles) nt = *a.n_tiles * XPIECES;
     else nt = (a.M + XMT * 16 - 1) / (XMT * 16);
     const int work = nt * nchunks * ksplit;
     const int w8 = (work + 7) & ~7;
@@ -81,9 +97,13 @@ __global__ __launch_bounds__(512) void k_gemm_x(const GemmArgs a) {
   }
   int group = 0, row0, rows;
   if (a.tiles) {
-    group = a.tiles[4 * tile];
-    row0 = a.tiles[4 * tile + 1];
-    rows = a.tiles[4 * tile + 2];
+    // piece `part` of table tile t (a tile of fewer rows leaves its last
+    // pieces empty: the workgroup returns before its first barrier)
+    const int t = tile / XPIECES, part = tile - t * XPIECES;
+    group = a.tiles[4 * t];
+    row0 = a.tiles[4 * t + 1] + part * XMT * 16;
+    rows = min(XMT * 16, a.tiles[4 * t + 2] - part * XMT * 16);
+    if (rows <= 0) return;
   } else {
     row0 = tile * XMT * 16;
     rows = min(XMT * 16, a.M - row0);
@@ -279,7 +299,8 @@ static void run_x(const GemmArgs& a, hipStream_t s) {
   // grid sized for the most row tiles (grouped: max_tiles; dense: M/256),
   // rounded to the 8 XCDs; surplus workgroups return at once
   const int chunks = (a.Nt + 4 * XNTW - 1) / (4 * XNTW);
-  const int tiles = a.tiles ? a.max_tiles : (a.M + XMT * 16 - 1) / (XMT * 16);
+  constexpr int XMT = XRows<WT>::MT;
+  const int tiles = a.tiles ? a.max_tiles * XRows<WT>::PIECES : (a.M + XMT * 16 - 1) / (XMT * 16);
   const int blocks = (int)round_up((int64_t)tiles * chunks * (a.ksplit > 1 ? a.ksplit : 1), 8);
   hipLaunchKernelGGL((k_gemm_x<WT, AT, EPI>), dim3(blocks), dim3(64 * XWAVES), 0, s, a);
 }
