@@ -40,7 +40,7 @@ constexpr int XNTW = 4;   // weight tiles per wave: a workgroup covers 256 colum
 // waves 4-7 rows 128-255).  fp8 weights (in registers): 128 rows, four row
 // tiles per wave, so the accumulators take 64 instead of 128 VGPRs and two
 // workgroups share a CU, one's first loads and epilogue overlapping the
-// other's MFMAs (the 32-request pass's output projection 6.71 -> 5.46 ms,
+// other's MFMAs (the 32-request pass's output projection 6.65 -> 5.39 ms,
 // same box; the bf16 instantiations ran slower that way: canvas LM head
 // 0.44-0.46 -> 0.49 ms, 32-request LM head 12.5 -> 13.7 ms).  A 256-row tile
 // of the routing table is then PIECES work items.
@@ -296,8 +296,9 @@ __global__ __launch_bounds__(512, (XRows<WT>::PER_CU)) void k_gemm_x(const GemmA
 
 template <int WT, int AT, int EPI>
 static void run_x(const GemmArgs& a, hipStream_t s) {
-  // grid sized for the most row tiles (grouped: max_tiles; dense: M/256),
-  // rounded to the 8 XCDs; surplus workgroups return at once
+  // grid sized for the most work items (grouped: max_tiles times the pieces
+  // of a tile; dense: the row slabs), rounded to the 8 XCDs; surplus
+  // workgroups return at once
   const int chunks = (a.Nt + 4 * XNTW - 1) / (4 * XNTW);
   constexpr int XMT = XRows<WT>::MT;
   const int tiles = a.tiles ? a.max_tiles * XRows<WT>::PIECES : (a.M + XMT * 16 - 1) / (XMT * 16);
