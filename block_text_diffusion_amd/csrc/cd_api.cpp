@@ -43,7 +43,9 @@ constexpr int GROUPED_MT = 2;          // expert GEMM row tile = 32 rows (few ro
 constexpr int BIG_TILE_ROWS = 256;     // expert row tile of the LDS-staged kernel (many rows per expert)
 
 // Many rows per expert (batched canvases, prefill): 256-row expert tiles on
-// the LDS-staged kernel, which reuses every weight byte 256 times.
+// the LDS-staged kernels, which reuse every weight byte for all rows of a
+// work item (256, or 128 for fp8 weights and the fp8-activation kernel, whose
+// work items are the two halves of a tile).
 bool big_expert_tiles(int64_t assignments, int E) { return assignments >= (int64_t)BIG_TILE_ROWS * E; }
 constexpr int MAX_SPLIT = ATT_MAX_SPLIT;   // attention key splits
 constexpr int MAX_RSPLIT = MAX_ROUTER_SPLIT;         // router contraction splits

@@ -82,12 +82,14 @@ struct GemmArgs {
 // Both launchers return 0, or CD_ERR_UNSUPPORTED (-5) for an MXFP4 launch with
 // a split contraction (its scale dwords are indexed from k-tile 0).
 int launch_gemm(int wdt, int adt, int mt, int epi, const GemmArgs& a, hipStream_t s);
-// 256-row work items, activations staged in LDS (a.ksplit > 1: EPI_F32 partials)
+// 256-row work items (128-row halves with fp8 weights), activations staged in
+// LDS (a.ksplit > 1: EPI_F32 partials)
 int launch_gemm_x(int wdt, int adt, int epi, const GemmArgs& a, hipStream_t s);
 // fp8 (DT_FP8) or MXFP4 (DT_FP4, EPI_SWIGLU / EPI_ROWS) weights x fp8
 // activations (E4M3 rows of X, one fp32 scale per row in a.xscale) on the
-// 16x16x128 f8f6f4 MFMA, 256-row work items as launch_gemm_x; every
-// epilogue but EPI_F32, no split contraction.  0 or CD_ERR_UNSUPPORTED.
+// 16x16x128 f8f6f4 MFMA, 128-row work items (two per 256-row tile or slab,
+// two workgroups per CU); every epilogue but EPI_F32, no split contraction.
+// 0 or CD_ERR_UNSUPPORTED.
 int launch_gemm_x8(int wdt, int epi, const GemmArgs& a, hipStream_t s);
 // q = E4M3 rows of bf16 x with one scale per row (amax / 448), for
 // launch_gemm_x8; rows at or past *n_dev (if not null) are skipped.  K a
